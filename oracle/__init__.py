@@ -1,0 +1,157 @@
+"""CPU oracle for band -> bidiagonal bulge chasing.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+(``band_bidiagonal_bulge_amd``); the two meet only through the seeded input
+generators in ``bb_inputs``.
+
+The arithmetic lives in ``bb_oracle.c`` / ``bb_oracle_body.h`` (plain C, one
+scalar loop per step of the method, fp32 or fp64).  This module builds that
+library with gcc and marshals numpy arrays to it.
+
+Follows the page "Accelerating Bidiagonalization of Banded Matrices through
+Memory-Aware Bulge-Chasing on GPUs" (three-cycle-separation passage,
+Algorithm 2 passage) and the page "A two-stage reduction on an Apple M5 Pro",
+section 6 (one row or one column cleared per reflector, sweeps chasing their
+bulge a block of b at a time).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = [os.path.join(_HERE, "bb_oracle.c"), os.path.join(_HERE, "bb_oracle_body.h")]
+_LIB_PATH = os.path.join(_HERE, "libbb_oracle.so")
+# -ffp-contract=off: only the explicit fma() calls fuse; -mfma lets gcc emit
+# them as single instructions (correctly rounded either way).
+_CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-mfma", "-fno-math-errno"]
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (host only).  Returns the library path."""
+    stale = not os.path.exists(_LIB_PATH) or any(
+        os.path.getmtime(s) > os.path.getmtime(_LIB_PATH) for s in _SRC)
+    if force or stale:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", *_CFLAGS, "-o", tmp, _SRC[0], "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _cpu_has_fma() -> bool:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("flags"):
+                    return " fma " in (line.rstrip() + " ")
+    except OSError:
+        pass
+    return True
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not _cpu_has_fma():
+            raise RuntimeError("oracle build uses the FMA instruction; this host CPU lacks it")
+        path = _LIB_PATH if os.path.exists(_LIB_PATH) else build()
+        L = ctypes.CDLL(path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        for suf in ("f64", "f32"):
+            f = getattr(L, "bb_oracle_reduce_" + suf)
+            f.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i64, ctypes.POINTER(i64)]
+            f.restype = i32
+            g = getattr(L, "bb_oracle_run_cycles_" + suf)
+            g.argtypes = [vp, i64, i64, i32, i32, vp, i64, vp]
+            g.restype = i32
+        L.bb_oracle_ld.argtypes = [i64, i32, i32]
+        L.bb_oracle_ld.restype = i64
+        L.bb_oracle_T.argtypes = [i64, i32, i32]
+        L.bb_oracle_T.restype = i64
+        _lib = L
+    return _lib
+
+
+def _np_dtype(name):
+    return {"f32": np.float32, "f64": np.float64}[name]
+
+
+def _suffix(dt):
+    return "f32" if np.dtype(dt) == np.float32 else "f64"
+
+
+def working_ld(n: int, bw: int, tw: int) -> int:
+    """Stored diagonals of the working band: T sub + diagonal + BW+T super."""
+    return int(lib().bb_oracle_ld(n, bw, tw))
+
+
+def working_T(n: int, bw: int, tw: int) -> int:
+    return int(lib().bb_oracle_T(n, bw, tw))
+
+
+def reduce(band: np.ndarray, bw: int, tw: int, compute: str | None = None,
+           return_band: bool = False, max_cycles: int = -1):
+    """Sequential bulge-chasing reduction of an upper band.
+
+    band     (n, >= bw+1) array, row i holds A(i, i..i+bw); entries past n
+             are ignored.  Its dtype (f32/f64) is the storage precision.
+    compute  'f32' or 'f64' (default: the band's dtype).  An fp32 band with
+             compute='f64' is widened exactly before the reduction.
+    Returns (d, e) or (d, e, working_band, T) with return_band.
+    With max_cycles >= 0 the reduction stops early (bench sampling only) and
+    the third return value is the number of cycles executed.
+    """
+    band = np.asarray(band)
+    n = band.shape[0]
+    cdt = _np_dtype(compute) if compute else band.dtype
+    a = np.ascontiguousarray(band, dtype=cdt)
+    d = np.zeros(n, dtype=cdt)
+    e = np.zeros(max(n - 1, 0), dtype=cdt)
+    ld = working_ld(n, bw, tw)
+    out = np.zeros((n, ld), dtype=cdt) if return_band else None
+    done = ctypes.c_int64(0)
+    f = getattr(lib(), "bb_oracle_reduce_" + _suffix(cdt))
+    rc = f(a.ctypes.data, a.shape[1], n, bw, tw, d.ctypes.data,
+           e.ctypes.data if e.size else None,
+           out.ctypes.data if out is not None else None, max_cycles, ctypes.byref(done))
+    if rc != 0:
+        raise ValueError("oracle rejected arguments (rc=%d)" % rc)
+    if max_cycles >= 0:
+        return d, e, int(done.value)
+    if return_band:
+        return d, e, out, working_T(n, bw, tw)
+    return d, e
+
+
+def run_cycles(band: np.ndarray, bw: int, tw: int, order, compute: str | None = None):
+    """Runs the given (pass, R, k) cycles in order; returns the working band."""
+    band = np.asarray(band)
+    n = band.shape[0]
+    cdt = _np_dtype(compute) if compute else band.dtype
+    a = np.ascontiguousarray(band, dtype=cdt)
+    o = np.ascontiguousarray(np.asarray(order, dtype=np.int32).reshape(-1, 3))
+    out = np.zeros((n, working_ld(n, bw, tw)), dtype=cdt)
+    f = getattr(lib(), "bb_oracle_run_cycles_" + _suffix(cdt))
+    rc = f(a.ctypes.data, a.shape[1], n, bw, tw, o.ctypes.data, o.shape[0], out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected the cycle list (rc=%d)" % rc)
+    return out
+
+
+def band_to_dense(work: np.ndarray, T: int) -> np.ndarray:
+    """Dense n x n matrix from a working band (element (i,j) at [i, j-i+T])."""
+    n, ld = work.shape
+    A = np.zeros((n, n), dtype=work.dtype)
+    for i in range(n):
+        for o in range(ld):
+            j = i + o - T
+            if 0 <= j < n:
+                A[i, j] = work[i, o]
+    return A
