@@ -1,0 +1,68 @@
+"""Band -> bidiagonal reduction by Householder bulge chasing on MI355X (gfx950).
+
+The reduction runs in the HIP library ``libbb.so`` (C ABI in include/bb.h).
+This package is its thin Python binding: the ``bb_*`` functions mirror the C
+entry points, and :func:`reduce` wraps them for torch tensors (torch is used
+for device memory and the stream only).
+"""
+from __future__ import annotations
+
+from ._lib import (BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS, BBError,
+                   bb_device_status, bb_export_band, bb_plan, bb_plan_info, bb_reduce, bb_status_str, bb_tuning,
+                   bb_workspace_bytes, lib)
+
+__all__ = ["reduce", "export_band", "workspace", "tuning", "dtype_code", "bb_plan", "bb_workspace_bytes",
+           "bb_reduce", "bb_export_band", "bb_device_status", "bb_status_str", "BBError", "EXPORTS"]
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    if torch_dtype == torch.float32:
+        return BB_F32
+    if torch_dtype == torch.float64:
+        return BB_F64
+    raise TypeError("band must be float32 or float64")
+
+
+def tuning(scheduler: int = 0, stagger: int = 0, max_blocks: int = 0, threads_per_block: int = 0,
+           spin_limit: int = 0) -> bb_tuning:
+    return bb_tuning(scheduler, stagger, max_blocks, threads_per_block, spin_limit)
+
+
+def workspace(n: int, bw: int, tw: int, torch_dtype, device="cuda"):
+    """Device workspace for bb_reduce as a uint8 tensor."""
+    import torch
+    nbytes = bb_workspace_bytes(n, bw, tw, dtype_code(torch_dtype))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, stream=None):
+    """Reduces a device band (n, >= bw+1) float32/float64 tensor; returns (d, e).
+
+    Row i of ``band`` holds A(i, i..i+bw).  Runs on ``stream`` (default: the
+    current torch stream) asynchronously.  ``work`` may be a preallocated
+    workspace from :func:`workspace`.
+    """
+    import torch
+    if not band.is_cuda or band.dim() != 2 or band.stride(1) != 1:
+        raise ValueError("band must be a 2-D device tensor with unit column stride")
+    n = band.shape[0]
+    dt = dtype_code(band.dtype)
+    if work is None:
+        work = workspace(n, bw, tw, band.dtype, band.device)
+    d = torch.empty(n, dtype=band.dtype, device=band.device)
+    e = torch.empty(max(n - 1, 0), dtype=band.dtype, device=band.device)
+    s = stream if stream is not None else torch.cuda.current_stream(band.device)
+    bb_reduce(band.data_ptr(), band.stride(0), n, bw, tw, dt, d.data_ptr(), e.data_ptr() if n > 1 else 0,
+              work.data_ptr(), work.numel(), tun, s.cuda_stream)
+    return d, e
+
+
+def export_band(work, n: int, bw: int, tw: int, torch_dtype, stream=None):
+    """Working band left in ``work`` as an (n, ld) tensor and its sub offset."""
+    import torch
+    info = bb_plan(n, bw, tw, dtype_code(torch_dtype))
+    out = torch.empty((n, info.ld), dtype=torch_dtype, device=work.device)
+    s = stream if stream is not None else torch.cuda.current_stream(work.device)
+    bb_export_band(work.data_ptr(), n, bw, tw, dtype_code(torch_dtype), out.data_ptr(), s.cuda_stream)
+    return out, info.sub

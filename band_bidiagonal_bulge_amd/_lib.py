@@ -1,0 +1,102 @@
+"""ctypes binding of libbb.so: the C ABI of include/bb.h, same names.
+
+Argument marshalling only; every step of the reduction runs in the HIP
+kernels.  Loading fails loudly when the library has not been built: there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbb.so")
+
+BB_F32, BB_F64 = 0, 1
+BB_OK, BB_ERR_ARG, BB_ERR_WORKSPACE, BB_ERR_HIP, BB_ERR_UNSUPPORTED, BB_ERR_TIMEOUT = range(6)
+BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT = 0, 1, 2
+
+# Every symbol include/bb.h declares.
+EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_export_band", "bb_device_status", "bb_status_str")
+
+
+class bb_tuning(ctypes.Structure):
+    _fields_ = [("scheduler", ctypes.c_int32), ("stagger", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("threads_per_block", ctypes.c_int32), ("spin_limit", ctypes.c_int64)]
+
+
+class bb_plan_info(ctypes.Structure):
+    _fields_ = [("passes", ctypes.c_int32), ("ld", ctypes.c_int32), ("sub", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("sweeps", ctypes.c_int64), ("cycles", ctypes.c_int64),
+                ("steps", ctypes.c_int64), ("alg_bytes", ctypes.c_double), ("flops", ctypes.c_double)]
+
+
+class BBError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        L.bb_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(bb_plan_info)]
+        L.bb_workspace_bytes.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
+        L.bb_reduce.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, sz, ctypes.POINTER(bb_tuning), vp]
+        L.bb_export_band.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+        L.bb_device_status.argtypes = [vp, i64, i32, i32, i32, vp]
+        L.bb_status_str.argtypes = [i32]
+        L.bb_status_str.restype = ctypes.c_char_p
+        for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_export_band", "bb_device_status"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().bb_status_str(status).decode()
+
+
+def bb_plan(n: int, bw: int, tw: int, dtype: int) -> bb_plan_info:
+    out = bb_plan_info()
+    rc = lib().bb_plan(n, bw, tw, dtype, ctypes.byref(out))
+    if rc != BB_OK:
+        raise BBError(rc, "bb_plan")
+    return out
+
+
+def bb_workspace_bytes(n: int, bw: int, tw: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().bb_workspace_bytes(n, bw, tw, dtype, ctypes.byref(out))
+    if rc != BB_OK:
+        raise BBError(rc, "bb_workspace_bytes")
+    return int(out.value)
+
+
+def bb_reduce(band_ptr: int, ld_band: int, n: int, bw: int, tw: int, dtype: int, d_ptr: int, e_ptr: int,
+              work_ptr: int, work_bytes: int, tuning: bb_tuning | None, stream: int) -> None:
+    rc = lib().bb_reduce(band_ptr, ld_band, n, bw, tw, dtype, d_ptr, e_ptr or None, work_ptr, work_bytes,
+                         ctypes.byref(tuning) if tuning is not None else None, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_reduce")
+
+
+def bb_export_band(work_ptr: int, n: int, bw: int, tw: int, dtype: int, dst_ptr: int, stream: int) -> None:
+    rc = lib().bb_export_band(work_ptr, n, bw, tw, dtype, dst_ptr, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_export_band")
+
+
+def bb_device_status(work_ptr: int, n: int, bw: int, tw: int, dtype: int, stream: int) -> int:
+    return int(lib().bb_device_status(work_ptr, n, bw, tw, dtype, stream or None))
+
+
+def bb_status_str(status: int) -> str:
+    return status_str(status)

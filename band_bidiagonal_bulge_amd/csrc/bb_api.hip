@@ -1,0 +1,173 @@
+// C ABI of the band -> bidiagonal reduction (declared in include/bb.h):
+// argument validation, planning and the host side of the schedulers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "bb.h"
+#include "bb_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int32_t kMaxTile = 64;  // t+1 entries per row/column held in VGPRs
+
+bool valid_shape(int64_t n, int32_t bw, int32_t tw, int32_t dtype) {
+  if (dtype != BB_F32 && dtype != BB_F64) return false;
+  if (n < 1 || n > kMaxN || bw < 0 || tw < 1) return false;
+  if (bw > 4096) return false;
+  return true;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int pick_maxm(int32_t maxt) {
+  if (maxt + 1 <= 9) return 9;
+  if (maxt + 1 <= 17) return 17;
+  if (maxt + 1 <= 33) return 33;
+  return 65;
+}
+
+// Safe stagger for a pass: two cycles keep consecutive sweeps apart when the
+// target bandwidth b' exceeds 1, three always do (page: three-cycle
+// separation passage, R + n BW > R + 1 + BW + TW).
+int32_t stagger_for(const bb::Pass &p, int32_t requested) {
+  const int32_t safe = (p.b - p.t > 1) ? 2 : 3;
+  return std::max(requested, safe);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) {  // b > 0
+  return a >= 0 ? (a + b - 1) / b : -((-a) / b);
+}
+
+bb_status hip_status(hipError_t e) { return e == hipSuccess ? BB_OK : BB_ERR_HIP; }
+
+bb_status run_step_scheduler(void *wband, const bb::Geometry &g, const bb_tuning &tu, hipStream_t st) {
+  const int maxm = pick_maxm(g.maxt);
+  for (const bb::Pass &p : bb::pass_list(g.bw, g.tw)) {
+    const int64_t ns = bb::sweeps_of(g.n, p);
+    if (ns == 0) continue;
+    const int32_t s = stagger_for(p, tu.stagger);
+    int nt = tu.threads_per_block;
+    if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
+    const int64_t bp = p.b - p.t;
+    const int64_t steps = bb::steps_of(g.n, p, s);
+    for (int64_t L = 0; L < steps; ++L) {
+      // sweeps with 0 <= k = L - s R < K_R: R <= L/s and
+      // R (s b - 1) >= L b - (n - 2 - b')
+      const int64_t rhi = std::min(ns - 1, L / s);
+      const int64_t rlo = std::max<int64_t>(0, ceil_div(L * p.b - (g.n - 2 - bp), int64_t(s) * p.b - 1));
+      if (rhi < rlo) continue;
+      hipError_t e = bb::launch_step(maxm, wband, g, p.b, p.t, L, s, rlo, rhi - rlo + 1, nt, st);
+      if (e != hipSuccess) return BB_ERR_HIP;
+    }
+  }
+  return BB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bb_status bb_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, bb_plan_info *out) {
+  if (!out || !valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
+  bb_plan_info info;
+  std::memset(&info, 0, sizeof(info));
+  info.ld = g.ld;
+  info.sub = g.sub;
+  double bytes = 0, flops = 0;
+  for (const bb::Pass &p : bb::pass_list(bw, tw)) {
+    ++info.passes;
+    const int64_t ns = bb::sweeps_of(n, p);
+    info.sweeps += ns;
+    info.steps += bb::steps_of(n, p, 3);
+    for (int64_t R = 0; R < ns; ++R) {
+      const int64_t K = bb::cycles_of(n, p, R);
+      info.cycles += K;
+      for (int64_t k = 0; k < K; ++k) {
+        const bb::CycleShape cs = bb::cycle_shape(n, p, R, k);
+        bytes += 2.0 * double(cs.m) * double(cs.rows + cs.cols - cs.m) * g.esize;
+        // norm 2(m-1); per applied row/column: dot 2(m-1) + 2, update 2(m-1) + 1
+        flops += 2.0 * (2 * (cs.m - 1)) + double(cs.rows - 1 + cs.cols - 1) * (4.0 * (cs.m - 1) + 3.0);
+      }
+    }
+  }
+  info.alg_bytes = bytes;
+  info.flops = flops;
+  *out = info;
+  return BB_OK;
+}
+
+bb_status bb_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes) {
+  if (!bytes || !valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
+  if (g.maxt > kMaxTile) return BB_ERR_UNSUPPORTED;
+  *bytes = g.total_bytes;
+  return BB_OK;
+}
+
+bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
+                    void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream) {
+  if (!valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
+  if (g.maxt > kMaxTile) return BB_ERR_UNSUPPORTED;
+  if (!band || !d || !work || (n > 1 && !e) || ld_band < int64_t(bw) + 1) return BB_ERR_ARG;
+  if (!aligned(band, g.esize) || !aligned(d, g.esize) || (e && !aligned(e, g.esize)) || !aligned(work, 256))
+    return BB_ERR_ARG;
+  if (work_bytes < g.total_bytes) return BB_ERR_WORKSPACE;
+  bb_tuning tu;
+  std::memset(&tu, 0, sizeof(tu));
+  if (tuning) tu = *tuning;
+  if (tu.scheduler < 0 || tu.scheduler > BB_SCHED_STEP) return tu.scheduler == BB_SCHED_PERSISTENT ? BB_ERR_UNSUPPORTED : BB_ERR_ARG;
+  if (tu.stagger != 0 && (tu.stagger < 2 || tu.stagger > 64)) return BB_ERR_ARG;
+  if (tu.threads_per_block != 0 && (tu.threads_per_block < 64 || tu.threads_per_block > 256 ||
+                                    tu.threads_per_block % 64 != 0))
+    return BB_ERR_ARG;
+  if (tu.max_blocks < 0 || tu.spin_limit < 0) return BB_ERR_ARG;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void *wband = work;
+  uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
+  if (bb::launch_fill_u32(sync, int64_t(g.sync_words), 0u, st) != hipSuccess) return BB_ERR_HIP;
+  if (bb::launch_pack(band, ld_band, wband, g, st) != hipSuccess) return BB_ERR_HIP;
+  bb_status rc = run_step_scheduler(wband, g, tu, st);
+  if (rc != BB_OK) return rc;
+  return hip_status(bb::launch_extract(wband, g, d, n > 1 ? e : nullptr, st));
+}
+
+bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,
+                         void *stream) {
+  if (!valid_shape(n, bw, tw, dtype) || !work || !dst) return BB_ERR_ARG;
+  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
+  const size_t bytes = size_t(n) * size_t(g.ld) * size_t(g.esize);
+  return hip_status(hipMemcpyAsync(dst, work, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+}
+
+bb_status bb_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream) {
+  if (!valid_shape(n, bw, tw, dtype) || !work) return BB_ERR_ARG;
+  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return BB_ERR_HIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, static_cast<const char *>(work) + g.sync_offset, sizeof(word), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return BB_ERR_HIP;
+  return word == 0 ? BB_OK : BB_ERR_TIMEOUT;
+}
+
+const char *bb_status_str(int32_t status) {
+  switch (status) {
+    case BB_OK: return "ok";
+    case BB_ERR_ARG: return "invalid argument";
+    case BB_ERR_WORKSPACE: return "workspace too small";
+    case BB_ERR_HIP: return "HIP call or kernel launch failed";
+    case BB_ERR_UNSUPPORTED: return "unsupported shape (tile width above 64)";
+    case BB_ERR_TIMEOUT: return "device-side wait expired";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

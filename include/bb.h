@@ -1,0 +1,133 @@
+/*
+ * bb.h -- C ABI of the MI355X (gfx950) band -> bidiagonal reduction library.
+ *
+ * The library reduces an upper-banded n x n matrix A of bandwidth BW
+ * (A(i,j) != 0 only for 0 <= j-i <= BW) to upper bidiagonal form
+ * B = Q^T A P by Householder bulge chasing with successive band reduction:
+ * each pass removes t = min(TW, b-1) diagonals of the current bandwidth b,
+ * down to b = 1.  A sweep per row annihilates one group of the row and one
+ * group of the column it fills per cycle, and chases the bulge down the band;
+ * consecutive sweeps run concurrently under the page's non-overlap rule.
+ * Defined by the page "Accelerating Bidiagonalization of Banded Matrices
+ * through Memory-Aware Bulge-Chasing on GPUs" (three-cycle-separation
+ * passage; Algorithm 2 memory-strategy passage) and the page "A two-stage
+ * reduction on an Apple M5 Pro", section 6 (sweep s may run its step once
+ * sweep s-1 has finished the step two ahead).
+ *
+ * Conventions for every entry point:
+ *   - All pointers named "device" are HIP device pointers; "host" pointers
+ *     are ordinary host memory.  The caller owns every buffer and the stream;
+ *     the library allocates no device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; results are ready once the
+ *     stream has been synchronised.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns an error and enqueues nothing.  No C++ exception
+ *     crosses this interface.
+ *   - dtype is BB_F32 or BB_F64 and is both the storage and the arithmetic
+ *     precision of the reduction.
+ *   - Values are not checked for NaN/Inf; non-finite input propagates.
+ */
+#ifndef BB_H_
+#define BB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BB_F32 = 0, BB_F64 = 1 } bb_dtype;
+
+typedef enum {
+  BB_OK = 0,
+  BB_ERR_ARG = 1,          /* invalid size, pointer or dtype */
+  BB_ERR_WORKSPACE = 2,    /* work_bytes below bb_workspace_bytes() */
+  BB_ERR_HIP = 3,          /* a HIP call or kernel launch failed */
+  BB_ERR_UNSUPPORTED = 4,  /* valid but not implemented (tile width > 64) */
+  BB_ERR_TIMEOUT = 5       /* a device-side bounded wait expired */
+} bb_status;
+
+/* Schedulers of the sweeps (page: Algorithm 1 launches one kernel per cycle
+ * with kernel completion as the synchronisation). */
+typedef enum {
+  BB_SCHED_DEFAULT = 0,   /* the fastest scheduler for the shape */
+  BB_SCHED_STEP = 1,      /* one launch per step: step L runs every (R, k=L-s*R) */
+  BB_SCHED_PERSISTENT = 2 /* resident workgroups; per-sweep progress counters */
+} bb_scheduler;
+
+/* Optional tuning; pass NULL for the gfx950 defaults.  Zero fields take the
+ * default. */
+typedef struct {
+  int32_t scheduler;         /* bb_scheduler */
+  int32_t stagger;           /* cycles between consecutive sweeps: 0 = the
+                                smallest safe value (2 when the pass's target
+                                bandwidth b' > 1, else 3); 3 = always three */
+  int32_t max_blocks;        /* persistent: resident workgroups (0 = device fill) */
+  int32_t threads_per_block; /* 64..256, multiple of 64 (0 = default) */
+  int64_t spin_limit;        /* persistent: polls before BB_ERR_TIMEOUT (0 = default) */
+} bb_tuning;
+
+/* Host-side plan of a reduction (no device work). */
+typedef struct {
+  int32_t passes;     /* number of band-reduction passes */
+  int32_t ld;         /* stored diagonals per row of the working band */
+  int32_t sub;        /* sub-diagonals stored (fill below the diagonal) */
+  int32_t reserved;
+  int64_t sweeps;     /* sweeps over all passes */
+  int64_t cycles;     /* cycles over all passes */
+  int64_t steps;      /* dependent steps at three-cycle stagger, all passes */
+  double alg_bytes;   /* algorithmic bytes: per cycle, read + write of the
+                         union of its row block and column block */
+  double flops;       /* floating-point operations of all reflectors/applies */
+} bb_plan_info;
+
+/* Plan for (n, bw, tw, dtype).  out: host pointer.  Errors: BB_ERR_ARG. */
+bb_status bb_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, bb_plan_info *out);
+
+/* Bytes of device workspace bb_reduce needs (working band + counters).
+ * bytes: host pointer.  Errors: BB_ERR_ARG, BB_ERR_UNSUPPORTED. */
+bb_status bb_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes);
+
+/*
+ * Reduces the band to bidiagonal form.
+ *   band     device, read only: row i holds A(i, i+o) at band[i*ld_band + o],
+ *            o = 0..bw; entries with i+o >= n are ignored.
+ *   ld_band  >= bw + 1 (elements).
+ *   n >= 1, bw >= 0, tw >= 1 (clamped per pass to b-1).
+ *   d        device, n entries: d[i] = B(i,i).
+ *   e        device, n-1 entries: e[i] = B(i,i+1) (may be NULL when n == 1).
+ *            Signs are those the reflectors produce (not normalised).
+ *   work     device workspace of work_bytes >= bb_workspace_bytes(); its
+ *            contents on entry do not matter; it holds the working band and
+ *            the scheduler's counters afterwards.  Distinct concurrent calls
+ *            need distinct workspaces.
+ *   tuning   host pointer or NULL.
+ *   stream   hipStream_t as void*.
+ * bw <= 1 copies the band out.  Errors: BB_ERR_ARG, BB_ERR_WORKSPACE,
+ * BB_ERR_UNSUPPORTED, BB_ERR_HIP (launch failure).
+ */
+bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype,
+                    void *d, void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream);
+
+/* Copies the working band left in `work` by the last bb_reduce with the same
+ * (n, bw, tw, dtype) to dst (device, n * ld elements of dtype; element (i,j)
+ * at dst[i*ld + j-i+sub] with ld, sub from bb_plan).  Errors: BB_ERR_ARG,
+ * BB_ERR_HIP. */
+bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,
+                         void *stream);
+
+/* Synchronises `stream` and reports the device-side status word of the
+ * last bb_reduce on `work` (BB_OK or BB_ERR_TIMEOUT).  Errors: BB_ERR_ARG,
+ * BB_ERR_HIP. */
+bb_status bb_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream);
+
+/* Static description of a status code. */
+const char *bb_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BB_H_ */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+* libbb.so loads and exports every function include/bb.h declares;
+* bb_plan agrees with an independent enumeration of passes, sweeps and
+  cycles, and with the closed form of the algorithmic bytes per cycle;
+* invalid arguments are rejected on the host before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import band_bidiagonal_bulge_amd as bbm
+from band_bidiagonal_bulge_amd import _lib
+from refs import cycles_of_sweep, pass_list
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "bb.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:bb_status|const char \*)\s*(bb_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+    nm = os.popen("nm -D --defined-only " + _lib.LIB_PATH).read()
+    for name in names:
+        assert re.search(r"\bT " + name + r"\b", nm), name
+
+
+def test_status_strings():
+    for s in range(6):
+        assert bbm.bb_status_str(s) and bbm.bb_status_str(s) != "unknown status"
+    assert bbm.bb_status_str(99) == "unknown status"
+
+
+def _enumerate(n, bw, tw, esize):
+    cycles = sweeps = 0
+    nbytes = 0.0
+    for (b, t) in pass_list(bw, tw):
+        bp = b - t
+        ns = max(n - bp - 1, 0)
+        sweeps += ns
+        for R in range(ns):
+            K = cycles_of_sweep(n, b, t, R)
+            cycles += K
+            for k in range(K):
+                c = R + bp + k * b
+                ch = min(c + t, n - 1)
+                r = R if k == 0 else c - b
+                m = ch - c + 1
+                rows = ch - r + 1
+                cols = min(c + t + b, n - 1) - c + 1
+                nbytes += 2 * m * (rows + cols - m) * esize
+    return sweeps, cycles, nbytes
+
+
+@pytest.mark.parametrize("n,bw,tw,dt", [(512, 16, 8, 1), (300, 33, 7, 0), (97, 10, 20, 1), (5, 4, 2, 0)])
+def test_plan_matches_enumeration(n, bw, tw, dt):
+    info = bbm.bb_plan(n, bw, tw, dt)
+    sweeps, cycles, nbytes = _enumerate(n, bw, tw, 8 if dt == 1 else 4)
+    assert info.passes == len(pass_list(bw, tw))
+    assert info.sweeps == sweeps and info.cycles == cycles
+    assert abs(info.alg_bytes - nbytes) <= 1e-9 * nbytes
+    t0 = min(tw, bw - 1) if bw > 1 else 0
+    assert info.sub == t0 and info.ld == 2 * t0 + bw + 1
+
+
+def test_plan_headline_workload_counts():
+    # n = 16384, BW 64 -> 48 -> 32 -> 16 -> 1 with TW = 16, fp32
+    info = bbm.bb_plan(16384, 64, 16, 0)
+    assert info.passes == 4
+    assert info.sweeps == 16335 + 16351 + 16367 + 16382
+    assert info.cycles == 2092800 + 2793131 + 4193792 + 8394752
+    assert abs(info.alg_bytes / 1e9 - (41.11 + 42.78 + 46.07 + 51.47)) < 0.02
+
+
+def test_workspace_bytes_cover_band_and_counters():
+    n, bw, tw = 1000, 20, 6
+    nb = bbm.bb_workspace_bytes(n, bw, tw, 1)
+    info = bbm.bb_plan(n, bw, tw, 1)
+    assert nb >= n * info.ld * 8 + 4 * n
+    assert nb % 256 == 0
+
+
+def test_invalid_arguments_rejected_on_host():
+    L = _lib.lib()
+    sz = ctypes.c_size_t(0)
+    assert L.bb_workspace_bytes(0, 4, 2, 0, ctypes.byref(sz)) == _lib.BB_ERR_ARG
+    assert L.bb_workspace_bytes(10, -1, 2, 0, ctypes.byref(sz)) == _lib.BB_ERR_ARG
+    assert L.bb_workspace_bytes(10, 4, 0, 0, ctypes.byref(sz)) == _lib.BB_ERR_ARG
+    assert L.bb_workspace_bytes(10, 4, 2, 7, ctypes.byref(sz)) == _lib.BB_ERR_ARG
+    assert L.bb_workspace_bytes(10, 4, 2, 0, None) == _lib.BB_ERR_ARG
+    assert L.bb_workspace_bytes(1000, 200, 100, 0, ctypes.byref(sz)) == _lib.BB_ERR_UNSUPPORTED
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    # null band / d / e / work
+    assert L.bb_reduce(None, 5, 10, 4, 2, 0, fake, fake, fake, 1 << 20, None, None) == _lib.BB_ERR_ARG
+    assert L.bb_reduce(fake, 5, 10, 4, 2, 0, None, fake, fake, 1 << 20, None, None) == _lib.BB_ERR_ARG
+    assert L.bb_reduce(fake, 5, 10, 4, 2, 0, fake, None, fake, 1 << 20, None, None) == _lib.BB_ERR_ARG
+    assert L.bb_reduce(fake, 5, 10, 4, 2, 0, fake, fake, None, 1 << 20, None, None) == _lib.BB_ERR_ARG
+    # ld_band too small, misaligned pointers, workspace too small
+    assert L.bb_reduce(fake, 4, 10, 4, 2, 0, fake, fake, fake, 1 << 20, None, None) == _lib.BB_ERR_ARG
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L.bb_reduce(odd, 5, 10, 4, 2, 0, fake, fake, fake, 1 << 20, None, None) == _lib.BB_ERR_ARG
+    assert L.bb_reduce(fake, 5, 10, 4, 2, 0, fake, fake, fake, 16, None, None) == _lib.BB_ERR_WORKSPACE
+    # bad tuning
+    for bad in (_lib.bb_tuning(9, 0, 0, 0, 0), _lib.bb_tuning(1, 1, 0, 0, 0), _lib.bb_tuning(1, 0, 0, 100, 0),
+                _lib.bb_tuning(1, 0, -1, 0, 0), _lib.bb_tuning(1, 0, 0, 0, -5)):
+        assert L.bb_reduce(fake, 5, 10, 4, 2, 0, fake, fake, fake, 1 << 20, ctypes.byref(bad), None) == \
+            _lib.BB_ERR_ARG
+    # n = 1 needs no e
+    assert L.bb_reduce(fake, 5, 1, 4, 2, 0, fake, None, fake, 16, None, None) == _lib.BB_ERR_WORKSPACE
