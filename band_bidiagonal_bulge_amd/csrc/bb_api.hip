@@ -23,11 +23,30 @@ bool valid_shape(int64_t n, int32_t bw, int32_t tw, int32_t dtype) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int pick_maxm(int32_t maxt) {
-  if (maxt + 1 <= 9) return 9;
-  if (maxt + 1 <= 17) return 17;
-  if (maxt + 1 <= 33) return 33;
+// Register tile of a pass: t+1 entries per row/column.  Tiles of exactly
+// t+1 run without bounds in the inner loops for every interior cycle; other
+// widths use the next larger tile with guarded loops.
+int pick_maxm(int32_t t) {
+  switch (t + 1) {
+    case 8: case 9: case 16: case 17: case 32: case 33: case 64: case 65: return t + 1;
+    default: break;
+  }
+  if (t + 1 <= 9) return 9;
+  if (t + 1 <= 17) return 17;
+  if (t + 1 <= 33) return 33;
   return 65;
+}
+
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // gfx950 LDS available to one workgroup
+
+// Every pass must fit its staged row and column blocks in LDS and its band
+// in 31-bit byte offsets (buffer addressing).
+bool supported(const bb::Geometry &g) {
+  if (g.maxt > kMaxTile) return false;
+  if (uint64_t(g.n) * uint64_t(g.ld) * uint64_t(g.esize) >= (uint64_t(1) << 31)) return false;
+  for (const bb::Pass &p : bb::pass_list(g.bw, g.tw))
+    if (bb::stage_lds_bytes(g.dtype, pick_maxm(p.t), p.b, p.t) > kMaxLdsBytes) return false;
+  return true;
 }
 
 // Safe stagger for a pass: two cycles keep consecutive sweeps apart when the
@@ -45,8 +64,8 @@ int64_t ceil_div(int64_t a, int64_t b) {  // b > 0
 bb_status hip_status(hipError_t e) { return e == hipSuccess ? BB_OK : BB_ERR_HIP; }
 
 bb_status run_step_scheduler(void *wband, const bb::Geometry &g, const bb_tuning &tu, hipStream_t st) {
-  const int maxm = pick_maxm(g.maxt);
   for (const bb::Pass &p : bb::pass_list(g.bw, g.tw)) {
+    const int maxm = pick_maxm(p.t);
     const int64_t ns = bb::sweeps_of(g.n, p);
     if (ns == 0) continue;
     const int32_t s = stagger_for(p, tu.stagger);
@@ -63,6 +82,37 @@ bb_status run_step_scheduler(void *wband, const bb::Geometry &g, const bb_tuning
       hipError_t e = bb::launch_step(maxm, wband, g, p.b, p.t, L, s, rlo, rhi - rlo + 1, nt, st);
       if (e != hipSuccess) return BB_ERR_HIP;
     }
+  }
+  return BB_OK;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  return cus;
+}
+
+constexpr int64_t kDefaultSpin = int64_t(1) << 24;  // polls (~0.5 us each) before giving up
+
+bb_status run_persistent_scheduler(void *wband, const bb::Geometry &g, const bb_tuning &tu, uint32_t *sync,
+                                   hipStream_t st) {
+  const int cus = device_cus();
+  for (const bb::Pass &p : bb::pass_list(g.bw, g.tw)) {
+    const int maxm = pick_maxm(p.t);
+    const int64_t ns = bb::sweeps_of(g.n, p);
+    if (ns == 0) continue;
+    // claim counter and per-sweep progress start at zero for every pass
+    if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
+        bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
+      return BB_ERR_HIP;
+    int nt = tu.threads_per_block;
+    if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
+    int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(cus);
+    grid = std::min<int64_t>(grid, ns);
+    const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+    if (bb::launch_persist(maxm, wband, g, p.b, p.t, ns, sync, int(grid), nt, spin, st) != hipSuccess)
+      return BB_ERR_HIP;
   }
   return BB_OK;
 }
@@ -104,7 +154,7 @@ bb_status bb_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, bb_plan_info
 bb_status bb_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes) {
   if (!bytes || !valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
   const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
-  if (g.maxt > kMaxTile) return BB_ERR_UNSUPPORTED;
+  if (!supported(g)) return BB_ERR_UNSUPPORTED;
   *bytes = g.total_bytes;
   return BB_OK;
 }
@@ -113,7 +163,7 @@ bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, in
                     void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream) {
   if (!valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
   const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
-  if (g.maxt > kMaxTile) return BB_ERR_UNSUPPORTED;
+  if (!supported(g)) return BB_ERR_UNSUPPORTED;
   if (!band || !d || !work || (n > 1 && !e) || ld_band < int64_t(bw) + 1) return BB_ERR_ARG;
   if (!aligned(band, g.esize) || !aligned(d, g.esize) || (e && !aligned(e, g.esize)) || !aligned(work, 256))
     return BB_ERR_ARG;
@@ -121,7 +171,7 @@ bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, in
   bb_tuning tu;
   std::memset(&tu, 0, sizeof(tu));
   if (tuning) tu = *tuning;
-  if (tu.scheduler < 0 || tu.scheduler > BB_SCHED_STEP) return tu.scheduler == BB_SCHED_PERSISTENT ? BB_ERR_UNSUPPORTED : BB_ERR_ARG;
+  if (tu.scheduler < 0 || tu.scheduler > BB_SCHED_PERSISTENT) return BB_ERR_ARG;
   if (tu.stagger != 0 && (tu.stagger < 2 || tu.stagger > 64)) return BB_ERR_ARG;
   if (tu.threads_per_block != 0 && (tu.threads_per_block < 64 || tu.threads_per_block > 256 ||
                                     tu.threads_per_block % 64 != 0))
@@ -133,7 +183,8 @@ bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, in
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
   if (bb::launch_fill_u32(sync, int64_t(g.sync_words), 0u, st) != hipSuccess) return BB_ERR_HIP;
   if (bb::launch_pack(band, ld_band, wband, g, st) != hipSuccess) return BB_ERR_HIP;
-  bb_status rc = run_step_scheduler(wband, g, tu, st);
+  bb_status rc = tu.scheduler == BB_SCHED_STEP ? run_step_scheduler(wband, g, tu, st)
+                                                : run_persistent_scheduler(wband, g, tu, sync, st);
   if (rc != BB_OK) return rc;
   return hip_status(bb::launch_extract(wband, g, d, n > 1 ? e : nullptr, st));
 }
@@ -164,7 +215,7 @@ const char *bb_status_str(int32_t status) {
     case BB_ERR_ARG: return "invalid argument";
     case BB_ERR_WORKSPACE: return "workspace too small";
     case BB_ERR_HIP: return "HIP call or kernel launch failed";
-    case BB_ERR_UNSUPPORTED: return "unsupported shape (tile width above 64)";
+    case BB_ERR_UNSUPPORTED: return "unsupported shape (tile width above 64, or band too wide for LDS staging)";
     case BB_ERR_TIMEOUT: return "device-side wait expired";
     default: return "unknown status";
   }

@@ -18,4 +18,14 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t count, uint32_t v, hipStream_t s
 hipError_t launch_step(int maxm, void *wband, const Geometry &g, int b, int t, int64_t L, int s, int64_t Rlo,
                        int64_t nblk, int nt, hipStream_t st);
 
+// Persistent scheduler for one pass: `grid` workgroups of nt threads claim the
+// pass's sweeps in order; sync = the workspace's counter area (status word,
+// claim counter, per-sweep progress), claim and progress zeroed beforehand.
+hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
+                          int grid, int nt, int64_t spin_limit, hipStream_t st);
+
+// LDS bytes one workgroup stages per cycle for a pass (b, t) with register
+// tile maxm.
+size_t stage_lds_bytes(int dtype, int maxm, int b, int t);
+
 }  // namespace bb

@@ -25,6 +25,10 @@
 namespace bb {
 namespace {
 
+// s_waitcnt immediate with vmcnt = 0 and expcnt / lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ __forceinline__ double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
 __device__ __forceinline__ float sqrt_(float a) { return __builtin_sqrtf(a); }
@@ -37,14 +41,15 @@ struct Refl {
 };
 
 // Reflector of x[0..m-1] (x in LDS, read by every thread: broadcast).
-template <typename T, int MAXM>
+// FULL: m == MAXM, no bounds on the loop.
+template <typename T, int MAXM, bool FULL>
 __device__ __forceinline__ Refl<T> house(const T *x, int m) {
   Refl<T> h;
   const T alpha = x[0];
   T s = T(0);
 #pragma unroll
   for (int j = 1; j < MAXM; ++j)
-    if (j < m) s = fma_(x[j], x[j], s);
+    if (FULL || j < m) s = fma_(x[j], x[j], s);
   if (s == T(0)) {
     h.nz = false;
     h.beta = alpha;
@@ -60,110 +65,392 @@ __device__ __forceinline__ Refl<T> house(const T *x, int m) {
   return h;
 }
 
-// Band view: element (i, j) at a[i*ld + (j - i + sub)].
-template <typename T>
-struct BandRef {
-  T *a;
+// Band in memory through a buffer resource: element (i, j) at byte offset
+// (i*ld + j - i + sub) * sizeof(T).  Out-of-range loads return zero and
+// out-of-range stores are dropped by the hardware.  AUX is the cache policy:
+// 0 for ordinary accesses (one launch per step: the kernel boundary orders
+// the cycles), kSc1 for agent-scope accesses that stay coherent across the
+// XCDs' separate L2 caches (workgroups handing data to each other inside one
+// launch).
+constexpr int kSc1 = 16;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int AUX>
+struct Band {
+  __amdgpu_buffer_rsrc_t r;
   int64_t ld;
   int32_t sub;
   int64_t n;
-  __device__ __forceinline__ int64_t idx(int64_t i, int64_t j) const { return i * ld + (j - i + sub); }
+  __device__ __forceinline__ uint32_t off(int64_t i, int64_t j) const {
+    return uint32_t((i * ld + (j - i + sub)) * int64_t(sizeof(T)));
+  }
+  // byte offset of (i, j) and byte strides: next column +sizeof(T), next row
+  // (same column) +(ld-1)*sizeof(T)
+  __device__ __forceinline__ uint32_t row_step() const { return uint32_t((ld - 1) * int64_t(sizeof(T))); }
+  __device__ __forceinline__ T ld_(uint32_t o) const {
+    if constexpr (sizeof(T) == 4)
+      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, AUX));
+    else
+      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, AUX));
+  }
+  __device__ __forceinline__ u32x4 ld4_(uint32_t o) const { return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, AUX); }
+  __device__ __forceinline__ void st4_(uint32_t o, u32x4 v) const { __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, AUX); }
+  __device__ __forceinline__ void st_(uint32_t o, T v) const {
+    if constexpr (sizeof(T) == 4)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, o, 0, AUX);
+    else
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, o, 0, AUX);
+  }
 };
 
-// One cycle (R, k) of the pass (b, t), executed by the whole workgroup.
-// xs, ys: LDS vectors of MAXM entries.  The caller guarantees the cycle
-// exists (c <= n-2) and that no other workgroup touches its window.
-template <typename T, int MAXM>
-__device__ void block_cycle(const BandRef<T> A, int b, int t, int64_t R, int64_t k, T *xs, T *ys) {
-  const int64_t n = A.n;
-  const int64_t c = R + (b - t) + k * b;
-  const int64_t ch = c + t < n - 1 ? c + t : n - 1;
-  const int m = int(ch - c + 1);
-  const int64_t r = (k == 0) ? R : c - b;
-  const int tid = threadIdx.x;
-  const int nt = blockDim.x;
+template <typename T, int AUX>
+__device__ __forceinline__ Band<T, AUX> make_band(T *a, int64_t ld, int32_t sub, int64_t n) {
+  Band<T, AUX> B;
+  B.r = __builtin_amdgcn_make_buffer_rsrc(a, 0, int(uint32_t(n * ld * int64_t(sizeof(T)))), kRsrcWord3);
+  B.ld = ld;
+  B.sub = sub;
+  B.n = n;
+  return B;
+}
 
-  // 1. row reflector from A(r, c..ch), staged in LDS
-  if (tid < m) xs[tid] = A.a[A.idx(r, c + tid)];
-  __syncthreads();
-  const Refl<T> h = house<T, MAXM>(xs, m);
+// Geometry of cycle (R, k) of the pass (b, t).
+struct Cyc {
+  int64_t c, ch, r, jend;
+  int m;
+  __device__ __forceinline__ Cyc(int64_t n, int b, int t, int64_t R, int64_t k) {
+    c = R + (b - t) + k * b;
+    ch = c + t < n - 1 ? c + t : n - 1;
+    m = int(ch - c + 1);
+    r = (k == 0) ? R : c - b;
+    jend = c + t + b < n - 1 ? c + t + b : n - 1;
+  }
+};
 
-  // right apply: one row i = r+1..ch per thread, its m entries in VGPRs.
-  // Column c of rows c..ch (the next reflector's input) goes to LDS only;
-  // the column step writes it to memory.
-  for (int64_t i = r + 1 + tid; i <= ch; i += nt) {
-    T *p = A.a + A.idx(i, c);
-    T v[MAXM];
+// Vector access to the m <= MAXM consecutive entries of one band row segment
+// (16-byte loads/stores where they fit, a scalar tail otherwise).  A
+// full-width load may run past the segment: those values are never used, and
+// anything past the end of the band reads as zero (buffer bounds).
+
+template <typename T, int MAXM, class B>
+__device__ __forceinline__ void load_seg(const B &A, uint32_t o, T (&v)[MAXM]) {
+  constexpr int PER = 16 / int(sizeof(T));  // elements per 16-byte access
+#ifdef BB_SCALAR_SEG
+  constexpr int NV = 0;
+#else
+  constexpr int NV = MAXM / PER;
+#endif
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    // Reinterpret the whole 16-byte vector at once: per-component casts of
+    // the load builtin's result let the compiler shrink it to one dword.
+    typedef T vecT __attribute__((ext_vector_type(PER)));
+    const vecT x = __builtin_bit_cast(vecT, A.ld4_(o + uint32_t(q * 16)));
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[PER * q + j] = x[j];
+  }
+#pragma unroll
+  for (int j = NV * PER; j < MAXM; ++j) v[j] = A.ld_(o + uint32_t(j * sizeof(T)));
+}
+
+template <typename T, int MAXM, bool FULL, class B>
+__device__ __forceinline__ void store_seg(const B &A, uint32_t o, const T (&v)[MAXM], int m) {
+  constexpr int PER = 16 / int(sizeof(T));
+#ifdef BB_SCALAR_SEG
+  constexpr int NV = 0;
+#else
+  constexpr int NV = MAXM / PER;
+#endif
+  if (FULL) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      typedef T vecT __attribute__((ext_vector_type(PER)));
+      vecT y;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) y[j] = v[PER * q + j];
+      const u32x4 x = __builtin_bit_cast(u32x4, y);
+      A.st4_(o + uint32_t(q * 16), x);
+    }
+#pragma unroll
+    for (int j = NV * PER; j < MAXM; ++j) A.st_(o + uint32_t(j * sizeof(T)), v[j]);
+  } else {
 #pragma unroll
     for (int j = 0; j < MAXM; ++j)
-      if (j < m) v[j] = p[j];
-    if (h.nz) {
+      if (j < m) A.st_(o + uint32_t(j * sizeof(T)), v[j]);
+  }
+}
+
+// Row half of a cycle, executed by the whole workgroup: one band row per
+// thread, rows r..ch, each row's m entries (columns c..ch) loaded straight
+// into VGPRs with vector loads.  Row r is the reflector input: its thread
+// stages it in LDS (xs); every thread then forms the reflector and the
+// threads of rows r+1..ch apply it from the right.  Row r becomes (beta,
+// 0, ..., 0); column c of rows c..ch goes to LDS (ys) for the column half.
+template <typename T, int MAXM, bool FULL, class B>
+__device__ void row_half(const B &A, const Cyc &q, T *xs, T *ys) {
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int m = q.m;
+  const int nr = int(q.ch - q.r) + 1;
+  const uint32_t rstep = A.row_step();
+  const uint32_t o0 = A.off(q.r, q.c);
+  T v[MAXM];
+  if (tid < nr) load_seg<T, MAXM>(A, o0 + uint32_t(tid) * rstep, v);
+  if (tid == 0) {
+#pragma unroll
+    for (int j = 0; j < MAXM; ++j)
+      if (FULL || j < m) xs[j] = v[j];
+  }
+  __syncthreads();
+  const Refl<T> h = house<T, MAXM, FULL>(xs, m);
+  for (int i = tid; i < nr; i += nt) {
+    const uint32_t o = o0 + uint32_t(i) * rstep;
+    if (i != tid) load_seg<T, MAXM>(A, o, v);  // rows beyond the workgroup
+    if (i == 0) {
+      if (h.nz) v[0] = h.beta;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j) v[j] = T(0);
+    } else if (h.nz) {
       T s = T(0);
 #pragma unroll
       for (int j = 1; j < MAXM; ++j)
-        if (j < m) s = fma_(v[j], xs[j], s);
+        if (FULL || j < m) s = fma_(v[j], xs[j], s);
       const T w = fma_(s, h.inv, v[0]);
       const T tw = h.tau * w;
       v[0] = v[0] - tw;
 #pragma unroll
       for (int j = 1; j < MAXM; ++j)
-        if (j < m) v[j] = fma_(-tw, xs[j] * h.inv, v[j]);
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (j < m) p[j] = v[j];
+        if (FULL || j < m) v[j] = fma_(-tw, xs[j] * h.inv, v[j]);
     }
-    if (i >= c)
-      ys[i - c] = v[0];
-    else if (h.nz)
-      p[0] = v[0];
+    const int ic = i - int(q.c - q.r);  // row c + ic
+    if (ic >= 0) ys[ic] = v[0];
+    if (i == 0 || h.nz) store_seg<T, MAXM, FULL>(A, o, v, m);
   }
-  if (tid == nt - 1) {
-    if (h.nz) A.a[A.idx(r, c)] = h.beta;
-    for (int j = 1; j < m; ++j) A.a[A.idx(r, c + j)] = T(0);
-  }
-  __syncthreads();
+}
 
-  // 2. column reflector from the updated A(c..ch, c) in LDS
-  const Refl<T> g = house<T, MAXM>(ys, m);
-  const int64_t jend = c + t + b < n - 1 ? c + t + b : n - 1;
-  if (g.nz) {
-    const int64_t st = A.ld - 1;  // (c+i, j) sits i*(ld-1) after (c, j)
-    for (int64_t j = c + 1 + tid; j <= jend; j += nt) {
-      T *p = A.a + A.idx(c, j);
-      T v[MAXM];
+// Column half: one band column per thread, columns c..jend, each column's m
+// entries (rows c..ch, (ld-1) elements apart) loaded into VGPRs; threads of
+// consecutive columns touch consecutive words.  The reflector comes from the
+// updated column c in LDS (ys); columns c+1..jend are updated from the left
+// and column c becomes (beta, 0, ..., 0).
+template <typename T, int MAXM, bool FULL, class B>
+__device__ void col_half(const B &A, const Cyc &q, const T *ys) {
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int m = q.m;
+  const int nc = int(q.jend - q.c) + 1;
+  const uint32_t rstep = A.row_step();
+  const uint32_t o0 = A.off(q.c, q.c);
+  T v[MAXM];
+  if (tid >= 1 && tid < nc) {
 #pragma unroll
-      for (int i = 0; i < MAXM; ++i)
-        if (i < m) v[i] = p[i * st];
-      T s = T(0);
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (i < m) s = fma_(ys[i], v[i], s);
-      const T w = fma_(s, g.inv, v[0]);
-      const T tw = g.tau * w;
-      v[0] = v[0] - tw;
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (i < m) v[i] = fma_(-tw, ys[i] * g.inv, v[i]);
-#pragma unroll
-      for (int i = 0; i < MAXM; ++i)
-        if (i < m) p[i * st] = v[i];
+    for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o0 + uint32_t(tid) * uint32_t(sizeof(T)) + uint32_t(i) * rstep);
+  }
+  const Refl<T> g = house<T, MAXM, FULL>(ys, m);
+  for (int jj = tid; jj < nc; jj += nt) {
+    const uint32_t o = o0 + uint32_t(jj) * uint32_t(sizeof(T));
+    if (jj == 0) {
+      A.st_(o, g.nz ? g.beta : ys[0]);
+      for (int i = 1; i < m; ++i) A.st_(o + uint32_t(i) * rstep, T(0));
+      continue;
     }
+    if (!g.nz) continue;
+    if (jj != tid) {
+#pragma unroll
+      for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o + uint32_t(i) * rstep);
+    }
+    T s = T(0);
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) s = fma_(ys[i], v[i], s);
+    const T w = fma_(s, g.inv, v[0]);
+    const T tw = g.tau * w;
+    A.st_(o, v[0] - tw);
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) A.st_(o + uint32_t(i) * rstep, fma_(-tw, ys[i] * g.inv, v[i]));
   }
-  if (tid == nt - 1) {
-    A.a[A.idx(c, c)] = g.nz ? g.beta : ys[0];
-    for (int i = 1; i < m; ++i) A.a[A.idx(c + i, c)] = T(0);
-  }
+}
+
+template <typename T, int MAXM, class B>
+__device__ __forceinline__ void row_half_any(const B &A, const Cyc &q, T *xs, T *ys) {
+  if (q.m == MAXM)
+    row_half<T, MAXM, true>(A, q, xs, ys);
+  else
+    row_half<T, MAXM, false>(A, q, xs, ys);
+}
+
+template <typename T, int MAXM, class B>
+__device__ __forceinline__ void col_half_any(const B &A, const Cyc &q, const T *ys) {
+  if (q.m == MAXM)
+    col_half<T, MAXM, true>(A, q, ys);
+  else
+    col_half<T, MAXM, false>(A, q, ys);
 }
 
 // One launch per step L of a pass: block q runs sweep R = Rlo + q, cycle
 // k = L - s R (page: Algorithm 1, one kernel launch per cycle, kernel
 // completion as the synchronisation).
 template <typename T, int MAXM>
-__global__ void __launch_bounds__(256) k_step(BandRef<T> A, int b, int t, int64_t L, int s, int64_t Rlo) {
+__global__ void __launch_bounds__(256) k_step(T *a, int64_t ld, int32_t sub, int64_t n, int b, int t, int64_t L,
+                                              int s, int64_t Rlo) {
   __shared__ T xs[MAXM];
   __shared__ T ys[MAXM];
+  const Band<T, 0> A = make_band<T, 0>(a, ld, sub, n);
   const int64_t R = Rlo + blockIdx.x;
-  block_cycle<T, MAXM>(A, b, t, R, L - int64_t(s) * R, xs, ys);
+  const Cyc q(n, b, t, R, L - int64_t(s) * R);
+  row_half_any<T, MAXM>(A, q, xs, ys);
+  // the column half reloads cells the row half just stored
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  col_half_any<T, MAXM>(A, q, ys);
+}
+
+// Cycles of sweep R: k = 0 .. K-1 with R + b' + k b <= n-2.
+__device__ __forceinline__ int64_t cycles_of_dev(int64_t n, int b, int t, int64_t R) {
+  const int64_t last = n - 2 - R - (b - t);
+  return last < 0 ? 0 : last / b + 1;
+}
+
+// Half-cycles of sweep R-1 that must be complete before half h of cycle k of
+// sweep R may start.  Half-cycles are numbered 2k (row half) and 2k+1
+// (column half).  A lag of d = 2 half-cycles suffices when b' >= 3, 3 when
+// b' = 2 and 4 when b' = 1 (the page's rule: two cycles of separation only
+// when the target band is wider than bidiagonal), capped at all of R-1.  The
+// cap is only sound because a sweep publishes its final count after its
+// predecessor has published its own: "sweep R-1 complete" then implies
+// "every earlier sweep complete", which the truncated windows at the last
+// column need (there sweeps further back than R-1 still overlap).
+__device__ __forceinline__ int64_t half_cycles_needed(int b, int t, int64_t k, int h, int64_t kprev) {
+  const int bp = b - t;
+  const int d = bp >= 3 ? 2 : (bp == 2 ? 3 : 4);
+  const int64_t all = 2 * kprev;
+  const int64_t need = 2 * k + h + d;
+  return need < all ? need : all;
+}
+
+// Bounded poll of a progress counter (one thread).  Returns false, after
+// setting the status word, when spin_limit polls pass without the counter
+// reaching `need`.
+__device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t need, int64_t spin_limit,
+                                              uint32_t *status) {
+  int64_t polls = 0;
+  while (__hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++polls > spin_limit) {
+      __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+  return true;
+}
+
+// Persistent scheduler: each workgroup claims sweeps in increasing order
+// (an atomic counter), and runs all cycles of its sweep; before each half
+// cycle it waits on its predecessor's progress counter, after it publishes
+// its own.  Claims are monotone, so every sweep waited on is held by a
+// running workgroup: no deadlock for any grid size.  Waits are bounded by
+// spin_limit polls; on expiry the workgroup sets the status word and stops,
+// and so, in turn, do its successors.
+//
+// AUX selects how band data crosses between workgroups (and XCDs, whose L2
+// caches are not coherent with each other): kSc1 makes every band access an
+// agent-coherent one, so completing the stores (vmcnt 0) before the counter
+// moves is the whole release; 0 uses ordinary cached accesses with an
+// agent-scope release fence (L2 write-back) before each publish and an
+// acquire fence (invalidate) after each wait.
+#ifndef BB_PERSIST_AUX
+#define BB_PERSIST_AUX 16
+#endif
+template <typename T, int MAXM, int AUX>
+__global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, int64_t n, int b, int t,
+                                                 int64_t nsweeps, uint32_t *sync, int64_t spin_limit) {
+  const Band<T, AUX> A = make_band<T, AUX>(a, ld, sub, n);
+  __shared__ T xs[MAXM];
+  __shared__ T ys[MAXM];
+  __shared__ int64_t sR;
+  __shared__ int sgo;
+  uint32_t *status = sync;
+  uint32_t *claim = sync + kClaim;
+  uint32_t *prog = sync + kSyncHeader;
+  const int tid = threadIdx.x;
+#ifdef BB_PROFILE
+  // wall-clock ticks spent waiting, in row halves, column halves, publishing
+  uint64_t t_wait = 0, t_row = 0, t_col = 0, t_pub = 0, n_half = 0, t_mark = 0;
+  unsigned long long *prof = reinterpret_cast<unsigned long long *>(sync + kProf);
+#define BB_TICK(acc)                        \
+  do {                                      \
+    const uint64_t now_ = wall_clock64();   \
+    acc += now_ - t_mark;                   \
+    t_mark = now_;                          \
+  } while (0)
+#else
+#define BB_TICK(acc) \
+  do {               \
+  } while (0)
+#endif
+  if (tid == 0) sgo = 1;
+  for (;;) {
+    if (tid == 0) sR = int64_t(atomicAdd(claim, 1u));
+    __syncthreads();
+    const int64_t R = sR;
+    if (R >= nsweeps || !sgo) break;
+    const int64_t K = cycles_of_dev(A.n, b, t, R);
+    const int64_t Kp = R > 0 ? cycles_of_dev(A.n, b, t, R - 1) : 0;
+    const uint32_t *pred = prog + (R - 1) * kLine;
+    for (int64_t k = 0; k < K; ++k) {
+      const Cyc q(A.n, b, t, R, k);
+      for (int h = 0; h < 2; ++h) {
+#ifdef BB_PROFILE
+        t_mark = wall_clock64();
+        ++n_half;
+#endif
+        if (R > 0) {
+          if (tid == 0) {
+            sgo = wait_progress(pred, uint32_t(half_cycles_needed(b, t, k, h, Kp)), spin_limit, status);
+            if (AUX == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          }
+          __syncthreads();
+          if (!sgo) return;
+        }
+        BB_TICK(t_wait);
+        if (h == 0) {
+          row_half_any<T, MAXM>(A, q, xs, ys);
+          BB_TICK(t_row);
+        } else {
+          col_half_any<T, MAXM>(A, q, ys);
+          BB_TICK(t_col);
+        }
+        // Publish: every wave's stores complete, then one thread moves the
+        // counter.  The final count waits for the predecessor's final count.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (tid == 0) {
+          bool go = true;
+          if (R > 0 && h == 1 && k == K - 1) go = wait_progress(pred, uint32_t(2 * Kp), spin_limit, status);
+          if (AUX == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          if (go)
+            __hip_atomic_store(prog + R * kLine, uint32_t(2 * k + h + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            sgo = 0;  // the final count never moves: successors time out in turn
+        }
+        BB_TICK(t_pub);
+      }
+    }
+    __syncthreads();  // sR is rewritten by the next claim
+  }
+#ifdef BB_PROFILE
+  if (tid == 0) {
+    atomicAdd(prof + 0, (unsigned long long)t_wait);
+    atomicAdd(prof + 1, (unsigned long long)t_row);
+    atomicAdd(prof + 2, (unsigned long long)t_col);
+    atomicAdd(prof + 3, (unsigned long long)t_pub);
+    atomicAdd(prof + 4, (unsigned long long)n_half);
+  }
+#endif
+#undef BB_TICK
 }
 
 // User band (row-offset layout) -> working band with zeroed bulge room.
@@ -205,8 +492,9 @@ inline unsigned grid_for(int64_t work, int block) {
 template <typename T, int MAXM>
 hipError_t step_t(void *wband, const Geometry &g, int b, int t, int64_t L, int s, int64_t Rlo, int64_t nblk,
                   int nt, hipStream_t st) {
-  BandRef<T> A{static_cast<T *>(wband), g.ld, g.sub, g.n};
-  hipLaunchKernelGGL((k_step<T, MAXM>), dim3(unsigned(nblk)), dim3(nt), 0, st, A, b, t, L, s, Rlo);
+  hipLaunchKernelGGL((k_step<T, MAXM>), dim3(unsigned(nblk)), dim3(nt), 0, st,
+                     static_cast<T *>(wband),
+                     int64_t(g.ld), g.sub, g.n, b, t, L, s, Rlo);
   return hipGetLastError();
 }
 
@@ -214,15 +502,56 @@ template <typename T>
 hipError_t step_dispatch(int maxm, void *wband, const Geometry &g, int b, int t, int64_t L, int s, int64_t Rlo,
                          int64_t nblk, int nt, hipStream_t st) {
   switch (maxm) {
+    case 8: return step_t<T, 8>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
     case 9: return step_t<T, 9>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
+    case 16: return step_t<T, 16>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
     case 17: return step_t<T, 17>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
+    case 32: return step_t<T, 32>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
     case 33: return step_t<T, 33>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
+    case 64: return step_t<T, 64>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
     case 65: return step_t<T, 65>(wband, g, b, t, L, s, Rlo, nblk, nt, st);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <typename T, int MAXM>
+hipError_t persist_t(void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync, int grid,
+                     int nt, int64_t spin_limit, hipStream_t st) {
+  hipLaunchKernelGGL((k_persist<T, MAXM, BB_PERSIST_AUX>), dim3(unsigned(grid)), dim3(nt), 0, st,
+                     static_cast<T *>(wband),
+                     int64_t(g.ld), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t persist_dispatch(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
+                            int grid, int nt, int64_t spin_limit, hipStream_t st) {
+  switch (maxm) {
+    case 8: return persist_t<T, 8>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    case 9: return persist_t<T, 9>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    case 16: return persist_t<T, 16>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    case 17: return persist_t<T, 17>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    case 32: return persist_t<T, 32>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    case 33: return persist_t<T, 33>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    case 64: return persist_t<T, 64>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    case 65: return persist_t<T, 65>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+size_t stage_lds_bytes(int dtype, int maxm, int b, int t) {
+  (void)b;
+  (void)t;
+  return size_t(2 * maxm) * (dtype == 1 ? 8 : 4);
+}
+
+hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
+                          int grid, int nt, int64_t spin_limit, hipStream_t st) {
+  if (g.dtype == 1) return persist_dispatch<double>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+  return persist_dispatch<float>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+}
 
 hipError_t launch_pack(const void *band, int64_t ld_band, void *wband, const Geometry &g, hipStream_t st) {
   const int block = 256;

@@ -66,9 +66,15 @@ struct Geometry {
   size_t total_bytes = 0;
 };
 
-// Counter area (32-bit words): [0] device status, [1..63] reserved,
-// [64 ...] one progress word per sweep.
-constexpr int64_t kSyncHeader = 64;
+// Counter area (32-bit words).  Every counter that one workgroup writes and
+// others poll sits alone in a 128-byte cache line (kLine words), so a store
+// to one never disturbs the line another workgroup is polling:
+//   [0] device status; [kClaim] sweep claim counter; [kProf ..] profiling
+//   counters (instrumented builds); [kSyncHeader + R*kLine] progress of sweep R.
+constexpr int64_t kLine = 32;
+constexpr int64_t kClaim = kLine;
+constexpr int64_t kProf = 2 * kLine;
+constexpr int64_t kSyncHeader = 4 * kLine;
 
 inline Geometry make_geometry(int64_t n, int32_t bw, int32_t tw, int32_t dtype) {
   Geometry g;
@@ -82,7 +88,7 @@ inline Geometry make_geometry(int64_t n, int32_t bw, int32_t tw, int32_t dtype) 
   g.ld = g.sub + bw + g.maxt + 1;
   g.band_bytes = (size_t(n) * size_t(g.ld) * size_t(g.esize) + 255) / 256 * 256;
   g.sync_offset = g.band_bytes;
-  g.sync_words = size_t(kSyncHeader + n + 64);
+  g.sync_words = size_t(kSyncHeader + (n + 1) * kLine);
   g.total_bytes = g.sync_offset + (g.sync_words * 4 + 255) / 256 * 256;
   return g;
 }

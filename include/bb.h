@@ -45,7 +45,9 @@ typedef enum {
   BB_ERR_ARG = 1,          /* invalid size, pointer or dtype */
   BB_ERR_WORKSPACE = 2,    /* work_bytes below bb_workspace_bytes() */
   BB_ERR_HIP = 3,          /* a HIP call or kernel launch failed */
-  BB_ERR_UNSUPPORTED = 4,  /* valid but not implemented (tile width > 64) */
+  BB_ERR_UNSUPPORTED = 4,  /* valid but not implemented: tile width > 64, a
+                              pass whose (b+t+1) x (t+1) blocks exceed LDS,
+                              or a band of 2 GiB or more */
   BB_ERR_TIMEOUT = 5       /* a device-side bounded wait expired */
 } bb_status;
 

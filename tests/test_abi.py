@@ -85,7 +85,7 @@ def test_workspace_bytes_cover_band_and_counters():
     n, bw, tw = 1000, 20, 6
     nb = bbm.bb_workspace_bytes(n, bw, tw, 1)
     info = bbm.bb_plan(n, bw, tw, 1)
-    assert nb >= n * info.ld * 8 + 4 * n
+    assert nb >= n * info.ld * 8 + 128 * n
     assert nb % 256 == 0
 
 

@@ -81,13 +81,39 @@ def test_all_zero_and_zero_rows(dt):
     _check_bitwise(band, bw, tw)
 
 
-@pytest.mark.parametrize("tun", [dict(stagger=3), dict(threads_per_block=64), dict(threads_per_block=128),
-                                 dict(scheduler=1, stagger=2)])
-def test_scheduler_variants_bitwise(tun):
-    n, bw, tw = 900, 48, 16
-    log(f"variant {tun}")
-    band = bb_inputs.make_band(n, bw, "f32", "normal", seed=5)
+STEP, PERSIST = 1, 2
+
+
+@pytest.mark.parametrize("tun", [dict(scheduler=STEP), dict(scheduler=STEP, stagger=3),
+                                 dict(scheduler=STEP, threads_per_block=64),
+                                 dict(scheduler=PERSIST), dict(scheduler=PERSIST, max_blocks=1),
+                                 dict(scheduler=PERSIST, max_blocks=2), dict(scheduler=PERSIST, max_blocks=7),
+                                 dict(scheduler=PERSIST, threads_per_block=64),
+                                 dict(scheduler=PERSIST, threads_per_block=256, max_blocks=1000)])
+@pytest.mark.parametrize("n,bw,tw,dt", [(900, 48, 16, "f32"), (700, 24, 7, "f64"), (400, 9, 2, "f32")])
+def test_scheduler_variants_bitwise(tun, n, bw, tw, dt):
+    log(f"variant {tun} n={n} bw={bw} tw={tw} {dt}")
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=5)
     _check_bitwise(band, bw, tw, bbm.tuning(**tun))
+
+
+def test_forced_timeout_reports_status():
+    # A spin limit of one poll makes the first wait on a predecessor expire;
+    # every workgroup then stops and the launch ends normally.
+    import torch
+    n, bw, tw = 3000, 32, 16
+    band = torch.from_numpy(bb_inputs.make_band(n, bw, "f32", "normal", seed=2)).to("cuda:0")
+    work = bbm.workspace(n, bw, tw, band.dtype)
+    log("forced timeout")
+    bbm.reduce(band, bw, tw, bbm.tuning(scheduler=PERSIST, spin_limit=1), work)
+    st = bbm.bb_device_status(work.data_ptr(), n, bw, tw, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == 5, bbm.bb_status_str(st)
+    # the next normal call on the same workspace clears the status
+    d, e = bbm.reduce(band, bw, tw, None, work)
+    st = bbm.bb_device_status(work.data_ptr(), n, bw, tw, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    od, oe = oracle.reduce(band.cpu().numpy(), bw, tw)
+    np.testing.assert_array_equal(d.cpu().numpy(), od)
 
 
 def test_repeated_calls_reuse_workspace():
