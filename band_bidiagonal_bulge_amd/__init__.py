@@ -8,11 +8,11 @@ for device memory and the stream only).
 from __future__ import annotations
 
 from ._lib import (BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS, BBError,
-                   bb_device_status, bb_export_band, bb_plan, bb_plan_info, bb_reduce, bb_status_str, bb_tuning,
-                   bb_workspace_bytes, lib)
+                   bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
+                   bb_run_pass, bb_status_str, bb_tuning, bb_workspace_bytes, lib)
 
 __all__ = ["reduce", "export_band", "workspace", "tuning", "dtype_code", "bb_plan", "bb_workspace_bytes",
-           "bb_reduce", "bb_export_band", "bb_device_status", "bb_status_str", "BBError", "EXPORTS"]
+           "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band", "bb_device_status", "bb_status_str", "BBError", "EXPORTS"]
 
 
 def dtype_code(torch_dtype) -> int:

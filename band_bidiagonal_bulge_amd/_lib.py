@@ -17,7 +17,8 @@ BB_OK, BB_ERR_ARG, BB_ERR_WORKSPACE, BB_ERR_HIP, BB_ERR_UNSUPPORTED, BB_ERR_TIME
 BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT = 0, 1, 2
 
 # Every symbol include/bb.h declares.
-EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_export_band", "bb_device_status", "bb_status_str")
+EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band",
+           "bb_device_status", "bb_status_str")
 
 
 class bb_tuning(ctypes.Structure):
@@ -50,11 +51,15 @@ def lib():
         L.bb_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(bb_plan_info)]
         L.bb_workspace_bytes.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
         L.bb_reduce.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, sz, ctypes.POINTER(bb_tuning), vp]
+        L.bb_pack.argtypes = [vp, i64, i64, i32, i32, i32, vp, sz, vp]
+        L.bb_run_pass.argtypes = [i64, i32, i32, i32, i32, vp, sz, ctypes.POINTER(bb_tuning), vp]
+        L.bb_extract.argtypes = [vp, sz, i64, i32, i32, i32, vp, vp, vp]
         L.bb_export_band.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         L.bb_device_status.argtypes = [vp, i64, i32, i32, i32, vp]
         L.bb_status_str.argtypes = [i32]
         L.bb_status_str.restype = ctypes.c_char_p
-        for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_export_band", "bb_device_status"):
+        for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract",
+                  "bb_export_band", "bb_device_status"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -86,6 +91,28 @@ def bb_reduce(band_ptr: int, ld_band: int, n: int, bw: int, tw: int, dtype: int,
                          ctypes.byref(tuning) if tuning is not None else None, stream or None)
     if rc != BB_OK:
         raise BBError(rc, "bb_reduce")
+
+
+def bb_pack(band_ptr: int, ld_band: int, n: int, bw: int, tw: int, dtype: int, work_ptr: int, work_bytes: int,
+            stream: int) -> None:
+    rc = lib().bb_pack(band_ptr, ld_band, n, bw, tw, dtype, work_ptr, work_bytes, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_pack")
+
+
+def bb_run_pass(n: int, bw: int, tw: int, dtype: int, pass_index: int, work_ptr: int, work_bytes: int,
+                tuning: bb_tuning | None, stream: int) -> None:
+    rc = lib().bb_run_pass(n, bw, tw, dtype, pass_index, work_ptr, work_bytes,
+                           ctypes.byref(tuning) if tuning is not None else None, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_run_pass")
+
+
+def bb_extract(work_ptr: int, work_bytes: int, n: int, bw: int, tw: int, dtype: int, d_ptr: int, e_ptr: int,
+               stream: int) -> None:
+    rc = lib().bb_extract(work_ptr, work_bytes, n, bw, tw, dtype, d_ptr, e_ptr or None, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_extract")
 
 
 def bb_export_band(work_ptr: int, n: int, bw: int, tw: int, dtype: int, dst_ptr: int, stream: int) -> None:

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "bb.h"
 #include "bb_internal.hpp"
@@ -63,25 +64,23 @@ int64_t ceil_div(int64_t a, int64_t b) {  // b > 0
 
 bb_status hip_status(hipError_t e) { return e == hipSuccess ? BB_OK : BB_ERR_HIP; }
 
-bb_status run_step_scheduler(void *wband, const bb::Geometry &g, const bb_tuning &tu, hipStream_t st) {
-  for (const bb::Pass &p : bb::pass_list(g.bw, g.tw)) {
-    const int maxm = pick_maxm(p.t);
-    const int64_t ns = bb::sweeps_of(g.n, p);
-    if (ns == 0) continue;
-    const int32_t s = stagger_for(p, tu.stagger);
-    int nt = tu.threads_per_block;
-    if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
-    const int64_t bp = p.b - p.t;
-    const int64_t steps = bb::steps_of(g.n, p, s);
-    for (int64_t L = 0; L < steps; ++L) {
-      // sweeps with 0 <= k = L - s R < K_R: R <= L/s and
-      // R (s b - 1) >= L b - (n - 2 - b')
-      const int64_t rhi = std::min(ns - 1, L / s);
-      const int64_t rlo = std::max<int64_t>(0, ceil_div(L * p.b - (g.n - 2 - bp), int64_t(s) * p.b - 1));
-      if (rhi < rlo) continue;
-      hipError_t e = bb::launch_step(maxm, wband, g, p.b, p.t, L, s, rlo, rhi - rlo + 1, nt, st);
-      if (e != hipSuccess) return BB_ERR_HIP;
-    }
+bb_status run_step_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
+                        hipStream_t st) {
+  const int maxm = pick_maxm(p.t);
+  const int64_t ns = bb::sweeps_of(g.n, p);
+  if (ns == 0) return BB_OK;
+  const int32_t s = stagger_for(p, tu.stagger);
+  int nt = tu.threads_per_block;
+  if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
+  const int64_t bp = p.b - p.t;
+  const int64_t steps = bb::steps_of(g.n, p, s);
+  for (int64_t L = 0; L < steps; ++L) {
+    // sweeps with 0 <= k = L - s R < K_R: R <= L/s and
+    // R (s b - 1) >= L b - (n - 2 - b')
+    const int64_t rhi = std::min(ns - 1, L / s);
+    const int64_t rlo = std::max<int64_t>(0, ceil_div(L * p.b - (g.n - 2 - bp), int64_t(s) * p.b - 1));
+    if (rhi < rlo) continue;
+    if (bb::launch_step(maxm, wband, g, p.b, p.t, L, s, rlo, rhi - rlo + 1, nt, st) != hipSuccess) return BB_ERR_HIP;
   }
   return BB_OK;
 }
@@ -95,26 +94,52 @@ int device_cus() {
 
 constexpr int64_t kDefaultSpin = int64_t(1) << 24;  // polls (~0.5 us each) before giving up
 
-bb_status run_persistent_scheduler(void *wband, const bb::Geometry &g, const bb_tuning &tu, uint32_t *sync,
-                                   hipStream_t st) {
-  const int cus = device_cus();
-  for (const bb::Pass &p : bb::pass_list(g.bw, g.tw)) {
-    const int maxm = pick_maxm(p.t);
-    const int64_t ns = bb::sweeps_of(g.n, p);
-    if (ns == 0) continue;
-    // claim counter and per-sweep progress start at zero for every pass
-    if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
-        bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
-      return BB_ERR_HIP;
-    int nt = tu.threads_per_block;
-    if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
-    int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(cus);
-    grid = std::min<int64_t>(grid, ns);
-    const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
-    if (bb::launch_persist(maxm, wband, g, p.b, p.t, ns, sync, int(grid), nt, spin, st) != hipSuccess)
-      return BB_ERR_HIP;
-  }
+bb_status run_persistent_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
+                              uint32_t *sync, hipStream_t st) {
+  const int maxm = pick_maxm(p.t);
+  const int64_t ns = bb::sweeps_of(g.n, p);
+  if (ns == 0) return BB_OK;
+  // claim counter and per-sweep progress start at zero for every pass
+  if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
+      bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
+    return BB_ERR_HIP;
+  int nt = tu.threads_per_block;
+  if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
+  int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(device_cus());
+  grid = std::min<int64_t>(grid, ns);
+  const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+  if (bb::launch_persist(maxm, wband, g, p.b, p.t, ns, sync, int(grid), nt, spin, st) != hipSuccess)
+    return BB_ERR_HIP;
   return BB_OK;
+}
+
+// Shared validation of the workspace-level entry points.
+bb_status check_work(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const void *work, size_t work_bytes,
+                     bb::Geometry *g) {
+  if (!valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  *g = bb::make_geometry(n, bw, tw, dtype);
+  if (!supported(*g)) return BB_ERR_UNSUPPORTED;
+  if (!work || !aligned(work, 256)) return BB_ERR_ARG;
+  if (work_bytes < g->total_bytes) return BB_ERR_WORKSPACE;
+  return BB_OK;
+}
+
+bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
+  std::memset(tu, 0, sizeof(*tu));
+  if (tuning) *tu = *tuning;
+  if (tu->scheduler < 0 || tu->scheduler > BB_SCHED_PERSISTENT) return BB_ERR_ARG;
+  if (tu->stagger != 0 && (tu->stagger < 2 || tu->stagger > 64)) return BB_ERR_ARG;
+  if (tu->threads_per_block != 0 && (tu->threads_per_block < 64 || tu->threads_per_block > 256 ||
+                                     tu->threads_per_block % 64 != 0))
+    return BB_ERR_ARG;
+  if (tu->max_blocks < 0 || tu->spin_limit < 0) return BB_ERR_ARG;
+  return BB_OK;
+}
+
+bb_status run_pass(void *work, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu, hipStream_t st) {
+  uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
+  return tu.scheduler == BB_SCHED_STEP ? run_step_pass(work, g, p, tu, st)
+                                       : run_persistent_pass(work, g, p, tu, sync, st);
 }
 
 }  // namespace
@@ -159,34 +184,55 @@ bb_status bb_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, s
   return BB_OK;
 }
 
-bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
-                    void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream) {
-  if (!valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
-  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
-  if (!supported(g)) return BB_ERR_UNSUPPORTED;
-  if (!band || !d || !work || (n > 1 && !e) || ld_band < int64_t(bw) + 1) return BB_ERR_ARG;
-  if (!aligned(band, g.esize) || !aligned(d, g.esize) || (e && !aligned(e, g.esize)) || !aligned(work, 256))
-    return BB_ERR_ARG;
-  if (work_bytes < g.total_bytes) return BB_ERR_WORKSPACE;
-  bb_tuning tu;
-  std::memset(&tu, 0, sizeof(tu));
-  if (tuning) tu = *tuning;
-  if (tu.scheduler < 0 || tu.scheduler > BB_SCHED_PERSISTENT) return BB_ERR_ARG;
-  if (tu.stagger != 0 && (tu.stagger < 2 || tu.stagger > 64)) return BB_ERR_ARG;
-  if (tu.threads_per_block != 0 && (tu.threads_per_block < 64 || tu.threads_per_block > 256 ||
-                                    tu.threads_per_block % 64 != 0))
-    return BB_ERR_ARG;
-  if (tu.max_blocks < 0 || tu.spin_limit < 0) return BB_ERR_ARG;
-
+bb_status bb_pack(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *work,
+                  size_t work_bytes, void *stream) {
+  bb::Geometry g;
+  const bb_status rc = check_work(n, bw, tw, dtype, work, work_bytes, &g);
+  if (rc != BB_OK) return rc;
+  if (!band || ld_band < int64_t(bw) + 1 || !aligned(band, g.esize)) return BB_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  void *wband = work;
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
   if (bb::launch_fill_u32(sync, int64_t(g.sync_words), 0u, st) != hipSuccess) return BB_ERR_HIP;
-  if (bb::launch_pack(band, ld_band, wband, g, st) != hipSuccess) return BB_ERR_HIP;
-  bb_status rc = tu.scheduler == BB_SCHED_STEP ? run_step_scheduler(wband, g, tu, st)
-                                                : run_persistent_scheduler(wband, g, tu, sync, st);
+  return hip_status(bb::launch_pack(band, ld_band, work, g, st));
+}
+
+bb_status bb_run_pass(int64_t n, int32_t bw, int32_t tw, int32_t dtype, int32_t pass, void *work, size_t work_bytes,
+                      const bb_tuning *tuning, void *stream) {
+  bb::Geometry g;
+  bb_status rc = check_work(n, bw, tw, dtype, work, work_bytes, &g);
   if (rc != BB_OK) return rc;
-  return hip_status(bb::launch_extract(wband, g, d, n > 1 ? e : nullptr, st));
+  bb_tuning tu;
+  if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
+  const std::vector<bb::Pass> passes = bb::pass_list(bw, tw);
+  if (pass < 0 || pass >= int32_t(passes.size())) return BB_ERR_ARG;
+  return run_pass(work, g, passes[size_t(pass)], tu, static_cast<hipStream_t>(stream));
+}
+
+bb_status bb_extract(const void *work, size_t work_bytes, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
+                     void *e, void *stream) {
+  bb::Geometry g;
+  const bb_status rc = check_work(n, bw, tw, dtype, work, work_bytes, &g);
+  if (rc != BB_OK) return rc;
+  if (!d || (n > 1 && !e) || !aligned(d, g.esize) || (e && !aligned(e, g.esize))) return BB_ERR_ARG;
+  return hip_status(bb::launch_extract(work, g, d, n > 1 ? e : nullptr, static_cast<hipStream_t>(stream)));
+}
+
+bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
+                    void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream) {
+  // validate everything before enqueuing anything
+  bb::Geometry g;
+  bb_status rc = check_work(n, bw, tw, dtype, work, work_bytes, &g);
+  if (rc != BB_OK && rc != BB_ERR_WORKSPACE) return rc;
+  if (!band || !d || (n > 1 && !e) || ld_band < int64_t(bw) + 1) return BB_ERR_ARG;
+  if (!aligned(band, g.esize) || !aligned(d, g.esize) || (e && !aligned(e, g.esize))) return BB_ERR_ARG;
+  if (rc != BB_OK) return rc;
+  bb_tuning tu;
+  if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
+  if ((rc = bb_pack(band, ld_band, n, bw, tw, dtype, work, work_bytes, stream)) != BB_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (const bb::Pass &p : bb::pass_list(bw, tw))
+    if ((rc = run_pass(work, g, p, tu, st)) != BB_OK) return rc;
+  return bb_extract(work, work_bytes, n, bw, tw, dtype, d, e, stream);
 }
 
 bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,

@@ -90,6 +90,50 @@ def cpu_baseline(band, w, seconds):
                       f"({nbytes / 1e9:.2f} GB algorithmic, {dt:.1f} s, one thread)"}
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: stored counter readings are only valid for it."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "band_bidiagonal_bulge_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per cycle-kernel launch from the stored counter readings
+    (profiles/traffic_<workload>.json, written by --ingest-counters), or None
+    when they are missing or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t
+
+
+def pass_tables(w):
+    """Per pass: (b, t, algorithmic bytes) of the workload."""
+    esize = 8 if w.dtype == "f64" else 4
+    out = []
+    for (b, t) in pass_list(w.bw, w.tw):
+        bp = b - t
+        R = np.arange(max(w.n - bp - 1, 0), dtype=np.int64)
+        K = (w.n - 2 - R - bp) // b + 1
+        Rr = np.repeat(R, K)
+        k = np.arange(Rr.size, dtype=np.int64) - np.repeat(np.cumsum(K) - K, K)
+        c = Rr + bp + k * b
+        ch = np.minimum(c + t, w.n - 1)
+        r = np.where(k == 0, Rr, c - b)
+        m = ch - c + 1
+        cols = np.minimum(c + t + b, w.n - 1) - c + 1
+        out.append((b, t, float(np.sum(2.0 * m * ((ch - r + 1) + cols - m) * esize))))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,7 +143,14 @@ def main():
     ap.add_argument("--scheduler", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs (no GPU)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args.workload, *args.ingest_counters, args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this reduction runs on one GPU: one matrix is one dependent chain of "
                                    "sweeps; --gpus above 1 is not supported"}))
@@ -114,33 +165,58 @@ def main():
     tb = torch.from_numpy(band).to(dev)
     dt = bbm.dtype_code(tb.dtype)
     info = bbm.bb_plan(w.n, w.bw, w.tw, dt)
+    passes = pass_tables(w)
+    assert len(passes) == info.passes
     work = bbm.workspace(w.n, w.bw, w.tw, tb.dtype, dev)
     d = torch.empty(w.n, dtype=tb.dtype, device=dev)
     e = torch.empty(w.n - 1, dtype=tb.dtype, device=dev)
     tun = bbm.tuning(scheduler=args.scheduler)
     stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    wp, wn = work.data_ptr(), work.numel()
 
-    def one():
-        bbm.bb_reduce(tb.data_ptr(), tb.stride(0), w.n, w.bw, w.tw, dt, d.data_ptr(), e.data_ptr(),
-                      work.data_ptr(), work.numel(), tun, stream.cuda_stream)
+    def one(evs=None):
+        # pack, every pass, extract: the same launches bb_reduce makes; events
+        # (on the stream the kernels run on) bracket each pass's launches
+        bbm.bb_pack(tb.data_ptr(), tb.stride(0), w.n, w.bw, w.tw, dt, wp, wn, sp)
+        for p in range(info.passes):
+            if evs is not None:
+                evs[p][0].record(stream)
+            bbm.bb_run_pass(w.n, w.bw, w.tw, dt, p, wp, wn, tun, sp)
+            if evs is not None:
+                evs[p][1].record(stream)
+        bbm.bb_extract(wp, wn, w.n, w.bw, w.tw, dt, d.data_ptr(), e.data_ptr(), sp)
+
+    if args.copy_probe_mib:
+        nb = args.copy_probe_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(info.passes)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s, f in evs:
-        s.record(stream)
-        one()
-        f.record(stream)
+    for s in range(args.steps):
+        one(ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = [s.elapsed_time(f) for s, f in evs]
+    status = bbm.bb_device_status(wp, w.n, w.bw, w.tw, dt, sp)
+    pass_ms = [[ev[s][p][0].elapsed_time(ev[s][p][1]) for s in range(args.steps)] for p in range(info.passes)]
     ms_per_step = wall * 1e3 / args.steps
     value = info.alg_bytes / (ms_per_step * 1e-3) / 1e9
-    kern_ms = statistics.median(ev_ms)
-    achieved = info.alg_bytes / (kern_ms * 1e-3) / 1e9
-    status = bbm.bb_device_status(work.data_ptr(), w.n, w.bw, w.tw, dt, stream.cuda_stream)
+    # dominant kernel: the cycle kernel, one launch per pass; algorithmic
+    # bytes per launch over the average launch duration
+    launches = info.passes * args.steps
+    avg_launch_ms = sum(sum(x) for x in pass_ms) / launches
+    bytes_per_launch = sum(p[2] for p in passes) / info.passes
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    traffic = stored_traffic(w.name)
 
     out = {
         "metric": "effective GB/s (algorithmic bytes / time), band->bidiagonal n=16384 BW=64 TW=16 fp32"
@@ -159,15 +235,59 @@ def main():
         "config": {"workload": w.name, "n": w.n, "bw": w.bw, "tw": w.tw, "dist": w.dist, "seed": w.seed,
                    "passes": info.passes, "cycles": info.cycles, "alg_bytes": info.alg_bytes,
                    "scheduler": args.scheduler},
-        "ms_per_reduction_events": {"median": round(kern_ms, 4), "min": round(min(ev_ms), 4)},
         "device_status": bbm.bb_status_str(status),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 5), "traffic": None,
-                     "kernel": "cycle kernel launches of one reduction (pack/extract included)"},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 5),
+                     "traffic": None if traffic is None else round(traffic["hbm_bytes_per_launch"], 1),
+                     "kernel": "k_persist (cycle kernel), one launch per pass",
+                     "launches": launches, "avg_launch_ms": round(avg_launch_ms, 4),
+                     "alg_bytes_per_launch": bytes_per_launch},
+        "passes": [{"b": b, "t": t, "alg_bytes": ab, "median_ms": round(statistics.median(pass_ms[i]), 4),
+                    "GBps": round(ab / (statistics.median(pass_ms[i]) * 1e-3) / 1e9, 2)}
+                   for i, (b, t, ab) in enumerate(passes)],
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(band, w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _read_counter_csv(path, counter):
+    """Per-dispatch rows of a rocprofv3 --pmc counter_collection.csv:
+    [(kernel_name, value)] in dispatch order."""
+    import csv
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") == counter:
+                rows.append((int(r.get("Dispatch_Id", 0)), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for (_, k, v) in rows]
+
+
+def ingest_counters(workload, fetch_csv, write_csv, copy_mib):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the cycle kernel, each
+    scaled by what the same counter reads for the plain copy of copy_mib MiB
+    (which moves exactly copy_mib MiB each way)."""
+    if copy_mib <= 0:
+        raise SystemExit("--copy-probe-mib is needed to scale the counters")
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_probe_mib": copy_mib}
+    total = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counter_csv(path, name)
+        copy = [v for (k, v) in rows if "copybuffer" in k.lower()]
+        cyc = [v for (k, v) in rows if "k_persist" in k]
+        if not copy or not cyc:
+            raise SystemExit(f"{path}: no copy-probe or cycle-kernel rows for {name}")
+        factor = (copy_mib * 1024.0) / max(copy)  # KiB the copy moves / KiB counted
+        per_launch = sum(cyc) / len(cyc) * 1024.0 * factor
+        out[name] = {"copy_probe_kib": max(copy), "scale": factor, "cycle_kernel_kib_mean": sum(cyc) / len(cyc),
+                     "launches": len(cyc), "bytes_per_launch": per_launch}
+        total += per_launch
+    out["hbm_bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(path)
 
 
 if __name__ == "__main__":

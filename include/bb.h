@@ -113,6 +113,30 @@ bb_status bb_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, s
 bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype,
                     void *d, void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream);
 
+/*
+ * The three stages bb_reduce runs, for callers that time or interleave them:
+ * bb_pack, then bb_run_pass for pass = 0 .. passes-1 in order, then
+ * bb_extract, all on one stream, equal bb_reduce with the same arguments.
+ *
+ * bb_pack: resets the counters in `work` and copies the caller's band (same
+ *   layout and requirements as bb_reduce's `band`, `ld_band`) into the
+ *   working band with zeroed room for the bulge.
+ * bb_run_pass: runs pass `pass` (0-based; the pass list takes the bandwidth
+ *   b -> b - min(tw, b-1) until it reaches 1, page "Accelerating
+ *   Bidiagonalization of Banded Matrices through Memory-Aware Bulge-Chasing
+ *   on GPUs", tile-width passage) on the working band in `work`; every
+ *   earlier pass must have run on it.  tuning as for bb_reduce.
+ * bb_extract: writes d and e (as for bb_reduce) from the working band.
+ * Errors: BB_ERR_ARG (also for pass out of range), BB_ERR_WORKSPACE,
+ * BB_ERR_UNSUPPORTED, BB_ERR_HIP.
+ */
+bb_status bb_pack(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *work,
+                  size_t work_bytes, void *stream);
+bb_status bb_run_pass(int64_t n, int32_t bw, int32_t tw, int32_t dtype, int32_t pass, void *work, size_t work_bytes,
+                      const bb_tuning *tuning, void *stream);
+bb_status bb_extract(const void *work, size_t work_bytes, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
+                     void *e, void *stream);
+
 /* Copies the working band left in `work` by the last bb_reduce with the same
  * (n, bw, tw, dtype) to dst (device, n * ld elements of dtype; element (i,j)
  * at dst[i*ld + j-i+sub] with ld, sub from bb_plan).  Errors: BB_ERR_ARG,

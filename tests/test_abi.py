@@ -116,3 +116,25 @@ def test_invalid_arguments_rejected_on_host():
             _lib.BB_ERR_ARG
     # n = 1 needs no e
     assert L.bb_reduce(fake, 5, 1, 4, 2, 0, fake, None, fake, 16, None, None) == _lib.BB_ERR_WORKSPACE
+
+
+def test_staged_entry_points_validate_on_host():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    big = 1 << 30
+    # bb_pack: null band, short ld_band, small workspace, misaligned work
+    assert L.bb_pack(None, 5, 10, 4, 2, 0, fake, big, None) == _lib.BB_ERR_ARG
+    assert L.bb_pack(fake, 4, 10, 4, 2, 0, fake, big, None) == _lib.BB_ERR_ARG
+    assert L.bb_pack(fake, 5, 10, 4, 2, 0, fake, 16, None) == _lib.BB_ERR_WORKSPACE
+    assert L.bb_pack(fake, 5, 10, 4, 2, 0, ctypes.c_void_p((1 << 20) + 8), big, None) == _lib.BB_ERR_ARG
+    # bb_run_pass: pass index out of range (10, 4, 2 has passes 4->2->1)
+    assert bbm.bb_plan(10, 4, 2, 0).passes == 2
+    for bad_pass in (-1, 2, 100):
+        assert L.bb_run_pass(10, 4, 2, 0, bad_pass, fake, big, None, None) == _lib.BB_ERR_ARG
+    assert L.bb_run_pass(10, 4, 2, 0, 0, fake, 16, None, None) == _lib.BB_ERR_WORKSPACE
+    bad = _lib.bb_tuning(9, 0, 0, 0, 0)
+    assert L.bb_run_pass(10, 4, 2, 0, 0, fake, big, ctypes.byref(bad), None) == _lib.BB_ERR_ARG
+    # bb_extract: null d, null e with n > 1, misaligned d
+    assert L.bb_extract(fake, big, 10, 4, 2, 0, None, fake, None) == _lib.BB_ERR_ARG
+    assert L.bb_extract(fake, big, 10, 4, 2, 0, fake, None, None) == _lib.BB_ERR_ARG
+    assert L.bb_extract(fake, big, 10, 4, 2, 1, ctypes.c_void_p((1 << 20) + 4), fake, None) == _lib.BB_ERR_ARG

@@ -172,3 +172,39 @@ def test_workload_stored_oracle(name):
     np.testing.assert_array_equal(e, z["e"])
     off = [o for o in range(W.shape[1]) if o - sub not in (0, 1)]
     assert np.all(W[:, off] == 0)
+
+
+@pytest.mark.parametrize("sched", [bbm.BB_SCHED_STEP, bbm.BB_SCHED_PERSISTENT])
+@pytest.mark.parametrize("n,bw,tw,dt", [(700, 48, 16, "f32"), (333, 20, 7, "f64")])
+def test_staged_calls_equal_reduce(n, bw, tw, dt, sched):
+    """bb_pack + bb_run_pass (each pass, in order) + bb_extract == bb_reduce, and
+    the working band after the first pass equals the oracle's after its first
+    pass's cycles."""
+    import torch
+    log(f"staged n={n} bw={bw} tw={tw} {dt} sched={sched}")
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=n)
+    dev = torch.device("cuda:0")
+    tb = torch.from_numpy(band).to(dev)
+    code = bbm.dtype_code(tb.dtype)
+    info = bbm.bb_plan(n, bw, tw, code)
+    work = bbm.workspace(n, bw, tw, tb.dtype, dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    tun = bbm.tuning(scheduler=sched)
+    d = torch.empty(n, dtype=tb.dtype, device=dev)
+    e = torch.empty(n - 1, dtype=tb.dtype, device=dev)
+    bbm.bb_pack(tb.data_ptr(), tb.stride(0), n, bw, tw, code, work.data_ptr(), work.numel(), st)
+    bbm.bb_run_pass(n, bw, tw, code, 0, work.data_ptr(), work.numel(), tun, st)
+    W1, _ = bbm.export_band(work, n, bw, tw, tb.dtype)
+    torch.cuda.synchronize()
+    b0, t0 = bw, min(tw, bw - 1)
+    K = [(n - 2 - R - (b0 - t0)) // b0 + 1 for R in range(max(n - (b0 - t0) - 1, 0))]
+    first_pass = np.array([(0, R, k) for R in range(len(K)) for k in range(K[R])], dtype=np.int64)
+    OW1 = oracle.run_cycles(band, bw, tw, first_pass)
+    np.testing.assert_array_equal(W1.cpu().numpy(), OW1)
+    for p in range(1, info.passes):
+        bbm.bb_run_pass(n, bw, tw, code, p, work.data_ptr(), work.numel(), tun, st)
+    bbm.bb_extract(work.data_ptr(), work.numel(), n, bw, tw, code, d.data_ptr(), e.data_ptr(), st)
+    torch.cuda.synchronize()
+    rd, re = gpu_reduce(band, bw, tw, tun)
+    np.testing.assert_array_equal(d.cpu().numpy(), rd)
+    np.testing.assert_array_equal(e.cpu().numpy(), re)
