@@ -7,7 +7,8 @@ for device memory and the stream only).
 """
 from __future__ import annotations
 
-from ._lib import (BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS, BBError,
+from ._lib import (BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
+                   BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
                    bb_run_pass, bb_status_str, bb_tuning, bb_workspace_bytes, lib)
 
@@ -25,8 +26,8 @@ def dtype_code(torch_dtype) -> int:
 
 
 def tuning(scheduler: int = 0, stagger: int = 0, max_blocks: int = 0, threads_per_block: int = 0,
-           spin_limit: int = 0) -> bb_tuning:
-    return bb_tuning(scheduler, stagger, max_blocks, threads_per_block, spin_limit)
+           spin_limit: int = 0, group_sweeps: int = 0) -> bb_tuning:
+    return bb_tuning(scheduler, stagger, max_blocks, threads_per_block, spin_limit, group_sweeps, 0)
 
 
 def workspace(n: int, bw: int, tw: int, torch_dtype, device="cuda"):

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libbb.so")
 
 BB_F32, BB_F64 = 0, 1
 BB_OK, BB_ERR_ARG, BB_ERR_WORKSPACE, BB_ERR_HIP, BB_ERR_UNSUPPORTED, BB_ERR_TIMEOUT = range(6)
-BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT = 0, 1, 2
+BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT, BB_SCHED_GROUP = 0, 1, 2, 3
 
 # Every symbol include/bb.h declares.
 EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band",
@@ -23,7 +23,8 @@ EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass
 
 class bb_tuning(ctypes.Structure):
     _fields_ = [("scheduler", ctypes.c_int32), ("stagger", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
-                ("threads_per_block", ctypes.c_int32), ("spin_limit", ctypes.c_int64)]
+                ("threads_per_block", ctypes.c_int32), ("spin_limit", ctypes.c_int64),
+                ("group_sweeps", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class bb_plan_info(ctypes.Structure):

@@ -5,6 +5,9 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "bb.h"
@@ -44,7 +47,7 @@ constexpr size_t kMaxLdsBytes = 160 * 1024;  // gfx950 LDS available to one work
 // in 31-bit byte offsets (buffer addressing).
 bool supported(const bb::Geometry &g) {
   if (g.maxt > kMaxTile) return false;
-  if (uint64_t(g.n) * uint64_t(g.ld) * uint64_t(g.esize) >= (uint64_t(1) << 31)) return false;
+  if (uint64_t(g.n) * uint64_t(g.stride) * uint64_t(g.esize) >= (uint64_t(1) << 31)) return false;
   for (const bb::Pass &p : bb::pass_list(g.bw, g.tw))
     if (bb::stage_lds_bytes(g.dtype, pick_maxm(p.t), p.b, p.t) > kMaxLdsBytes) return false;
   return true;
@@ -113,6 +116,64 @@ bb_status run_persistent_pass(void *wband, const bb::Geometry &g, const bb::Pass
   return BB_OK;
 }
 
+// Sweep groups in LDS: the largest G <= 8 whose ring fits in LDS, with the
+// ring as large as LDS allows (room for the auxiliary wave to run ahead).
+constexpr size_t kGroupLdsBytes = kMaxLdsBytes - 2048;  // headroom for the static control block
+constexpr int kGroupMaxSweeps = bb::kGroupMaxWaves - 2;
+
+struct GroupPlan {
+  int G = 0, W = 0;  // G = 0: the pass does not fit
+};
+
+int64_t ring_rows_cached(int64_t n, const bb::Pass &p, int G) {
+  static std::mutex mu;
+  static std::map<std::tuple<int64_t, int, int, int>, int64_t> cache;
+  const auto key = std::make_tuple(n, p.b, p.t, G);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const int64_t rows = bb::group_ring_rows(n, p, G);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = rows;
+  return rows;
+}
+
+GroupPlan group_plan(const bb::Geometry &g, const bb::Pass &p, int requested_g) {
+  GroupPlan gp;
+  if (pick_maxm(p.t) > 17) return gp;  // wider tiles spill registers in the group kernel
+  const int64_t row_bytes = int64_t(g.stride) * g.esize;
+  const int64_t W = std::min<int64_t>(int64_t(kGroupLdsBytes) / row_bytes, g.n);
+  const int lo = requested_g > 0 ? requested_g : 1;
+  const int hi = requested_g > 0 ? requested_g : kGroupMaxSweeps;
+  for (int G = hi; G >= lo; --G) {
+    if (ring_rows_cached(g.n, p, G) <= W) {
+      gp.G = G;
+      gp.W = int(W);
+      return gp;
+    }
+  }
+  return gp;
+}
+
+bb_status run_group_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
+                         const GroupPlan &gp, uint32_t *sync, hipStream_t st) {
+  const int64_t ns = bb::sweeps_of(g.n, p);
+  if (ns == 0) return BB_OK;
+  const int64_t ngroups = (ns + gp.G - 1) / gp.G;
+  if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
+      bb::launch_fill_u32(sync + bb::kSyncHeader, ngroups * bb::kLine, 0u, st) != hipSuccess)
+    return BB_ERR_HIP;
+  int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
+  grid = std::min<int64_t>(grid, ngroups);
+  const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+  if (bb::launch_group(pick_maxm(p.t), wband, g, p.b, p.t, bb::lag_of(p), ns, gp.G, gp.W, sync, int(grid), spin,
+                       st) != hipSuccess)
+    return BB_ERR_HIP;
+  return BB_OK;
+}
+
 // Shared validation of the workspace-level entry points.
 bb_status check_work(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const void *work, size_t work_bytes,
                      bb::Geometry *g) {
@@ -127,19 +188,26 @@ bb_status check_work(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const voi
 bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
   std::memset(tu, 0, sizeof(*tu));
   if (tuning) *tu = *tuning;
-  if (tu->scheduler < 0 || tu->scheduler > BB_SCHED_PERSISTENT) return BB_ERR_ARG;
+  if (tu->scheduler < 0 || tu->scheduler > BB_SCHED_GROUP) return BB_ERR_ARG;
   if (tu->stagger != 0 && (tu->stagger < 2 || tu->stagger > 64)) return BB_ERR_ARG;
   if (tu->threads_per_block != 0 && (tu->threads_per_block < 64 || tu->threads_per_block > 256 ||
                                      tu->threads_per_block % 64 != 0))
     return BB_ERR_ARG;
   if (tu->max_blocks < 0 || tu->spin_limit < 0) return BB_ERR_ARG;
+  if (tu->group_sweeps < 0 || tu->group_sweeps > kGroupMaxSweeps || tu->reserved != 0) return BB_ERR_ARG;
   return BB_OK;
 }
 
+// Scheduler of a pass: STEP and PERSISTENT as asked; GROUP when the pass fits
+// in LDS (else PERSISTENT); DEFAULT = GROUP where it fits.
 bb_status run_pass(void *work, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu, hipStream_t st) {
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
-  return tu.scheduler == BB_SCHED_STEP ? run_step_pass(work, g, p, tu, st)
-                                       : run_persistent_pass(work, g, p, tu, sync, st);
+  if (tu.scheduler == BB_SCHED_STEP) return run_step_pass(work, g, p, tu, st);
+  if (tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP) {
+    const GroupPlan gp = group_plan(g, p, tu.group_sweeps);
+    if (gp.G > 0) return run_group_pass(work, g, p, tu, gp, sync, st);
+  }
+  return run_persistent_pass(work, g, p, tu, sync, st);
 }
 
 }  // namespace
@@ -239,8 +307,9 @@ bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, in
                          void *stream) {
   if (!valid_shape(n, bw, tw, dtype) || !work || !dst) return BB_ERR_ARG;
   const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
-  const size_t bytes = size_t(n) * size_t(g.ld) * size_t(g.esize);
-  return hip_status(hipMemcpyAsync(dst, work, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+  const size_t row = size_t(g.ld) * size_t(g.esize);
+  return hip_status(hipMemcpy2DAsync(dst, row, work, size_t(g.stride) * size_t(g.esize), row, size_t(n),
+                                     hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
 }
 
 bb_status bb_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream) {

@@ -1,0 +1,729 @@
+// Sweep groups resident in LDS (gfx950): one workgroup runs G consecutive
+// sweeps of a pass, one wave per sweep, on a ring of band rows held in LDS,
+// plus two auxiliary waves that move rows between the ring and memory: a
+// loader and a writer (separate waves, so that waiting for loads never holds
+// up a write-back or a publish: vmcnt is per wave).
+//
+// Why: a sweep must stay a few half-cycles behind its predecessor (page
+// "Accelerating Bidiagonalization of Banded Matrices through Memory-Aware
+// Bulge-Chasing on GPUs", three-cycle-separation passage; page "A two-stage
+// reduction on an Apple M5 Pro", section 6).  Across workgroups every such
+// hand-off costs a round trip through memory; inside a workgroup it is an LDS
+// counter, and the data never leaves LDS.  Only the first sweep of a group
+// depends on another workgroup, and it does so by whole rows.
+//
+// Protocol (rows are the unit between groups):
+//   * group g (sweeps R0 .. R0+G-1) publishes X_g: every row below X_g has
+//     been written back by g and will not be touched by g again, and
+//     X_g <= X_{g-1}.  Group g loads row i only once X_{g-1} > i, so each row
+//     it reads holds the final values of all earlier sweeps, and no earlier
+//     sweep touches the row afterwards (every sweep touches rows in
+//     nondecreasing order).
+//   * inside the group, sweep j starts half-cycle q once sweep j-1 has done
+//     min(q + d, all of its) half-cycles, and publishes its final count only
+//     after sweep j-1 has published its own (the rule of the persistent
+//     scheduler; d = 2, 3, 4 for b' >= 3, 2, 1).  Sweep 0 has no in-group
+//     predecessor: its inputs are whole rows, complete when loaded.
+//   * each compute wave publishes the lowest row it will still touch; rows
+//     below the minimum over the group are dead: the writer writes them back
+//     and publishes X_g = rows written (never above X_{g-1}: only loaded rows
+//     are written, and only released rows are loaded); the loader then reuses
+//     their ring slots.
+// Every wait is a bounded poll; on expiry the status word is set and the
+// workgroup drains (the abort flag stops every wave of the group).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "bb_device.hpp"
+#include "bb_internal.hpp"
+
+namespace bb {
+namespace {
+
+constexpr int kGroupMaxSweeps = kGroupMaxWaves - 2;
+
+constexpr int32_t kLoadBatchRows = 64;  // rows per loader batch: early rows are signalled early
+
+struct GroupCtl {
+  int32_t g;                         // group being run
+  int32_t loaded_hi;                 // rows [R0, loaded_hi) resident in the ring
+  int32_t written;                   // rows [R0, written) written back; their slots are free
+  int32_t abort_;                    // a wait expired: drain
+  int32_t prog[kGroupMaxSweeps];     // half-cycles completed by sweep j
+  int32_t floor_[kGroupMaxSweeps];   // lowest row sweep j will still touch
+};
+
+__device__ __forceinline__ int32_t lds_load(const int32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Bounded LDS poll until *p >= need (whole wave).  False on expiry or abort.
+__device__ __forceinline__ bool lds_wait(const int32_t *p, int32_t need, GroupCtl &ctl, int64_t spin_limit,
+                                         uint32_t *status) {
+  int64_t polls = 0;
+  while (lds_load(p) < need) {
+    if (lds_load(&ctl.abort_)) return false;
+    __builtin_amdgcn_s_sleep(1);
+    if (++polls > spin_limit) {
+      lds_store(&ctl.abort_, 1);
+      __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+  return true;
+}
+
+// Instrumented builds (-DBB_PROFILE) accumulate wall-clock ticks (100 MHz)
+// per phase into 64-bit counters of the workspace's profiling area.
+#ifdef BB_PROFILE
+struct Prof {
+  uint64_t v[16] = {};
+  uint64_t mark = 0;
+  __device__ __forceinline__ void start() { mark = wall_clock64(); }
+  __device__ __forceinline__ void tick(int slot) {
+    const uint64_t now = wall_clock64();
+    v[slot] += now - mark;
+    mark = now;
+  }
+  __device__ __forceinline__ void add(int slot, uint64_t x) { v[slot] += x; }
+  __device__ void flush(uint32_t *sync, int lane) {
+    unsigned long long *p = reinterpret_cast<unsigned long long *>(sync + kProf);
+    if (lane == 0)
+      for (int i = 0; i < 16; ++i)
+        if (v[i]) atomicAdd(p + i, (unsigned long long)v[i]);
+  }
+};
+#define BB_P(stmt) stmt
+// Event trace of groups [kTraceG0, kTraceG0 + kTraceGroups) in the space
+// past the counter area (instrumented builds allocate it): per group,
+// kTraceHalves (start, end) stamps per sweep, then kTraceIters aux records
+// (stamp, xprev, loaded, written).
+constexpr int kTraceG0 = 100, kTraceGroups = 8, kTraceHalves = 1200, kTraceIters = 6000;
+constexpr int kTraceGroupWords = 8 * kTraceHalves * 2 + kTraceIters * 4;
+__device__ __forceinline__ uint32_t *trace_base(uint32_t *sync, int32_t n, int g) {
+  if (g < kTraceG0 || g >= kTraceG0 + kTraceGroups) return nullptr;
+  return sync + kSyncHeader + (int64_t(n) + 1) * kLine + int64_t(g - kTraceG0) * kTraceGroupWords;
+}
+#else
+#define BB_P(stmt)
+#endif
+
+// Ring of W band rows in LDS, S elements each (the working band's row
+// stride): row i lives in slot i mod W, element (i, j) at
+// L[slot * S + (j - i + sub)].
+template <typename T>
+struct Ring {
+  T *L;
+  int32_t S, W, sub;
+  __device__ __forceinline__ int32_t slot(int32_t i) const { return i % W; }
+  __device__ __forceinline__ int32_t next(int32_t s, int32_t di) const {  // slot of row i + di, di < W
+    s += di;
+    return s >= W ? s - W : s;
+  }
+  __device__ __forceinline__ T *at(int32_t s, int32_t i, int32_t j) const { return L + s * S + (j - i + sub); }
+};
+
+// The reflector of a half from the tail sum of squares sn = sum_{j>=1} x_j^2
+// (already accumulated in the contract's order) and alpha = x_0; nz false:
+// identity (zero tail).
+template <typename T>
+__device__ __forceinline__ Refl<T> house_from(T alpha, T sn) {
+  Refl<T> h;
+  h.nz = sn != T(0);
+  h.beta = alpha;
+  h.tau = T(0);
+  h.inv = T(0);
+  if (h.nz) {
+    const T nrm = sqrt_(fma_(alpha, alpha, sn));
+    h.beta = (alpha >= T(0)) ? -nrm : nrm;
+    h.tau = (h.beta - alpha) / h.beta;
+    h.inv = T(1) / (alpha - h.beta);
+  }
+  return h;
+}
+
+// Row half of a cycle on the ring, one wave.  Row r's entries c..ch (x) give
+// the reflector; it is applied from the right to rows r+1..ch, one lane per
+// row: rows r+1+lane and r+65+lane, whose dot products with x are
+// accumulated alongside the norm (neither depends on the reflector), so the
+// three serial chains overlap.  Row r becomes (beta, 0, ..., 0).
+//   sr: ring slot of row r; nr = ch - r rows below it.
+template <typename T, int MAXM, bool FULL, bool TWO>
+__device__ void ring_row_half(const Ring<T> &A, int32_t r, int32_t c, int32_t m, int32_t nr, int32_t sr,
+                              int lane) {
+  T *L = A.L;
+  const int32_t colr = c - r + A.sub;          // column c within row r
+  const T *px = L + sr * A.S + colr;
+  const int32_t a0 = lane + 1, a1 = lane + 65;
+  const bool h0 = a0 <= nr, h1 = a1 <= nr;
+  const int32_t i0 = h0 ? a0 : nr, i1 = h1 ? a1 : nr;  // inactive lanes read row ch, store nothing
+  int32_t s0 = sr + i0, s1 = sr + i1;
+  s0 = s0 >= A.W ? s0 - A.W : s0;
+  s1 = s1 >= A.W ? s1 - A.W : s1;
+  T *p0 = L + s0 * A.S + (colr - i0);
+  T *p1 = L + s1 * A.S + (colr - i1);
+  T x[MAXM], v0[MAXM], v1[MAXM];
+#pragma unroll
+  for (int j = 0; j < MAXM; ++j) {
+    x[j] = (FULL || j < m) ? px[j] : T(0);
+    v0[j] = (FULL || j < m) ? p0[j] : T(0);
+    if (TWO) v1[j] = (FULL || j < m) ? p1[j] : T(0);
+  }
+  T sn = T(0), d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j)
+    if (FULL || j < m) {
+      sn = fma_(x[j], x[j], sn);
+      d0 = fma_(v0[j], x[j], d0);
+      if (TWO) d1 = fma_(v1[j], x[j], d1);
+    }
+  const Refl<T> h = house_from(x[0], sn);
+  if (h.nz) {
+    T xv[MAXM];
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j) xv[j] = x[j] * h.inv;
+    const T tw0 = h.tau * fma_(d0, h.inv, v0[0]);
+    if (h0) {
+      p0[0] = v0[0] - tw0;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) p0[j] = fma_(-tw0, xv[j], v0[j]);
+    }
+    if (TWO && h1) {
+      const T tw1 = h.tau * fma_(d1, h.inv, v1[0]);
+      p1[0] = v1[0] - tw1;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) p1[j] = fma_(-tw1, xv[j], v1[j]);
+    }
+    for (int32_t i = 129 + lane; i <= nr; i += 64) {  // bands wider than 128 rows
+      int32_t si = sr + i;
+      si = si >= A.W ? si - A.W : si;
+      T *p = L + si * A.S + (colr - i);
+      T v[MAXM];
+#pragma unroll
+      for (int j = 0; j < MAXM; ++j) v[j] = (FULL || j < m) ? p[j] : T(0);
+      T dd = T(0);
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) dd = fma_(v[j], x[j], dd);
+      const T tw = h.tau * fma_(dd, h.inv, v[0]);
+      p[0] = v[0] - tw;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) p[j] = fma_(-tw, xv[j], v[j]);
+    }
+  }
+  if (lane == 0) {
+    T *p = L + sr * A.S + colr;
+    if (h.nz) p[0] = h.beta;
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j)
+      if (FULL || j < m) p[j] = T(0);
+  }
+}
+
+// Column half of a cycle on the ring, one wave.  Column c's entries in rows
+// c..ch (y) give the reflector; it is applied from the left to columns
+// c+1..jend, one lane per column (c+1+lane and c+65+lane), dot products
+// accumulated alongside the norm.  Column c becomes (beta, 0, ..., 0).
+//   sc: ring slot of row c; nc = jend - c columns right of c.
+// Element (c+i, c+jj) sits at L[o_i + jj], o_i = slot(c+i) * S + sub - i.
+template <typename T, int MAXM, bool FULL, bool TWO>
+__device__ void ring_col_half(const Ring<T> &A, int32_t m, int32_t nc, int32_t sc, int lane) {
+  T *L = A.L;
+  int32_t o[MAXM];
+#pragma unroll
+  for (int i = 0, s = sc; i < MAXM; ++i) {
+    o[i] = s * A.S + A.sub - i;
+    s = (s + 1 == A.W) ? 0 : s + 1;
+  }
+  const int32_t a0 = lane + 1, a1 = lane + 65;
+  const bool h0 = a0 <= nc, h1 = a1 <= nc;
+  const int32_t j0 = h0 ? a0 : nc, j1 = h1 ? a1 : nc;
+  T y[MAXM], v0[MAXM], v1[MAXM];
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) {
+    y[i] = (FULL || i < m) ? L[o[i]] : T(0);
+    v0[i] = (FULL || i < m) ? L[o[i] + j0] : T(0);
+    if (TWO) v1[i] = (FULL || i < m) ? L[o[i] + j1] : T(0);
+  }
+  T sn = T(0), d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i)
+    if (FULL || i < m) {
+      sn = fma_(y[i], y[i], sn);
+      d0 = fma_(y[i], v0[i], d0);
+      if (TWO) d1 = fma_(y[i], v1[i], d1);
+    }
+  const Refl<T> g = house_from(y[0], sn);
+  if (g.nz) {
+    T yv[MAXM];
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i) yv[i] = y[i] * g.inv;
+    const T tw0 = g.tau * fma_(d0, g.inv, v0[0]);
+    if (h0) {
+      L[o[0] + j0] = v0[0] - tw0;
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) L[o[i] + j0] = fma_(-tw0, yv[i], v0[i]);
+    }
+    if (TWO && h1) {
+      const T tw1 = g.tau * fma_(d1, g.inv, v1[0]);
+      L[o[0] + j1] = v1[0] - tw1;
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) L[o[i] + j1] = fma_(-tw1, yv[i], v1[i]);
+    }
+    for (int32_t jj = 129 + lane; jj <= nc; jj += 64) {  // bands wider than 128 columns
+      T v[MAXM];
+#pragma unroll
+      for (int i = 0; i < MAXM; ++i) v[i] = (FULL || i < m) ? L[o[i] + jj] : T(0);
+      T dd = T(0);
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) dd = fma_(y[i], v[i], dd);
+      const T tw = g.tau * fma_(dd, g.inv, v[0]);
+      L[o[0] + jj] = v[0] - tw;
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) L[o[i] + jj] = fma_(-tw, yv[i], v[i]);
+    }
+  }
+  if (lane == 0) {
+    L[o[0]] = g.nz ? g.beta : y[0];
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) L[o[i]] = T(0);
+  }
+}
+
+// The same two halves for a block whose rows sit in consecutive ring slots
+// (no wrap) with a compile-time row stride S: element (i, j) of the block is
+// base[i*(S-1) + j], so every access is one base address plus an immediate
+// offset.  Arithmetic identical to the ring versions above.
+template <typename T, int MAXM, bool FULL, bool TWO, int S>
+__device__ void lin_row_half(T *base, int32_t m, int32_t nr, int lane) {
+  constexpr int32_t D = S - 1;  // (i+1, j+1) is D+1 elements after (i, j); (i+1, j) is D after
+  const int32_t a0 = lane + 1, a1 = lane + 65;
+  const bool h0 = a0 <= nr, h1 = a1 <= nr;
+  const int32_t i0 = h0 ? a0 : nr, i1 = h1 ? a1 : nr;
+  T *p0 = base + i0 * D, *p1 = base + i1 * D;
+  T x[MAXM], v0[MAXM], v1[MAXM];
+#pragma unroll
+  for (int j = 0; j < MAXM; ++j) {
+    x[j] = (FULL || j < m) ? base[j] : T(0);
+    v0[j] = (FULL || j < m) ? p0[j] : T(0);
+    if (TWO) v1[j] = (FULL || j < m) ? p1[j] : T(0);
+  }
+  T sn = T(0), d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j)
+    if (FULL || j < m) {
+      sn = fma_(x[j], x[j], sn);
+      d0 = fma_(v0[j], x[j], d0);
+      if (TWO) d1 = fma_(v1[j], x[j], d1);
+    }
+  const Refl<T> h = house_from(x[0], sn);
+  if (h.nz) {
+    T xv[MAXM];
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j) xv[j] = x[j] * h.inv;
+    const T tw0 = h.tau * fma_(d0, h.inv, v0[0]);
+    if (h0) {
+      p0[0] = v0[0] - tw0;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) p0[j] = fma_(-tw0, xv[j], v0[j]);
+    }
+    if (TWO && h1) {
+      const T tw1 = h.tau * fma_(d1, h.inv, v1[0]);
+      p1[0] = v1[0] - tw1;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) p1[j] = fma_(-tw1, xv[j], v1[j]);
+    }
+    for (int32_t i = 129 + lane; i <= nr; i += 64) {  // bands wider than 128 rows
+      T *p = base + i * D;
+      T v[MAXM];
+#pragma unroll
+      for (int j = 0; j < MAXM; ++j) v[j] = (FULL || j < m) ? p[j] : T(0);
+      T dd = T(0);
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) dd = fma_(v[j], x[j], dd);
+      const T tw = h.tau * fma_(dd, h.inv, v[0]);
+      p[0] = v[0] - tw;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) p[j] = fma_(-tw, xv[j], v[j]);
+    }
+  }
+  if (lane == 0) {
+    if (h.nz) base[0] = h.beta;
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j)
+      if (FULL || j < m) base[j] = T(0);
+  }
+}
+
+template <typename T, int MAXM, bool FULL, bool TWO, int S>
+__device__ void lin_col_half(T *base, int32_t m, int32_t nc, int lane) {
+  constexpr int32_t D = S - 1;  // element (c+i, c+jj) at base[i*D + jj]
+  const int32_t a0 = lane + 1, a1 = lane + 65;
+  const bool h0 = a0 <= nc, h1 = a1 <= nc;
+  T *q0 = base + (h0 ? a0 : nc), *q1 = base + (h1 ? a1 : nc);
+  T y[MAXM], v0[MAXM], v1[MAXM];
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) {
+    y[i] = (FULL || i < m) ? base[i * D] : T(0);
+    v0[i] = (FULL || i < m) ? q0[i * D] : T(0);
+    if (TWO) v1[i] = (FULL || i < m) ? q1[i * D] : T(0);
+  }
+  T sn = T(0), d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i)
+    if (FULL || i < m) {
+      sn = fma_(y[i], y[i], sn);
+      d0 = fma_(y[i], v0[i], d0);
+      if (TWO) d1 = fma_(y[i], v1[i], d1);
+    }
+  const Refl<T> g = house_from(y[0], sn);
+  if (g.nz) {
+    T yv[MAXM];
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i) yv[i] = y[i] * g.inv;
+    const T tw0 = g.tau * fma_(d0, g.inv, v0[0]);
+    if (h0) {
+      q0[0] = v0[0] - tw0;
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) q0[i * D] = fma_(-tw0, yv[i], v0[i]);
+    }
+    if (TWO && h1) {
+      const T tw1 = g.tau * fma_(d1, g.inv, v1[0]);
+      q1[0] = v1[0] - tw1;
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) q1[i * D] = fma_(-tw1, yv[i], v1[i]);
+    }
+    for (int32_t jj = 129 + lane; jj <= nc; jj += 64) {  // bands wider than 128 columns
+      T *q = base + jj;
+      T v[MAXM];
+#pragma unroll
+      for (int i = 0; i < MAXM; ++i) v[i] = (FULL || i < m) ? q[i * D] : T(0);
+      T dd = T(0);
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) dd = fma_(y[i], v[i], dd);
+      const T tw = g.tau * fma_(dd, g.inv, v[0]);
+      q[0] = v[0] - tw;
+#pragma unroll
+      for (int i = 1; i < MAXM; ++i)
+        if (FULL || i < m) q[i * D] = fma_(-tw, yv[i], v[i]);
+    }
+  }
+  if (lane == 0) {
+    base[0] = g.nz ? g.beta : y[0];
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) base[i * D] = T(0);
+  }
+}
+
+// One sweep of the group, run by one wave.  Cycle geometry and ring slots
+// advance incrementally (c by b per cycle, the slot of c likewise).
+template <typename T, int MAXM, int SC>
+__device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, int t, int d, int32_t R, int j,
+                            int lane, int64_t spin_limit, uint32_t *status, uint32_t *sync) {
+  const int32_t K = int32_t(cycles_of_dev(n, b, t, R));
+  const int32_t Kp = j > 0 ? int32_t(cycles_of_dev(n, b, t, R - 1)) : 0;
+  int32_t c = R + (b - t);
+  int32_t sc = A.slot(c);
+  const int32_t sR = A.slot(R);
+  BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g);)
+  for (int32_t k = 0; k < K; ++k) {
+    const int32_t ch = min(c + t, n - 1);
+    const int32_t m = ch - c + 1;
+    const int32_t r = k == 0 ? R : c - b;
+    int32_t sr = sR;
+    if (k > 0) sr = sc - b < 0 ? sc - b + A.W : sc - b;
+    const int32_t jend = min(c + t + b, n - 1);
+    for (int h = 0; h < 2; ++h) {
+      const int32_t q = 2 * k + h;
+      if (j > 0 && !lds_wait(&ctl.prog[j - 1], min(q + d, 2 * Kp), ctl, spin_limit, status)) return;
+      BB_P(pr.tick(0);)
+      if (!lds_wait(&ctl.loaded_hi, ch + 1, ctl, spin_limit, status)) return;
+      BB_P(pr.tick(1); if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2] = uint32_t(pr.mark);)
+      if (SC > 0 && m == MAXM && (h == 0 ? sr + (ch - r) : sc + m - 1) < A.W) {
+        // interior block without a ring wrap: compile-time stride
+        if (h == 0) {
+          T *base = A.L + sr * SC + (c - r + A.sub);
+          if (ch - r > 64)
+            lin_row_half<T, MAXM, true, true, SC>(base, m, ch - r, lane);
+          else
+            lin_row_half<T, MAXM, true, false, SC>(base, m, ch - r, lane);
+        } else {
+          T *base = A.L + sc * SC + A.sub;
+          if (jend - c > 64)
+            lin_col_half<T, MAXM, true, true, SC>(base, m, jend - c, lane);
+          else
+            lin_col_half<T, MAXM, true, false, SC>(base, m, jend - c, lane);
+        }
+      } else if (h == 0) {
+        const int32_t nr = ch - r;
+        if (m == MAXM && nr > 64)
+          ring_row_half<T, MAXM, true, true>(A, r, c, m, nr, sr, lane);
+        else if (m == MAXM)
+          ring_row_half<T, MAXM, true, false>(A, r, c, m, nr, sr, lane);
+        else
+          ring_row_half<T, MAXM, false, true>(A, r, c, m, nr, sr, lane);
+      } else {
+        const int32_t nc = jend - c;
+        if (m == MAXM && nc > 64)
+          ring_col_half<T, MAXM, true, true>(A, m, nc, sc, lane);
+        else if (m == MAXM)
+          ring_col_half<T, MAXM, true, false>(A, m, nc, sc, lane);
+        else
+          ring_col_half<T, MAXM, false, true>(A, m, nc, sc, lane);
+      }
+      BB_P(pr.tick(2 + h);)
+      // The next half (this cycle's column half, or the next cycle's row
+      // half) starts at row c; after the last half the sweep touches nothing.
+      const int32_t fl = q + 1 < 2 * K ? c : n;
+      if (q + 1 == 2 * K && j > 0 && !lds_wait(&ctl.prog[j - 1], 2 * Kp, ctl, spin_limit, status)) return;
+      if (lane == 0) {
+        lds_store(&ctl.floor_[j], fl);
+        lds_store(&ctl.prog[j], q + 1);
+      }
+      BB_P(pr.tick(4); pr.add(5, 1);
+           if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2 + 1] = uint32_t(pr.mark);)
+    }
+    c += b;
+    sc += b;
+    while (sc >= A.W) sc -= A.W;
+  }
+  BB_P(pr.flush(sync, lane);)
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+
+
+// Copies rows [lo, hi) of the band from memory into their ring slots with
+// LDS-direct 16-byte loads (no registers involved), split where the ring
+// wraps.  Complete once vmcnt reaches zero.
+template <typename T>
+__device__ void ring_fill(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t lo, int32_t hi, int lane) {
+  const int32_t row_bytes = A.S * int32_t(sizeof(T));
+  unsigned char *base = reinterpret_cast<unsigned char *>(A.L);
+  while (lo < hi) {
+    const int32_t s = A.slot(lo);
+    const int32_t run = min(hi - lo, A.W - s);  // rows up to the end of the ring
+    const int32_t bytes = run * row_bytes;
+    for (int32_t off = 0; off < bytes; off += 1024) {
+      if (off + lane * 16 < bytes)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(mem, (lds_ptr_t)(base + s * row_bytes + off), 16,
+                                                 uint32_t(lo * row_bytes + off + lane * 16), 0, 0, kSc1);
+    }
+    lo += run;
+  }
+}
+
+// Writes rows [lo, hi) from their ring slots back to memory (agent-coherent
+// 16-byte stores).  Complete once vmcnt reaches zero.
+template <typename T>
+__device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t lo, int32_t hi, int lane) {
+  const int32_t row_bytes = A.S * int32_t(sizeof(T));
+  const unsigned char *base = reinterpret_cast<const unsigned char *>(A.L);
+  while (lo < hi) {
+    const int32_t s = A.slot(lo);
+    const int32_t run = min(hi - lo, A.W - s);
+    const int32_t bytes = run * row_bytes;
+    for (int32_t off = lane * 16; off < bytes; off += 1024) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(base + s * row_bytes + off);
+      __builtin_amdgcn_raw_buffer_store_b128(v, mem, uint32_t(lo * row_bytes + off), 0, kSc1);
+    }
+    lo += run;
+  }
+}
+
+// Idle accounting of the auxiliary waves: a bounded number of empty polls
+// in a row, then abort.
+__device__ __forceinline__ bool aux_idle(int64_t &idle, int64_t spin_limit, GroupCtl &ctl, uint32_t *status) {
+  __builtin_amdgcn_s_sleep(1);
+  if (++idle <= spin_limit) return true;
+  lds_store(&ctl.abort_, 1);
+  __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+// The writer: writes back the rows every sweep is done with, then publishes
+// X_g = rows written.
+template <typename T>
+__device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
+                             int32_t Gg, uint32_t *xself_line, int lane, int64_t spin_limit, uint32_t *status,
+                             uint32_t *sync) {
+  int32_t written = R0;
+  int64_t idle = 0;
+  BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g); int it_no = 0;)
+  for (;;) {
+    if (lds_load(&ctl.abort_)) return;
+    int32_t dead = n;
+    for (int j = 0; j < Gg; ++j) dead = min(dead, lds_load(&ctl.floor_[j]));
+    const int32_t wb = min(dead, lds_load(&ctl.loaded_hi));
+    if (wb > written) {
+      BB_P(const uint32_t t_a = uint32_t(wall_clock64());)
+      ring_drain(A, mem, written, wb, lane);
+      BB_P(const uint32_t t_b = uint32_t(wall_clock64());)
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in memory
+      written = wb;
+      lds_store(&ctl.written, written);  // their slots may be refilled
+      if (lane == 0) __hip_atomic_store(xself_line, uint32_t(written), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      idle = 0;
+      BB_P(pr.tick(6); pr.add(14, 1);
+           if (tr && lane == 0 && it_no < kTraceIters / 2) {
+             uint32_t *e = tr + 8 * kTraceHalves * 2 + it_no * 4;
+             e[0] = uint32_t(pr.mark); e[1] = t_a; e[2] = uint32_t(wb); e[3] = t_b;
+             ++it_no;
+           })
+      if (written >= n) return;
+    } else if (!aux_idle(idle, spin_limit, ctl, status)) {
+      return;
+    }
+  }
+}
+
+// The loader: polls the previous group's released rows and loads them into
+// free ring slots, in batches, signalling each batch.
+template <typename T>
+__device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
+                             const uint32_t *xprev_line, int lane, int64_t spin_limit, uint32_t *status,
+                             uint32_t *sync) {
+  int32_t loaded = R0;
+  int32_t xprev = xprev_line ? 0 : n;
+  int64_t idle = 0;
+  BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g); int it_no = 0;)
+  for (;;) {
+    if (lds_load(&ctl.abort_)) return;
+    if (xprev < n) xprev = int32_t(__hip_atomic_load(xprev_line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const int32_t lim = min(min(xprev, lds_load(&ctl.written) + A.W), min(n, loaded + kLoadBatchRows));
+    if (lim > loaded) {
+      ring_fill(A, mem, loaded, lim, lane);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in LDS
+      loaded = lim;
+      lds_store(&ctl.loaded_hi, loaded);
+      idle = 0;
+      BB_P(pr.tick(8); pr.add(13, 1);
+           if (tr && lane == 0 && it_no < kTraceIters / 2) {
+             uint32_t *e = tr + 8 * kTraceHalves * 2 + (kTraceIters / 2 + it_no) * 4;
+             e[0] = uint32_t(pr.mark); e[1] = uint32_t(xprev); e[2] = uint32_t(loaded); e[3] = 0;
+             ++it_no;
+           })
+      if (loaded >= n) return;
+    } else if (!aux_idle(idle, spin_limit, ctl, status)) {
+      return;
+    }
+  }
+}
+
+// Persistent group kernel: workgroups claim groups in increasing order.
+// blockDim = 64 (G + 2); dynamic LDS = W * S * sizeof(T).
+template <typename T, int MAXM, int SC>
+__global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, int32_t sub, int32_t n, int b,
+                                                                 int t, int d, int32_t nsweeps, int G, int W,
+                                                                 uint32_t *sync, int64_t spin_limit) {
+  extern __shared__ __align__(16) unsigned char lds_ring[];
+  __shared__ GroupCtl ctl;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);  // wave-uniform
+  const int lane = int(threadIdx.x) & 63;
+  uint32_t *status = sync;
+  uint32_t *claim = sync + kClaim;
+  uint32_t *prog = sync + kSyncHeader;
+  const Ring<T> A{reinterpret_cast<T *>(lds_ring), S, W, sub};
+  const __amdgpu_buffer_rsrc_t mem =
+      __builtin_amdgcn_make_buffer_rsrc(a, 0, int(uint32_t(int64_t(n) * S * int64_t(sizeof(T)))), kRsrcWord3);
+  if (threadIdx.x == 0) ctl.abort_ = 0;
+  for (;;) {
+    if (threadIdx.x == 0) ctl.g = int32_t(atomicAdd(claim, 1u));
+    __syncthreads();
+    const int32_t g = ctl.g;
+    const int64_t R0l = int64_t(g) * G;
+    if (R0l >= nsweeps || ctl.abort_) break;
+    const int32_t R0 = int32_t(R0l);
+    const int32_t Gg = min(G, nsweeps - R0);
+    __syncthreads();  // every wave has read ctl.g before it is reset below
+    if (threadIdx.x == 0) {
+      ctl.loaded_hi = R0;
+      ctl.written = R0;
+      for (int j = 0; j < kGroupMaxSweeps; ++j) {
+        ctl.prog[j] = 0;
+        ctl.floor_[j] = j < Gg ? R0 + j : n;
+      }
+    }
+    __syncthreads();
+    if (wave < Gg) {
+      group_sweep<T, MAXM, SC>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
+    } else if (wave == G) {
+      group_writer<T>(A, ctl, mem, n, R0, Gg, prog + int64_t(g) * kLine, lane, spin_limit, status, sync);
+    } else if (wave == G + 1) {
+      group_loader<T>(A, ctl, mem, n, R0, g > 0 ? prog + int64_t(g - 1) * kLine : nullptr, lane, spin_limit,
+                      status, sync);
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int MAXM, int SC>
+hipError_t group_t(void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
+                   uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+  const size_t lds = size_t(W) * size_t(g.stride) * sizeof(T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, SC>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_group<T, MAXM, SC>), dim3(unsigned(grid)), dim3(unsigned(64 * (G + 2))), lds, st,
+                     static_cast<T *>(wband), g.stride, g.sub, int32_t(g.n), b, t, d, int32_t(nsweeps), G, W, sync,
+                     spin_limit);
+  return hipGetLastError();
+}
+
+// Row strides with a compile-time specialisation (the working-band strides
+// of BW 64 / TW 16 and BW 32 / TW 16 in fp32, BW 16 / TW 8 in fp64); any
+// other stride runs the generic ring code.
+template <typename T, int MAXM>
+hipError_t group_stride(void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
+                        uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+  if (sizeof(T) == 4 && g.stride == 100)
+    return group_t<T, MAXM, 100>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  if (sizeof(T) == 4 && g.stride == 68)
+    return group_t<T, MAXM, 68>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  if (sizeof(T) == 8 && g.stride == 34)
+    return group_t<T, MAXM, 34>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  return group_t<T, MAXM, 0>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+}
+
+template <typename T>
+hipError_t group_dispatch(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
+                          int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+  switch (maxm) {
+    case 8: return group_stride<T, 8>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    case 9: return group_stride<T, 9>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    case 16: return group_stride<T, 16>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    case 17: return group_stride<T, 17>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
+                        int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+  if (g.dtype == 1) return group_dispatch<double>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  return group_dispatch<float>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+}
+
+}  // namespace bb

@@ -24,6 +24,13 @@ hipError_t launch_step(int maxm, void *wband, const Geometry &g, int b, int t, i
 hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
                           int grid, int nt, int64_t spin_limit, hipStream_t st);
 
+// Sweep groups resident in LDS for one pass: `grid` workgroups of 64 (G+2)
+// threads claim groups of G consecutive sweeps; each keeps a ring of W band
+// rows in LDS; d is the in-group lag in half-cycles.
+constexpr int kGroupMaxWaves = 8;  // G <= 6 sweeps plus a loader and a writer wave (2 waves per SIMD: 256 VGPRs)
+hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
+                        int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st);
+
 // LDS bytes one workgroup stages per cycle for a pass (b, t) with register
 // tile maxm.
 size_t stage_lds_bytes(int dtype, int maxm, int b, int t);

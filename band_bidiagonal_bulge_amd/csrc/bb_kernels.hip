@@ -8,126 +8,16 @@
 // and writes the row back; the same is repeated for the leftmost column of
 // the bulge just created, one thread per column of the left-apply block.
 //
-// Arithmetic contract (so that results are reproducible to the bit by any
-// implementation following it): reflector H = I - tau v v^T with
-// v = (1, x_j / (alpha - beta)), beta = -sign(alpha) ||x|| (sign(+-0) = +1),
-// tau = (beta - alpha) / beta; the tail sum of squares and every dot product
-// are serial in increasing index with fused multiply-adds, nothing else is
-// contracted (-ffp-contract=off), square root and division are correctly
-// rounded.  A zero tail makes the reflector the identity; the annihilated
-// entries are written as exact zeros either way.
+// The arithmetic contract the kernels follow is stated in bb_device.hpp.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
+#include "bb_device.hpp"
 #include "bb_internal.hpp"
 
 namespace bb {
 namespace {
-
-// s_waitcnt immediate with vmcnt = 0 and expcnt / lgkmcnt left at their
-// maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-__device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
-__device__ __forceinline__ double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
-__device__ __forceinline__ float sqrt_(float a) { return __builtin_sqrtf(a); }
-__device__ __forceinline__ double sqrt_(double a) { return __builtin_sqrt(a); }
-
-template <typename T>
-struct Refl {
-  T beta, tau, inv;
-  bool nz;  // false: identity (zero tail)
-};
-
-// Reflector of x[0..m-1] (x in LDS, read by every thread: broadcast).
-// FULL: m == MAXM, no bounds on the loop.
-template <typename T, int MAXM, bool FULL>
-__device__ __forceinline__ Refl<T> house(const T *x, int m) {
-  Refl<T> h;
-  const T alpha = x[0];
-  T s = T(0);
-#pragma unroll
-  for (int j = 1; j < MAXM; ++j)
-    if (FULL || j < m) s = fma_(x[j], x[j], s);
-  if (s == T(0)) {
-    h.nz = false;
-    h.beta = alpha;
-    h.tau = T(0);
-    h.inv = T(0);
-    return h;
-  }
-  const T nrm = sqrt_(fma_(alpha, alpha, s));
-  h.beta = (alpha >= T(0)) ? -nrm : nrm;
-  h.tau = (h.beta - alpha) / h.beta;
-  h.inv = T(1) / (alpha - h.beta);
-  h.nz = true;
-  return h;
-}
-
-// Band in memory through a buffer resource: element (i, j) at byte offset
-// (i*ld + j - i + sub) * sizeof(T).  Out-of-range loads return zero and
-// out-of-range stores are dropped by the hardware.  AUX is the cache policy:
-// 0 for ordinary accesses (one launch per step: the kernel boundary orders
-// the cycles), kSc1 for agent-scope accesses that stay coherent across the
-// XCDs' separate L2 caches (workgroups handing data to each other inside one
-// launch).
-constexpr int kSc1 = 16;
-constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor
-
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-template <typename T, int AUX>
-struct Band {
-  __amdgpu_buffer_rsrc_t r;
-  int64_t ld;
-  int32_t sub;
-  int64_t n;
-  __device__ __forceinline__ uint32_t off(int64_t i, int64_t j) const {
-    return uint32_t((i * ld + (j - i + sub)) * int64_t(sizeof(T)));
-  }
-  // byte offset of (i, j) and byte strides: next column +sizeof(T), next row
-  // (same column) +(ld-1)*sizeof(T)
-  __device__ __forceinline__ uint32_t row_step() const { return uint32_t((ld - 1) * int64_t(sizeof(T))); }
-  __device__ __forceinline__ T ld_(uint32_t o) const {
-    if constexpr (sizeof(T) == 4)
-      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, AUX));
-    else
-      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, AUX));
-  }
-  __device__ __forceinline__ u32x4 ld4_(uint32_t o) const { return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, AUX); }
-  __device__ __forceinline__ void st4_(uint32_t o, u32x4 v) const { __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, AUX); }
-  __device__ __forceinline__ void st_(uint32_t o, T v) const {
-    if constexpr (sizeof(T) == 4)
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, o, 0, AUX);
-    else
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, o, 0, AUX);
-  }
-};
-
-template <typename T, int AUX>
-__device__ __forceinline__ Band<T, AUX> make_band(T *a, int64_t ld, int32_t sub, int64_t n) {
-  Band<T, AUX> B;
-  B.r = __builtin_amdgcn_make_buffer_rsrc(a, 0, int(uint32_t(n * ld * int64_t(sizeof(T)))), kRsrcWord3);
-  B.ld = ld;
-  B.sub = sub;
-  B.n = n;
-  return B;
-}
-
-// Geometry of cycle (R, k) of the pass (b, t).
-struct Cyc {
-  int64_t c, ch, r, jend;
-  int m;
-  __device__ __forceinline__ Cyc(int64_t n, int b, int t, int64_t R, int64_t k) {
-    c = R + (b - t) + k * b;
-    ch = c + t < n - 1 ? c + t : n - 1;
-    m = int(ch - c + 1);
-    r = (k == 0) ? R : c - b;
-    jend = c + t + b < n - 1 ? c + t + b : n - 1;
-  }
-};
 
 // Vector access to the m <= MAXM consecutive entries of one band row segment
 // (16-byte loads/stores where they fit, a scalar tail otherwise).  A
@@ -308,11 +198,6 @@ __global__ void __launch_bounds__(256) k_step(T *a, int64_t ld, int32_t sub, int
   col_half_any<T, MAXM>(A, q, ys);
 }
 
-// Cycles of sweep R: k = 0 .. K-1 with R + b' + k b <= n-2.
-__device__ __forceinline__ int64_t cycles_of_dev(int64_t n, int b, int t, int64_t R) {
-  const int64_t last = n - 2 - R - (b - t);
-  return last < 0 ? 0 : last / b + 1;
-}
 
 // Half-cycles of sweep R-1 that must be complete before half h of cycle k of
 // sweep R may start.  Half-cycles are numbered 2k (row half) and 2k+1
@@ -456,12 +341,12 @@ __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, 
 // User band (row-offset layout) -> working band with zeroed bulge room.
 template <typename T>
 __global__ void k_pack(const T *__restrict__ band, int64_t ld_band, int64_t n, int bw, T *__restrict__ a,
-                       int64_t ld, int sub) {
-  const int64_t total = n * ld;
+                       int64_t stride, int sub) {
+  const int64_t total = n * stride;
   for (int64_t q = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; q < total;
        q += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t i = q / ld;
-    const int64_t o = q - i * ld - sub;  // j - i
+    const int64_t i = q / stride;
+    const int64_t o = q - i * stride - sub;  // j - i
     T v = T(0);
     if (o >= 0 && o <= bw && i + o < n) v = band[i * ld_band + o];
     a[q] = v;
@@ -469,11 +354,12 @@ __global__ void k_pack(const T *__restrict__ band, int64_t ld_band, int64_t n, i
 }
 
 template <typename T>
-__global__ void k_extract(const T *__restrict__ a, int64_t ld, int sub, int64_t n, T *__restrict__ d,
+__global__ void k_extract(const T *__restrict__ a, int64_t stride, int sub, int64_t n, T *__restrict__ d,
                           T *__restrict__ e) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) {
-    d[i] = a[i * ld + sub];
-    if (e != nullptr && i + 1 < n) e[i] = (ld > sub + 1) ? a[i * ld + sub + 1] : T(0);
+    d[i] = a[i * stride + sub];
+    // stride >= sub + 2 always (padding to 16 bytes); with bw = 0 the entry is padding and reads zero
+    if (e != nullptr && i + 1 < n) e[i] = a[i * stride + sub + 1];
   }
 }
 
@@ -494,7 +380,7 @@ hipError_t step_t(void *wband, const Geometry &g, int b, int t, int64_t L, int s
                   int nt, hipStream_t st) {
   hipLaunchKernelGGL((k_step<T, MAXM>), dim3(unsigned(nblk)), dim3(nt), 0, st,
                      static_cast<T *>(wband),
-                     int64_t(g.ld), g.sub, g.n, b, t, L, s, Rlo);
+                     int64_t(g.stride), g.sub, g.n, b, t, L, s, Rlo);
   return hipGetLastError();
 }
 
@@ -519,7 +405,7 @@ hipError_t persist_t(void *wband, const Geometry &g, int b, int t, int64_t nswee
                      int nt, int64_t spin_limit, hipStream_t st) {
   hipLaunchKernelGGL((k_persist<T, MAXM, BB_PERSIST_AUX>), dim3(unsigned(grid)), dim3(nt), 0, st,
                      static_cast<T *>(wband),
-                     int64_t(g.ld), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
+                     int64_t(g.stride), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
   return hipGetLastError();
 }
 
@@ -555,13 +441,13 @@ hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t
 
 hipError_t launch_pack(const void *band, int64_t ld_band, void *wband, const Geometry &g, hipStream_t st) {
   const int block = 256;
-  const unsigned grid = grid_for(g.n * g.ld, block);
+  const unsigned grid = grid_for(g.n * g.stride, block);
   if (g.dtype == 1)
     hipLaunchKernelGGL(k_pack<double>, dim3(grid), dim3(block), 0, st, static_cast<const double *>(band), ld_band,
-                       g.n, g.bw, static_cast<double *>(wband), int64_t(g.ld), g.sub);
+                       g.n, g.bw, static_cast<double *>(wband), int64_t(g.stride), g.sub);
   else
     hipLaunchKernelGGL(k_pack<float>, dim3(grid), dim3(block), 0, st, static_cast<const float *>(band), ld_band,
-                       g.n, g.bw, static_cast<float *>(wband), int64_t(g.ld), g.sub);
+                       g.n, g.bw, static_cast<float *>(wband), int64_t(g.stride), g.sub);
   return hipGetLastError();
 }
 
@@ -570,10 +456,10 @@ hipError_t launch_extract(const void *wband, const Geometry &g, void *d, void *e
   const unsigned grid = grid_for(g.n, block);
   if (g.dtype == 1)
     hipLaunchKernelGGL(k_extract<double>, dim3(grid), dim3(block), 0, st, static_cast<const double *>(wband),
-                       int64_t(g.ld), g.sub, g.n, static_cast<double *>(d), static_cast<double *>(e));
+                       int64_t(g.stride), g.sub, g.n, static_cast<double *>(d), static_cast<double *>(e));
   else
     hipLaunchKernelGGL(k_extract<float>, dim3(grid), dim3(block), 0, st, static_cast<const float *>(wband),
-                       int64_t(g.ld), g.sub, g.n, static_cast<float *>(d), static_cast<float *>(e));
+                       int64_t(g.stride), g.sub, g.n, static_cast<float *>(d), static_cast<float *>(e));
   return hipGetLastError();
 }
 

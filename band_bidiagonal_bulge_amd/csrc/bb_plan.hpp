@@ -53,14 +53,19 @@ inline int64_t steps_of(int64_t n, const Pass &p, int32_t s) {
   return best;
 }
 
-// Working band: element (i, j) at band[i*ld + (j - i + sub)], with room for
-// the bulge: sub = t of the first pass diagonals below the main diagonal and
-// bw + sub above it (nonzeros of a pass with (b, t) never leave that range).
+// Working band: element (i, j) at band[i*stride + (j - i + sub)], with room
+// for the bulge: sub = t of the first pass diagonals below the main diagonal
+// and bw + sub above it (nonzeros of a pass with (b, t) never leave that
+// range), ld = bw + 2 sub + 1 entries in use per row.  The row stride pads ld
+// to a multiple of 16 bytes: rows are whole 16-byte units (vector copies of
+// row ranges), and stride - 1 is odd, so lanes reading one row each at the
+// same column hit distinct LDS banks.
 struct Geometry {
   int64_t n = 0;
   int32_t bw = 0, tw = 0, dtype = 0, esize = 0;
   int32_t sub = 0, ld = 0, maxt = 0;
-  size_t band_bytes = 0;   // n * ld * esize, rounded up to 256
+  int32_t stride = 0;      // elements between rows of the working band
+  size_t band_bytes = 0;   // n * stride * esize, rounded up to 256
   size_t sync_offset = 0;  // byte offset of the counters
   size_t sync_words = 0;   // 32-bit words of counters
   size_t total_bytes = 0;
@@ -86,7 +91,9 @@ inline Geometry make_geometry(int64_t n, int32_t bw, int32_t tw, int32_t dtype) 
   g.maxt = bw > 1 ? std::min(tw, bw - 1) : 0;
   g.sub = g.maxt;
   g.ld = g.sub + bw + g.maxt + 1;
-  g.band_bytes = (size_t(n) * size_t(g.ld) * size_t(g.esize) + 255) / 256 * 256;
+  const int32_t per16 = 16 / g.esize;
+  g.stride = (g.ld + per16 - 1) / per16 * per16;
+  g.band_bytes = (size_t(n) * size_t(g.stride) * size_t(g.esize) + 255) / 256 * 256;
   g.sync_offset = g.band_bytes;
   g.sync_words = size_t(kSyncHeader + (n + 1) * kLine);
   g.total_bytes = g.sync_offset + (g.sync_words * 4 + 255) / 256 * 256;
@@ -108,6 +115,64 @@ inline CycleShape cycle_shape(int64_t n, const Pass &p, int64_t R, int64_t k) {
   const int64_t r = k == 0 ? R : c - p.b;
   const int64_t jend = std::min<int64_t>(c + p.t + p.b, n - 1);
   return {ch - c + 1, ch - r + 1, jend - c + 1};
+}
+
+// Half-cycle lag between consecutive sweeps: 2 when b' >= 3, 3 when b' = 2,
+// 4 when b' = 1.
+inline int lag_of(const Pass &p) {
+  const int bp = p.b - p.t;
+  return bp >= 3 ? 2 : (bp == 2 ? 3 : 4);
+}
+
+// Rows a sweep touches in half-cycle q (2k: row half, 2k+1: column half):
+// [lo, hi].
+inline void half_rows(int64_t n, const Pass &p, int64_t R, int64_t q, int64_t *lo, int64_t *hi) {
+  const int64_t k = q >> 1;
+  const int64_t c = R + (p.b - p.t) + k * p.b;
+  *hi = std::min<int64_t>(c + p.t, n - 1);
+  *lo = (q & 1) ? c : (k == 0 ? R : c - p.b);
+}
+
+// Ring rows a sweep group of G needs so that it always makes progress.  In a
+// state where no wave can move, each wave waits for its predecessor with
+// exactly d-1 half-cycles of lag in completed halves (or for rows); the ring
+// must then hold every row from the lowest row any wave will still touch to
+// the highest row any wave needs.  Bounded from above by taking the rows
+// needed at lag d-1 and the lowest rows at lag d, over every group and step.
+inline int64_t group_ring_rows(int64_t n, const Pass &p, int G) {
+  const int64_t ns = sweeps_of(n, p);
+  const int d = lag_of(p);
+  int64_t need = 0;
+  std::vector<int64_t> K(size_t(G), 0);
+  for (int64_t R0 = 0; R0 < ns; R0 += G) {
+    const int Gg = int(std::min<int64_t>(G, ns - R0));
+    int64_t steps = 0;
+    for (int j = 0; j < Gg; ++j) {
+      K[size_t(j)] = cycles_of(n, p, R0 + j);
+      steps = std::max<int64_t>(steps, 2 * K[size_t(j)] + int64_t(j) * d);
+    }
+    for (int64_t q0 = 0; q0 < steps; ++q0) {
+      int64_t hi = -1, fl = n;
+      for (int j = 0; j < Gg; ++j) {
+        const int64_t R = R0 + j, twoK = 2 * K[size_t(j)];
+        int64_t lo, h;
+        const int64_t qa = q0 - int64_t(j) * (d - 1);  // most advanced position: rows needed
+        if (qa >= 0 && qa < twoK) {
+          half_rows(n, p, R, qa, &lo, &h);
+          hi = std::max(hi, h);
+        }
+        const int64_t qb = q0 - int64_t(j) * d;  // least advanced position: rows still live
+        if (qb < 0) {
+          fl = std::min(fl, R);
+        } else if (qb < twoK) {
+          half_rows(n, p, R, qb, &lo, &h);
+          fl = std::min(fl, lo);
+        }
+      }
+      if (hi >= 0) need = std::max(need, hi - fl + 1);
+    }
+  }
+  return need;
 }
 
 }  // namespace bb

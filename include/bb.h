@@ -56,7 +56,10 @@ typedef enum {
 typedef enum {
   BB_SCHED_DEFAULT = 0,   /* the fastest scheduler for the shape */
   BB_SCHED_STEP = 1,      /* one launch per step: step L runs every (R, k=L-s*R) */
-  BB_SCHED_PERSISTENT = 2 /* resident workgroups; per-sweep progress counters */
+  BB_SCHED_PERSISTENT = 2, /* resident workgroups; per-sweep progress counters */
+  BB_SCHED_GROUP = 3       /* resident workgroups each running a group of
+                              consecutive sweeps on a ring of band rows in LDS;
+                              passes whose ring does not fit run PERSISTENT */
 } bb_scheduler;
 
 /* Optional tuning; pass NULL for the gfx950 defaults.  Zero fields take the
@@ -66,9 +69,11 @@ typedef struct {
   int32_t stagger;           /* cycles between consecutive sweeps: 0 = the
                                 smallest safe value (2 when the pass's target
                                 bandwidth b' > 1, else 3); 3 = always three */
-  int32_t max_blocks;        /* persistent: resident workgroups (0 = device fill) */
+  int32_t max_blocks;        /* persistent, group: resident workgroups (0 = device fill) */
   int32_t threads_per_block; /* 64..256, multiple of 64 (0 = default) */
-  int64_t spin_limit;        /* persistent: polls before BB_ERR_TIMEOUT (0 = default) */
+  int64_t spin_limit;        /* persistent, group: polls before BB_ERR_TIMEOUT (0 = default) */
+  int32_t group_sweeps;      /* group: sweeps per workgroup, 1..6 (0 = the most that fit) */
+  int32_t reserved;          /* must be 0 */
 } bb_tuning;
 
 /* Host-side plan of a reduction (no device work). */

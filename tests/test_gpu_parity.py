@@ -81,7 +81,7 @@ def test_all_zero_and_zero_rows(dt):
     _check_bitwise(band, bw, tw)
 
 
-STEP, PERSIST = 1, 2
+STEP, PERSIST, GROUP = 1, 2, 3
 
 
 @pytest.mark.parametrize("tun", [dict(scheduler=STEP), dict(scheduler=STEP, stagger=3),
@@ -89,7 +89,11 @@ STEP, PERSIST = 1, 2
                                  dict(scheduler=PERSIST), dict(scheduler=PERSIST, max_blocks=1),
                                  dict(scheduler=PERSIST, max_blocks=2), dict(scheduler=PERSIST, max_blocks=7),
                                  dict(scheduler=PERSIST, threads_per_block=64),
-                                 dict(scheduler=PERSIST, threads_per_block=256, max_blocks=1000)])
+                                 dict(scheduler=PERSIST, threads_per_block=256, max_blocks=1000),
+                                 dict(scheduler=GROUP), dict(scheduler=GROUP, group_sweeps=1),
+                                 dict(scheduler=GROUP, group_sweeps=2, max_blocks=1),
+                                 dict(scheduler=GROUP, group_sweeps=3, max_blocks=2),
+                                 dict(scheduler=GROUP, group_sweeps=6, max_blocks=5)])
 @pytest.mark.parametrize("n,bw,tw,dt", [(900, 48, 16, "f32"), (700, 24, 7, "f64"), (400, 9, 2, "f32")])
 def test_scheduler_variants_bitwise(tun, n, bw, tw, dt):
     log(f"variant {tun} n={n} bw={bw} tw={tw} {dt}")
@@ -97,15 +101,16 @@ def test_scheduler_variants_bitwise(tun, n, bw, tw, dt):
     _check_bitwise(band, bw, tw, bbm.tuning(**tun))
 
 
-def test_forced_timeout_reports_status():
+@pytest.mark.parametrize("sched", [PERSIST, GROUP])
+def test_forced_timeout_reports_status(sched):
     # A spin limit of one poll makes the first wait on a predecessor expire;
     # every workgroup then stops and the launch ends normally.
     import torch
     n, bw, tw = 3000, 32, 16
     band = torch.from_numpy(bb_inputs.make_band(n, bw, "f32", "normal", seed=2)).to("cuda:0")
     work = bbm.workspace(n, bw, tw, band.dtype)
-    log("forced timeout")
-    bbm.reduce(band, bw, tw, bbm.tuning(scheduler=PERSIST, spin_limit=1), work)
+    log(f"forced timeout sched={sched}")
+    bbm.reduce(band, bw, tw, bbm.tuning(scheduler=sched, spin_limit=1), work)
     st = bbm.bb_device_status(work.data_ptr(), n, bw, tw, 0, torch.cuda.current_stream().cuda_stream)
     assert st == 5, bbm.bb_status_str(st)
     # the next normal call on the same workspace clears the status
@@ -174,7 +179,7 @@ def test_workload_stored_oracle(name):
     assert np.all(W[:, off] == 0)
 
 
-@pytest.mark.parametrize("sched", [bbm.BB_SCHED_STEP, bbm.BB_SCHED_PERSISTENT])
+@pytest.mark.parametrize("sched", [bbm.BB_SCHED_STEP, bbm.BB_SCHED_PERSISTENT, bbm.BB_SCHED_GROUP])
 @pytest.mark.parametrize("n,bw,tw,dt", [(700, 48, 16, "f32"), (333, 20, 7, "f64")])
 def test_staged_calls_equal_reduce(n, bw, tw, dt, sched):
     """bb_pack + bb_run_pass (each pass, in order) + bb_extract == bb_reduce, and
