@@ -50,8 +50,9 @@ struct GroupCtl {
   int32_t loaded_hi;                 // rows [R0, loaded_hi) resident in the ring
   int32_t written;                   // rows [R0, written) written back; their slots are free
   int32_t abort_;                    // a wait expired: drain
-  int32_t prog[kGroupMaxSweeps];     // half-cycles completed by sweep j
-  int32_t floor_[kGroupMaxSweeps];   // lowest row sweep j will still touch
+  // per sweep j, published together by one 8-byte release store:
+  //   word 0: half-cycles completed; word 1: lowest row the sweep will still touch
+  uint64_t sweep[kGroupMaxSweeps];
 };
 
 __device__ __forceinline__ int32_t lds_load(const int32_t *p) {
@@ -60,13 +61,27 @@ __device__ __forceinline__ int32_t lds_load(const int32_t *p) {
 __device__ __forceinline__ void lds_store(int32_t *p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+__device__ __forceinline__ uint64_t sweep_word(int32_t prog, int32_t floor_row) {
+  return uint64_t(uint32_t(prog)) | (uint64_t(uint32_t(floor_row)) << 32);
+}
+__device__ __forceinline__ int32_t sweep_prog(uint64_t w) { return int32_t(uint32_t(w)); }
+__device__ __forceinline__ int32_t sweep_floor(uint64_t w) { return int32_t(uint32_t(w >> 32)); }
+__device__ __forceinline__ uint64_t lds_load64(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Bounded LDS poll until the progress of a sweep reaches `need` (whole
+// wave); `known` caches the last value seen, so a satisfied wait costs no
+// LDS access.  False on expiry or abort.
+__device__ __forceinline__ bool prog_wait(const uint64_t *w, int32_t &known, int32_t need, GroupCtl &ctl,
+                                          int64_t spin_limit, uint32_t *status);
 
 // Bounded LDS poll until *p >= need (whole wave).  False on expiry or abort.
 __device__ __forceinline__ bool lds_wait(const int32_t *p, int32_t need, GroupCtl &ctl, int64_t spin_limit,
                                          uint32_t *status) {
   int64_t polls = 0;
   while (lds_load(p) < need) {
-    if (lds_load(&ctl.abort_)) return false;
+    if ((polls & 15) == 15 && lds_load(&ctl.abort_)) return false;
     __builtin_amdgcn_s_sleep(1);
     if (++polls > spin_limit) {
       lds_store(&ctl.abort_, 1);
@@ -112,6 +127,32 @@ __device__ __forceinline__ uint32_t *trace_base(uint32_t *sync, int32_t n, int g
 #define BB_P(stmt)
 #endif
 
+__device__ __forceinline__ bool prog_wait(const uint64_t *w, int32_t &known, int32_t need, GroupCtl &ctl,
+                                          int64_t spin_limit, uint32_t *status) {
+  if (known >= need) return true;
+  int64_t polls = 0;
+  for (;;) {
+    known = sweep_prog(lds_load64(w));
+    if (known >= need) return true;
+    if ((polls & 15) == 15 && lds_load(&ctl.abort_)) return false;
+    __builtin_amdgcn_s_sleep(1);
+    if (++polls > spin_limit) {
+      lds_store(&ctl.abort_, 1);
+      __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+}
+
+// The same for the loaded-rows bound of the ring.
+__device__ __forceinline__ bool rows_wait(const int32_t *p, int32_t &known, int32_t need, GroupCtl &ctl,
+                                          int64_t spin_limit, uint32_t *status) {
+  if (known >= need) return true;
+  if (!lds_wait(p, need, ctl, spin_limit, status)) return false;
+  known = lds_load(p);
+  return true;
+}
+
 // Ring of W band rows in LDS, S elements each (the working band's row
 // stride): row i lives in slot i mod W, element (i, j) at
 // L[slot * S + (j - i + sub)].
@@ -153,8 +194,8 @@ __device__ __forceinline__ Refl<T> house_from(T alpha, T sn) {
 // three serial chains overlap.  Row r becomes (beta, 0, ..., 0).
 //   sr: ring slot of row r; nr = ch - r rows below it.
 template <typename T, int MAXM, bool FULL, bool TWO>
-__device__ void ring_row_half(const Ring<T> &A, int32_t r, int32_t c, int32_t m, int32_t nr, int32_t sr,
-                              int lane) {
+__device__ __attribute__((noinline)) void ring_row_half(const Ring<T> &A, int32_t r, int32_t c, int32_t m,
+                                                        int32_t nr, int32_t sr, int lane) {
   T *L = A.L;
   const int32_t colr = c - r + A.sub;          // column c within row r
   const T *px = L + sr * A.S + colr;
@@ -234,7 +275,8 @@ __device__ void ring_row_half(const Ring<T> &A, int32_t r, int32_t c, int32_t m,
 //   sc: ring slot of row c; nc = jend - c columns right of c.
 // Element (c+i, c+jj) sits at L[o_i + jj], o_i = slot(c+i) * S + sub - i.
 template <typename T, int MAXM, bool FULL, bool TWO>
-__device__ void ring_col_half(const Ring<T> &A, int32_t m, int32_t nc, int32_t sc, int lane) {
+__device__ __attribute__((noinline)) void ring_col_half(const Ring<T> &A, int32_t m, int32_t nc, int32_t sc,
+                                                        int lane) {
   T *L = A.L;
   int32_t o[MAXM];
 #pragma unroll
@@ -445,6 +487,7 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
   int32_t c = R + (b - t);
   int32_t sc = A.slot(c);
   const int32_t sR = A.slot(R);
+  int32_t known_pred = 0, known_rows = 0;
   BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g);)
   for (int32_t k = 0; k < K; ++k) {
     const int32_t ch = min(c + t, n - 1);
@@ -455,9 +498,9 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
     const int32_t jend = min(c + t + b, n - 1);
     for (int h = 0; h < 2; ++h) {
       const int32_t q = 2 * k + h;
-      if (j > 0 && !lds_wait(&ctl.prog[j - 1], min(q + d, 2 * Kp), ctl, spin_limit, status)) return;
+      if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(q + d, 2 * Kp), ctl, spin_limit, status)) return;
       BB_P(pr.tick(0);)
-      if (!lds_wait(&ctl.loaded_hi, ch + 1, ctl, spin_limit, status)) return;
+      if (!rows_wait(&ctl.loaded_hi, known_rows, ch + 1, ctl, spin_limit, status)) return;
       BB_P(pr.tick(1); if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2] = uint32_t(pr.mark);)
       if (SC > 0 && m == MAXM && (h == 0 ? sr + (ch - r) : sc + m - 1) < A.W) {
         // interior block without a ring wrap: compile-time stride
@@ -495,11 +538,10 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
       // The next half (this cycle's column half, or the next cycle's row
       // half) starts at row c; after the last half the sweep touches nothing.
       const int32_t fl = q + 1 < 2 * K ? c : n;
-      if (q + 1 == 2 * K && j > 0 && !lds_wait(&ctl.prog[j - 1], 2 * Kp, ctl, spin_limit, status)) return;
-      if (lane == 0) {
-        lds_store(&ctl.floor_[j], fl);
-        lds_store(&ctl.prog[j], q + 1);
-      }
+      if (q + 1 == 2 * K && j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, 2 * Kp, ctl, spin_limit, status))
+        return;
+      if (lane == 0)  // one release: the half's LDS writes are complete before either word moves
+        __hip_atomic_store(&ctl.sweep[j], sweep_word(q + 1, fl), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       BB_P(pr.tick(4); pr.add(5, 1);
            if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2 + 1] = uint32_t(pr.mark);)
     }
@@ -574,7 +616,7 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
   for (;;) {
     if (lds_load(&ctl.abort_)) return;
     int32_t dead = n;
-    for (int j = 0; j < Gg; ++j) dead = min(dead, lds_load(&ctl.floor_[j]));
+    for (int j = 0; j < Gg; ++j) dead = min(dead, sweep_floor(lds_load64(&ctl.sweep[j])));
     const int32_t wb = min(dead, lds_load(&ctl.loaded_hi));
     if (wb > written) {
       BB_P(const uint32_t t_a = uint32_t(wall_clock64());)
@@ -661,8 +703,7 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
       ctl.loaded_hi = R0;
       ctl.written = R0;
       for (int j = 0; j < kGroupMaxSweeps; ++j) {
-        ctl.prog[j] = 0;
-        ctl.floor_[j] = j < Gg ? R0 + j : n;
+        ctl.sweep[j] = sweep_word(0, j < Gg ? R0 + j : n);
       }
     }
     __syncthreads();

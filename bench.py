@@ -239,7 +239,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 5),
                      "traffic": None if traffic is None else round(traffic["hbm_bytes_per_launch"], 1),
-                     "kernel": "k_persist (cycle kernel), one launch per pass",
+                     "kernel": "cycle kernel (k_group where the pass's LDS ring fits, else k_persist), "
+                               "one launch per pass",
                      "launches": launches, "avg_launch_ms": round(avg_launch_ms, 4),
                      "alg_bytes_per_launch": bytes_per_launch},
         "passes": [{"b": b, "t": t, "alg_bytes": ab, "median_ms": round(statistics.median(pass_ms[i]), 4),
@@ -265,7 +266,7 @@ def _read_counter_csv(path, counter):
 
 
 def ingest_counters(workload, fetch_csv, write_csv, copy_mib):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the cycle kernel, each
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the cycle kernels, each
     scaled by what the same counter reads for the plain copy of copy_mib MiB
     (which moves exactly copy_mib MiB each way)."""
     if copy_mib <= 0:
@@ -275,7 +276,7 @@ def ingest_counters(workload, fetch_csv, write_csv, copy_mib):
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _read_counter_csv(path, name)
         copy = [v for (k, v) in rows if "copybuffer" in k.lower()]
-        cyc = [v for (k, v) in rows if "k_persist" in k]
+        cyc = [v for (k, v) in rows if "k_group" in k or "k_persist" in k or "k_step" in k]
         if not copy or not cyc:
             raise SystemExit(f"{path}: no copy-probe or cycle-kernel rows for {name}")
         factor = (copy_mib * 1024.0) / max(copy)  # KiB the copy moves / KiB counted
