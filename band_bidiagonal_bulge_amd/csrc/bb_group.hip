@@ -189,24 +189,25 @@ __device__ __forceinline__ Refl<T> house_from(T alpha, T sn) {
 
 // Row half of a cycle on the ring, one wave.  Row r's entries c..ch (x) give
 // the reflector; it is applied from the right to rows r+1..ch, one lane per
-// row: rows r+1+lane and r+65+lane, whose dot products with x are
+// row: rows r+1+lane and (TWO) r+65+lane, whose dot products with x are
 // accumulated alongside the norm (neither depends on the reflector), so the
-// three serial chains overlap.  Row r becomes (beta, 0, ..., 0).
-//   sr: ring slot of row r; nr = ch - r rows below it.
-template <typename T, int MAXM, bool FULL, bool TWO>
-__device__ __attribute__((noinline)) void ring_row_half(const Ring<T> &A, int32_t r, int32_t c, int32_t m,
-                                                        int32_t nr, int32_t sr, int lane) {
+// serial chains overlap.  Row r becomes (beta, 0, ..., 0), one element per
+// lane.  SC: compile-time row stride (0: the ring's runtime stride).
+//   sr: ring slot of row r; colr = c - r + sub (column c within row r);
+//   nr = ch - r rows below r.
+template <typename T, int MAXM, bool FULL, bool TWO, int SC>
+__device__ void ring_row_half(const Ring<T> &A, int32_t sr, int32_t colr, int32_t m, int32_t nr, int lane) {
+  const int32_t S = SC ? SC : A.S;
   T *L = A.L;
-  const int32_t colr = c - r + A.sub;          // column c within row r
-  const T *px = L + sr * A.S + colr;
+  T *px = L + sr * S + colr;
   const int32_t a0 = lane + 1, a1 = lane + 65;
   const bool h0 = a0 <= nr, h1 = a1 <= nr;
   const int32_t i0 = h0 ? a0 : nr, i1 = h1 ? a1 : nr;  // inactive lanes read row ch, store nothing
   int32_t s0 = sr + i0, s1 = sr + i1;
   s0 = s0 >= A.W ? s0 - A.W : s0;
   s1 = s1 >= A.W ? s1 - A.W : s1;
-  T *p0 = L + s0 * A.S + (colr - i0);
-  T *p1 = L + s1 * A.S + (colr - i1);
+  T *p0 = L + s0 * S + (colr - i0);
+  T *p1 = L + s1 * S + (colr - i1);
   T x[MAXM], v0[MAXM], v1[MAXM];
 #pragma unroll
   for (int j = 0; j < MAXM; ++j) {
@@ -244,7 +245,7 @@ __device__ __attribute__((noinline)) void ring_row_half(const Ring<T> &A, int32_
     for (int32_t i = 129 + lane; i <= nr; i += 64) {  // bands wider than 128 rows
       int32_t si = sr + i;
       si = si >= A.W ? si - A.W : si;
-      T *p = L + si * A.S + (colr - i);
+      T *p = L + si * S + (colr - i);
       T v[MAXM];
 #pragma unroll
       for (int j = 0; j < MAXM; ++j) v[j] = (FULL || j < m) ? p[j] : T(0);
@@ -259,172 +260,39 @@ __device__ __attribute__((noinline)) void ring_row_half(const Ring<T> &A, int32_
         if (FULL || j < m) p[j] = fma_(-tw, xv[j], v[j]);
     }
   }
-  if (lane == 0) {
-    T *p = L + sr * A.S + colr;
-    if (h.nz) p[0] = h.beta;
-#pragma unroll
-    for (int j = 1; j < MAXM; ++j)
-      if (FULL || j < m) p[j] = T(0);
+  if (lane < m) {
+    if (lane > 0)
+      px[lane] = T(0);
+    else if (h.nz)
+      px[0] = h.beta;
   }
 }
 
-// Column half of a cycle on the ring, one wave.  Column c's entries in rows
-// c..ch (y) give the reflector; it is applied from the left to columns
-// c+1..jend, one lane per column (c+1+lane and c+65+lane), dot products
-// accumulated alongside the norm.  Column c becomes (beta, 0, ..., 0).
-//   sc: ring slot of row c; nc = jend - c columns right of c.
-// Element (c+i, c+jj) sits at L[o_i + jj], o_i = slot(c+i) * S + sub - i.
-template <typename T, int MAXM, bool FULL, bool TWO>
-__device__ __attribute__((noinline)) void ring_col_half(const Ring<T> &A, int32_t m, int32_t nc, int32_t sc,
-                                                        int lane) {
-  T *L = A.L;
-  int32_t o[MAXM];
+// Column half on the ring, one wave.  Column c's entries in rows c..ch (y)
+// give the reflector; it is applied from the left to columns c+1..jend, one
+// lane per column (c+1+lane and, TWO, c+65+lane), dot products accumulated
+// alongside the norm.  Column c becomes (beta, 0, ..., 0), one element per
+// lane.  Element (c+i, c+jj) sits at base[off(i) + jj], base = (c, c),
+// off(i) = i*(S-1), less W*S for rows past the end of the ring (WRAP; rows
+// i >= iw).
+template <typename T, int MAXM, bool FULL, bool TWO, int SC, bool WRAP>
+__device__ __forceinline__ void ring_col_body(const Ring<T> &A, T *base, int32_t iw, int32_t m, int32_t nc,
+                                              int lane) {
+  const int32_t S = SC ? SC : A.S;
+  const int32_t D = S - 1;
+  const int32_t WS = A.W * S;
+  int32_t off[MAXM];
 #pragma unroll
-  for (int i = 0, s = sc; i < MAXM; ++i) {
-    o[i] = s * A.S + A.sub - i;
-    s = (s + 1 == A.W) ? 0 : s + 1;
-  }
-  const int32_t a0 = lane + 1, a1 = lane + 65;
-  const bool h0 = a0 <= nc, h1 = a1 <= nc;
-  const int32_t j0 = h0 ? a0 : nc, j1 = h1 ? a1 : nc;
-  T y[MAXM], v0[MAXM], v1[MAXM];
-#pragma unroll
-  for (int i = 0; i < MAXM; ++i) {
-    y[i] = (FULL || i < m) ? L[o[i]] : T(0);
-    v0[i] = (FULL || i < m) ? L[o[i] + j0] : T(0);
-    if (TWO) v1[i] = (FULL || i < m) ? L[o[i] + j1] : T(0);
-  }
-  T sn = T(0), d0 = T(0), d1 = T(0);
-#pragma unroll
-  for (int i = 1; i < MAXM; ++i)
-    if (FULL || i < m) {
-      sn = fma_(y[i], y[i], sn);
-      d0 = fma_(y[i], v0[i], d0);
-      if (TWO) d1 = fma_(y[i], v1[i], d1);
-    }
-  const Refl<T> g = house_from(y[0], sn);
-  if (g.nz) {
-    T yv[MAXM];
-#pragma unroll
-    for (int i = 1; i < MAXM; ++i) yv[i] = y[i] * g.inv;
-    const T tw0 = g.tau * fma_(d0, g.inv, v0[0]);
-    if (h0) {
-      L[o[0] + j0] = v0[0] - tw0;
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) L[o[i] + j0] = fma_(-tw0, yv[i], v0[i]);
-    }
-    if (TWO && h1) {
-      const T tw1 = g.tau * fma_(d1, g.inv, v1[0]);
-      L[o[0] + j1] = v1[0] - tw1;
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) L[o[i] + j1] = fma_(-tw1, yv[i], v1[i]);
-    }
-    for (int32_t jj = 129 + lane; jj <= nc; jj += 64) {  // bands wider than 128 columns
-      T v[MAXM];
-#pragma unroll
-      for (int i = 0; i < MAXM; ++i) v[i] = (FULL || i < m) ? L[o[i] + jj] : T(0);
-      T dd = T(0);
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) dd = fma_(y[i], v[i], dd);
-      const T tw = g.tau * fma_(dd, g.inv, v[0]);
-      L[o[0] + jj] = v[0] - tw;
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) L[o[i] + jj] = fma_(-tw, yv[i], v[i]);
-    }
-  }
-  if (lane == 0) {
-    L[o[0]] = g.nz ? g.beta : y[0];
-#pragma unroll
-    for (int i = 1; i < MAXM; ++i)
-      if (FULL || i < m) L[o[i]] = T(0);
-  }
-}
-
-// The same two halves for a block whose rows sit in consecutive ring slots
-// (no wrap) with a compile-time row stride S: element (i, j) of the block is
-// base[i*(S-1) + j], so every access is one base address plus an immediate
-// offset.  Arithmetic identical to the ring versions above.
-template <typename T, int MAXM, bool FULL, bool TWO, int S>
-__device__ void lin_row_half(T *base, int32_t m, int32_t nr, int lane) {
-  constexpr int32_t D = S - 1;  // (i+1, j+1) is D+1 elements after (i, j); (i+1, j) is D after
-  const int32_t a0 = lane + 1, a1 = lane + 65;
-  const bool h0 = a0 <= nr, h1 = a1 <= nr;
-  const int32_t i0 = h0 ? a0 : nr, i1 = h1 ? a1 : nr;
-  T *p0 = base + i0 * D, *p1 = base + i1 * D;
-  T x[MAXM], v0[MAXM], v1[MAXM];
-#pragma unroll
-  for (int j = 0; j < MAXM; ++j) {
-    x[j] = (FULL || j < m) ? base[j] : T(0);
-    v0[j] = (FULL || j < m) ? p0[j] : T(0);
-    if (TWO) v1[j] = (FULL || j < m) ? p1[j] : T(0);
-  }
-  T sn = T(0), d0 = T(0), d1 = T(0);
-#pragma unroll
-  for (int j = 1; j < MAXM; ++j)
-    if (FULL || j < m) {
-      sn = fma_(x[j], x[j], sn);
-      d0 = fma_(v0[j], x[j], d0);
-      if (TWO) d1 = fma_(v1[j], x[j], d1);
-    }
-  const Refl<T> h = house_from(x[0], sn);
-  if (h.nz) {
-    T xv[MAXM];
-#pragma unroll
-    for (int j = 1; j < MAXM; ++j) xv[j] = x[j] * h.inv;
-    const T tw0 = h.tau * fma_(d0, h.inv, v0[0]);
-    if (h0) {
-      p0[0] = v0[0] - tw0;
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) p0[j] = fma_(-tw0, xv[j], v0[j]);
-    }
-    if (TWO && h1) {
-      const T tw1 = h.tau * fma_(d1, h.inv, v1[0]);
-      p1[0] = v1[0] - tw1;
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) p1[j] = fma_(-tw1, xv[j], v1[j]);
-    }
-    for (int32_t i = 129 + lane; i <= nr; i += 64) {  // bands wider than 128 rows
-      T *p = base + i * D;
-      T v[MAXM];
-#pragma unroll
-      for (int j = 0; j < MAXM; ++j) v[j] = (FULL || j < m) ? p[j] : T(0);
-      T dd = T(0);
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) dd = fma_(v[j], x[j], dd);
-      const T tw = h.tau * fma_(dd, h.inv, v[0]);
-      p[0] = v[0] - tw;
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) p[j] = fma_(-tw, xv[j], v[j]);
-    }
-  }
-  if (lane == 0) {
-    if (h.nz) base[0] = h.beta;
-#pragma unroll
-    for (int j = 1; j < MAXM; ++j)
-      if (FULL || j < m) base[j] = T(0);
-  }
-}
-
-template <typename T, int MAXM, bool FULL, bool TWO, int S>
-__device__ void lin_col_half(T *base, int32_t m, int32_t nc, int lane) {
-  constexpr int32_t D = S - 1;  // element (c+i, c+jj) at base[i*D + jj]
+  for (int i = 0; i < MAXM; ++i) off[i] = i * D - ((WRAP && i >= iw) ? WS : 0);
   const int32_t a0 = lane + 1, a1 = lane + 65;
   const bool h0 = a0 <= nc, h1 = a1 <= nc;
   T *q0 = base + (h0 ? a0 : nc), *q1 = base + (h1 ? a1 : nc);
   T y[MAXM], v0[MAXM], v1[MAXM];
 #pragma unroll
   for (int i = 0; i < MAXM; ++i) {
-    y[i] = (FULL || i < m) ? base[i * D] : T(0);
-    v0[i] = (FULL || i < m) ? q0[i * D] : T(0);
-    if (TWO) v1[i] = (FULL || i < m) ? q1[i * D] : T(0);
+    y[i] = (FULL || i < m) ? base[off[i]] : T(0);
+    v0[i] = (FULL || i < m) ? q0[off[i]] : T(0);
+    if (TWO) v1[i] = (FULL || i < m) ? q1[off[i]] : T(0);
   }
   T sn = T(0), d0 = T(0), d1 = T(0);
 #pragma unroll
@@ -444,20 +312,20 @@ __device__ void lin_col_half(T *base, int32_t m, int32_t nc, int lane) {
       q0[0] = v0[0] - tw0;
 #pragma unroll
       for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) q0[i * D] = fma_(-tw0, yv[i], v0[i]);
+        if (FULL || i < m) q0[off[i]] = fma_(-tw0, yv[i], v0[i]);
     }
     if (TWO && h1) {
       const T tw1 = g.tau * fma_(d1, g.inv, v1[0]);
       q1[0] = v1[0] - tw1;
 #pragma unroll
       for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) q1[i * D] = fma_(-tw1, yv[i], v1[i]);
+        if (FULL || i < m) q1[off[i]] = fma_(-tw1, yv[i], v1[i]);
     }
     for (int32_t jj = 129 + lane; jj <= nc; jj += 64) {  // bands wider than 128 columns
       T *q = base + jj;
       T v[MAXM];
 #pragma unroll
-      for (int i = 0; i < MAXM; ++i) v[i] = (FULL || i < m) ? q[i * D] : T(0);
+      for (int i = 0; i < MAXM; ++i) v[i] = (FULL || i < m) ? q[off[i]] : T(0);
       T dd = T(0);
 #pragma unroll
       for (int i = 1; i < MAXM; ++i)
@@ -466,15 +334,56 @@ __device__ void lin_col_half(T *base, int32_t m, int32_t nc, int lane) {
       q[0] = v[0] - tw;
 #pragma unroll
       for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) q[i * D] = fma_(-tw, yv[i], v[i]);
+        if (FULL || i < m) q[off[i]] = fma_(-tw, yv[i], v[i]);
     }
   }
-  if (lane == 0) {
-    base[0] = g.nz ? g.beta : y[0];
-#pragma unroll
-    for (int i = 1; i < MAXM; ++i)
-      if (FULL || i < m) base[i * D] = T(0);
+  if (lane < m) {
+    const int32_t o = lane * D - ((WRAP && lane >= iw) ? WS : 0);
+    base[o] = lane > 0 ? T(0) : (g.nz ? g.beta : y[0]);
   }
+}
+
+// Row half with fewer than MAXM columns where the padding columns are not
+// known to be zero (tile widths below the register tile): out of line.
+template <typename T, int MAXM, int SC>
+__device__ __attribute__((noinline)) void ring_row_half_masked(const Ring<T> &A, int32_t sr, int32_t colr,
+                                                               int32_t m, int32_t nr, int lane) {
+  ring_row_half<T, MAXM, false, true, SC>(A, sr, colr, m, nr, lane);
+}
+
+// The rare column halves, out of line so that the common one keeps its
+// registers: rows that wrap around the ring (about m/W of the halves) and
+// the truncated last cycle of a sweep (m < MAXM).
+template <typename T, int MAXM, int SC>
+__device__ __attribute__((noinline)) void ring_col_half_rare(const Ring<T> &A, int32_t sc, int32_t m, int32_t nc,
+                                                             int lane) {
+  const int32_t S = SC ? SC : A.S;
+  T *base = A.L + sc * S + A.sub;
+  const int32_t iw = A.W - sc;  // rows c+i with i >= iw wrap to the start of the ring
+  if (m == MAXM) {
+    if (nc > 64)
+      ring_col_body<T, MAXM, true, true, SC, true>(A, base, iw, m, nc, lane);
+    else
+      ring_col_body<T, MAXM, true, false, SC, true>(A, base, iw, m, nc, lane);
+  } else {
+    ring_col_body<T, MAXM, false, true, SC, true>(A, base, iw, m, nc, lane);
+  }
+}
+
+//   sc: ring slot of row c; nc = jend - c columns right of c.
+template <typename T, int MAXM, int SC>
+__device__ __forceinline__ void ring_col_half(const Ring<T> &A, int32_t sc, int32_t m, int32_t nc, int lane) {
+  const int32_t S = SC ? SC : A.S;
+  const int32_t iw = A.W - sc;  // rows c+i with i >= iw wrap to the start of the ring
+  if (m != MAXM || iw < MAXM) {
+    ring_col_half_rare<T, MAXM, SC>(A, sc, m, nc, lane);
+    return;
+  }
+  T *base = A.L + sc * S + A.sub;
+  if (nc > 64)
+    ring_col_body<T, MAXM, true, true, SC, false>(A, base, iw, m, nc, lane);
+  else
+    ring_col_body<T, MAXM, true, false, SC, false>(A, base, iw, m, nc, lane);
 }
 
 // One sweep of the group, run by one wave.  Cycle geometry and ring slots
@@ -502,37 +411,22 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
       BB_P(pr.tick(0);)
       if (!rows_wait(&ctl.loaded_hi, known_rows, ch + 1, ctl, spin_limit, status)) return;
       BB_P(pr.tick(1); if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2] = uint32_t(pr.mark);)
-      if (SC > 0 && m == MAXM && (h == 0 ? sr + (ch - r) : sc + m - 1) < A.W) {
-        // interior block without a ring wrap: compile-time stride
-        if (h == 0) {
-          T *base = A.L + sr * SC + (c - r + A.sub);
-          if (ch - r > 64)
-            lin_row_half<T, MAXM, true, true, SC>(base, m, ch - r, lane);
+      if (h == 0) {
+        // With an exact register tile (MAXM = t+1) a truncated last cycle
+        // (m < MAXM) runs the full-width code: the entries it also reads lie
+        // past column n-1 but inside the row's stored range, hold +0, leave
+        // every sum and update unchanged to the bit, and get +0 written back.
+        const int32_t nr = ch - r, colr = c - r + A.sub;
+        if (m == MAXM || MAXM == t + 1) {
+          if (nr > 64)
+            ring_row_half<T, MAXM, true, true, SC>(A, sr, colr, MAXM, nr, lane);
           else
-            lin_row_half<T, MAXM, true, false, SC>(base, m, ch - r, lane);
+            ring_row_half<T, MAXM, true, false, SC>(A, sr, colr, MAXM, nr, lane);
         } else {
-          T *base = A.L + sc * SC + A.sub;
-          if (jend - c > 64)
-            lin_col_half<T, MAXM, true, true, SC>(base, m, jend - c, lane);
-          else
-            lin_col_half<T, MAXM, true, false, SC>(base, m, jend - c, lane);
+          ring_row_half_masked<T, MAXM, SC>(A, sr, colr, m, nr, lane);
         }
-      } else if (h == 0) {
-        const int32_t nr = ch - r;
-        if (m == MAXM && nr > 64)
-          ring_row_half<T, MAXM, true, true>(A, r, c, m, nr, sr, lane);
-        else if (m == MAXM)
-          ring_row_half<T, MAXM, true, false>(A, r, c, m, nr, sr, lane);
-        else
-          ring_row_half<T, MAXM, false, true>(A, r, c, m, nr, sr, lane);
       } else {
-        const int32_t nc = jend - c;
-        if (m == MAXM && nc > 64)
-          ring_col_half<T, MAXM, true, true>(A, m, nc, sc, lane);
-        else if (m == MAXM)
-          ring_col_half<T, MAXM, true, false>(A, m, nc, sc, lane);
-        else
-          ring_col_half<T, MAXM, false, true>(A, m, nc, sc, lane);
+        ring_col_half<T, MAXM, SC>(A, sc, m, jend - c, lane);
       }
       BB_P(pr.tick(2 + h);)
       // The next half (this cycle's column half, or the next cycle's row
