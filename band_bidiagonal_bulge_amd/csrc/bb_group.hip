@@ -43,7 +43,8 @@ namespace {
 
 constexpr int kGroupMaxSweeps = kGroupMaxWaves - 2;
 
-constexpr int32_t kLoadBatchRows = 64;  // rows per loader batch: early rows are signalled early
+constexpr int32_t kLoadBatchRows = 64;   // rows per loader batch: early rows are signalled early
+constexpr int32_t kDrainBatchRows = 32;  // rows per writer batch, published one batch at a time
 
 struct GroupCtl {
   int32_t g;                         // group being run
@@ -511,7 +512,9 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
     if (lds_load(&ctl.abort_)) return;
     int32_t dead = n;
     for (int j = 0; j < Gg; ++j) dead = min(dead, sweep_floor(lds_load64(&ctl.sweep[j])));
-    const int32_t wb = min(dead, lds_load(&ctl.loaded_hi));
+    // write back in batches, publishing after each: the next group's first
+    // sweep needs the lowest released rows first
+    const int32_t wb = min(min(dead, lds_load(&ctl.loaded_hi)), written + kDrainBatchRows);
     if (wb > written) {
       BB_P(const uint32_t t_a = uint32_t(wall_clock64());)
       ring_drain(A, mem, written, wb, lane);
