@@ -12,6 +12,9 @@ Prints one JSON line:
                   kernels run on), against the published HBM3E peak
   cpu_baseline    the CPU oracle (one thread) timed on a bounded prefix of the
                   same reduction, in the same unit
+  cpu_threaded    the oracle's cycles with each pass's sweeps on all host
+                  cores (at most 16), on the whole reduction when it fits the
+                  time bound, else on its first pass
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -88,6 +91,43 @@ def cpu_baseline(band, w, seconds):
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of the reduction's cycles in sequential order "
                       f"({nbytes / 1e9:.2f} GB algorithmic, {dt:.1f} s, one thread)"}
+
+
+def host_cores() -> int:
+    """Host threads for the threaded CPU chaser: the cores this process may
+    run on, at most 16 (the host share that goes with one GPU).  The chaser
+    caps them further per pass as the page does (2n/(3b), n/256)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_threaded(band, w, seconds):
+    import oracle
+    oracle.build_mt()
+    esize = 8 if w.dtype == "f64" else 4
+    passes = pass_list(w.bw, w.tw)
+    cyc = []
+    for (b, t) in passes:
+        R = np.arange(max(w.n - (b - t) - 1, 0), dtype=np.int64)
+        cyc.append(int(np.sum((w.n - 2 - R - (b - t)) // b + 1)))
+    threads = host_cores()
+    t0 = time.perf_counter()
+    _, _, used = oracle.reduce_mt(band, w.bw, w.tw, threads=-threads, max_passes=1)
+    dt = time.perf_counter() - t0
+    npass = 1
+    if dt * len(passes) < seconds and len(passes) > 1:
+        t0 = time.perf_counter()
+        _, _, used = oracle.reduce_mt(band, w.bw, w.tw, threads=-threads)
+        dt = time.perf_counter() - t0
+        npass = len(passes)
+    nbytes = alg_bytes_prefix(w.n, w.bw, w.tw, esize, sum(cyc[:npass]))
+    what = "the whole reduction" if npass == len(passes) else "its first pass"
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": used, "kind": "oracle-threaded",
+            "sample": f"{what} ({npass} of {len(passes)} passes, {nbytes / 1e9:.2f} GB algorithmic, "
+                      f"{dt:.2f} s, sweeps of a pass on {used} threads)"}
 
 
 def kernel_source_hash() -> str:
@@ -249,6 +289,7 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(band, w, args.cpu_seconds)
+        out["cpu_threaded"] = cpu_threaded(band, w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

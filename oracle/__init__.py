@@ -30,7 +30,41 @@ _LIB_PATH = os.path.join(_HERE, "libbb_oracle.so")
 # them as single instructions (correctly rounded either way).
 _CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-mfma", "-fno-math-errno"]
 
+_MT_SRC = [os.path.join(_HERE, "bb_oracle_mt.c"), os.path.join(_HERE, "bb_oracle_mt_body.h")] + _SRC
+_MT_LIB_PATH = os.path.join(_HERE, "libbb_oracle_mt.so")
+
 _lib = None
+_mt_lib = None
+
+
+def build_mt(force: bool = False) -> str:
+    """Compile the threaded runner (the oracle's cycles on host threads)."""
+    stale = not os.path.exists(_MT_LIB_PATH) or any(
+        os.path.getmtime(s) > os.path.getmtime(_MT_LIB_PATH) for s in _MT_SRC)
+    if force or stale:
+        tmp = _MT_LIB_PATH + ".tmp%d" % os.getpid()
+        flags = [f if f != "-std=c99" else "-std=c11" for f in _CFLAGS]
+        cmd = ["gcc", *flags, "-pthread", "-o", tmp, _MT_SRC[0], "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _MT_LIB_PATH)
+    return _MT_LIB_PATH
+
+
+def mt_lib():
+    global _mt_lib
+    if _mt_lib is None:
+        if not _cpu_has_fma():
+            raise RuntimeError("oracle build uses the FMA instruction; this host CPU lacks it")
+        path = _MT_LIB_PATH if os.path.exists(_MT_LIB_PATH) else build_mt()
+        L = ctypes.CDLL(path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        for suf in ("f64", "f32"):
+            f = getattr(L, "bb_oracle_mt_reduce_" + suf)
+            f.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, i32, ctypes.POINTER(i32)]
+            f.restype = i32
+        L.bb_oracle_mt_default_threads.restype = i32
+        _mt_lib = L
+    return _mt_lib
 
 
 def build(force: bool = False) -> str:
@@ -155,3 +189,30 @@ def band_to_dense(work: np.ndarray, T: int) -> np.ndarray:
             if 0 <= j < n:
                 A[i, j] = work[i, o]
     return A
+
+
+def reduce_mt(band: np.ndarray, bw: int, tw: int, threads: int = 0, compute: str | None = None,
+              return_band: bool = False, max_passes: int = -1):
+    """The oracle's reduction with each pass's sweeps on host threads;
+    bitwise equal to :func:`reduce`.  threads > 0: exactly that many (at most
+    one per sweep); threads < 0: at most -threads, capped per pass at 2n/(3b)
+    and n/256 (page "A two-stage reduction on an Apple M5 Pro", section 6);
+    0: every online core, capped the same way.  max_passes >= 0 stops
+    after that many passes (timing samples).  Returns (d, e, threads_used) or,
+    with return_band, (d, e, working_band, T, threads_used)."""
+    band = np.asarray(band)
+    n = band.shape[0]
+    cdt = _np_dtype(compute) if compute else band.dtype
+    a = np.ascontiguousarray(band, dtype=cdt)
+    d = np.zeros(n, dtype=cdt)
+    e = np.zeros(max(n - 1, 0), dtype=cdt)
+    out = np.zeros((n, working_ld(n, bw, tw)), dtype=cdt) if return_band else None
+    used = ctypes.c_int(0)
+    f = getattr(mt_lib(), "bb_oracle_mt_reduce_" + _suffix(cdt))
+    rc = f(a.ctypes.data, a.shape[1], n, bw, tw, d.ctypes.data, e.ctypes.data if e.size else None,
+           out.ctypes.data if out is not None else None, threads, max_passes, ctypes.byref(used))
+    if rc != 0:
+        raise ValueError("threaded oracle rejected arguments (rc=%d)" % rc)
+    if return_band:
+        return d, e, out, working_T(n, bw, tw), int(used.value)
+    return d, e, int(used.value)
