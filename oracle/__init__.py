@@ -33,8 +33,44 @@ _CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-mfma", 
 _MT_SRC = [os.path.join(_HERE, "bb_oracle_mt.c"), os.path.join(_HERE, "bb_oracle_mt_body.h")] + _SRC
 _MT_LIB_PATH = os.path.join(_HERE, "libbb_oracle_mt.so")
 
+_SV_SRC = [os.path.join(_HERE, "bb_oracle_svals.c"), os.path.join(_HERE, "bb_oracle_svals_body.h")]
+_SV_LIB_PATH = os.path.join(_HERE, "libbb_oracle_svals.so")
+
 _lib = None
 _mt_lib = None
+_sv_lib = None
+
+
+def build_svals(force: bool = False) -> str:
+    """Compile the bisection oracle (bidiagonal -> singular values)."""
+    stale = not os.path.exists(_SV_LIB_PATH) or any(
+        os.path.getmtime(s) > os.path.getmtime(_SV_LIB_PATH) for s in _SV_SRC)
+    if force or stale:
+        tmp = _SV_LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", *_CFLAGS, "-o", tmp, _SV_SRC[0], "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SV_LIB_PATH)
+    return _SV_LIB_PATH
+
+
+def svals_lib():
+    global _sv_lib
+    if _sv_lib is None:
+        path = _SV_LIB_PATH if os.path.exists(_SV_LIB_PATH) else build_svals()
+        L = ctypes.CDLL(path)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        for suf, real in (("f64", ctypes.c_double), ("f32", ctypes.c_float)):
+            f = getattr(L, "bb_oracle_svals_" + suf)
+            f.argtypes = [vp, vp, i64, i64, i64, vp]
+            f.restype = ctypes.c_int
+            g = getattr(L, "bb_oracle_gk_count_" + suf)
+            g.argtypes = [vp, vp, i64, real, real]
+            g.restype = i64
+            h = getattr(L, "bb_oracle_gk_interval_" + suf)
+            h.argtypes = [vp, vp, i64, vp, vp, vp]
+            h.restype = None
+        _sv_lib = L
+    return _sv_lib
 
 
 def build_mt(force: bool = False) -> str:
@@ -216,3 +252,44 @@ def reduce_mt(band: np.ndarray, bw: int, tw: int, threads: int = 0, compute: str
     if return_band:
         return d, e, out, working_T(n, bw, tw), int(used.value)
     return d, e, int(used.value)
+
+
+def _bidiag_args(d, e):
+    d = np.ascontiguousarray(d)
+    if d.dtype not in (np.float32, np.float64):
+        raise ValueError("d must be float32 or float64")
+    e = np.ascontiguousarray(e, dtype=d.dtype)
+    if e.size != max(d.size - 1, 0):
+        raise ValueError("e must have n-1 entries")
+    return d, e
+
+
+def svals(d: np.ndarray, e: np.ndarray, i0: int = 0, i1: int | None = None) -> np.ndarray:
+    """Singular values i0..i1-1 (descending) of the upper bidiagonal (d, e),
+    by bisection on the Golub-Kahan tridiagonal in the precision of d."""
+    d, e = _bidiag_args(d, e)
+    n = d.size
+    i1 = n if i1 is None else i1
+    out = np.zeros(max(i1 - i0, 0), dtype=d.dtype)
+    f = getattr(svals_lib(), "bb_oracle_svals_" + _suffix(d.dtype))
+    rc = f(d.ctypes.data, e.ctypes.data if e.size else None, n, i0, i1, out.ctypes.data)
+    if rc != 0:
+        raise ValueError("bisection oracle rejected arguments (rc=%d)" % rc)
+    return out
+
+
+def gk_interval(d: np.ndarray, e: np.ndarray):
+    """(lo, hi, pivmin) of the Golub-Kahan tridiagonal of (d, e)."""
+    d, e = _bidiag_args(d, e)
+    lo, hi, pm = (np.zeros(1, dtype=d.dtype) for _ in range(3))
+    getattr(svals_lib(), "bb_oracle_gk_interval_" + _suffix(d.dtype))(
+        d.ctypes.data, e.ctypes.data if e.size else None, d.size, lo.ctypes.data, hi.ctypes.data,
+        pm.ctypes.data)
+    return lo[0], hi[0], pm[0]
+
+
+def gk_count(d: np.ndarray, e: np.ndarray, x: float, pivmin: float) -> int:
+    """Sturm count: eigenvalues of the Golub-Kahan tridiagonal <= x."""
+    d, e = _bidiag_args(d, e)
+    f = getattr(svals_lib(), "bb_oracle_gk_count_" + _suffix(d.dtype))
+    return int(f(d.ctypes.data, e.ctypes.data if e.size else None, d.size, x, pivmin))
