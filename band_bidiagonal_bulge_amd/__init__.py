@@ -10,10 +10,12 @@ from __future__ import annotations
 from ._lib import (BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
                    BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
-                   bb_run_pass, bb_status_str, bb_tuning, bb_workspace_bytes, lib)
+                   bb_run_pass, bb_status_str, bb_svals, bb_svals_split, bb_svals_workspace_bytes, bb_tuning,
+                   bb_workspace_bytes, lib)
 
 __all__ = ["reduce", "export_band", "workspace", "tuning", "dtype_code", "bb_plan", "bb_workspace_bytes",
-           "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band", "bb_device_status", "bb_status_str", "BBError", "EXPORTS"]
+           "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band", "bb_device_status", "bb_svals", "bb_svals_workspace_bytes", "bb_svals_split",
+           "bb_status_str", "svals", "BBError", "EXPORTS"]
 
 
 def dtype_code(torch_dtype) -> int:
@@ -67,3 +69,27 @@ def export_band(work, n: int, bw: int, tw: int, torch_dtype, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(work.device)
     bb_export_band(work.data_ptr(), n, bw, tw, dtype_code(torch_dtype), out.data_ptr(), s.cuda_stream)
     return out, info.sub
+
+
+def svals(d, e, i0: int = 0, i1: int | None = None, levels: int = 0, tree_levels: int = 0, work=None,
+          stream=None):
+    """Singular values i0..i1-1 (descending) of the upper bidiagonal given by
+    device tensors d (n) and e (n-1), by bisection on the Golub-Kahan
+    tridiagonal; returns a device tensor of i1-i0 values.  tree_levels and
+    levels split the work (0: chosen for the size, tree_levels -1: no shared
+    tree); they do not change the result."""
+    import torch
+    if not d.is_cuda or d.dim() != 1 or not d.is_contiguous():
+        raise ValueError("d must be a contiguous 1-D device tensor")
+    n = d.shape[0]
+    if e.dtype != d.dtype or e.numel() != max(n - 1, 0) or (n > 1 and (not e.is_cuda or not e.is_contiguous())):
+        raise ValueError("e must be a contiguous device tensor of n-1 entries of d's dtype")
+    dt = dtype_code(d.dtype)
+    i1 = n if i1 is None else i1
+    out = torch.empty(max(i1 - i0, 0), dtype=d.dtype, device=d.device)
+    if work is None:
+        work = torch.empty(bb_svals_workspace_bytes(n, dt), dtype=torch.uint8, device=d.device)
+    s = stream if stream is not None else torch.cuda.current_stream(d.device)
+    bb_svals(d.data_ptr(), e.data_ptr() if n > 1 else 0, n, dt, i0, i1, tree_levels, levels,
+             out.data_ptr() if out.numel() else 0, work.data_ptr(), work.numel(), s.cuda_stream)
+    return out

@@ -210,9 +210,91 @@ bb_status run_pass(void *work, const bb::Geometry &g, const bb::Pass &p, const b
   return run_persistent_pass(work, g, p, tu, sync, st);
 }
 
+// Bisection of the Golub-Kahan tridiagonal: sizes, and how it is split.
+constexpr int64_t kMaxSvalsN = int64_t(1) << 29;  // 2n pivots indexed in 32 bits
+
+size_t svals_bytes(int64_t n, int32_t dtype) {
+  const size_t es = dtype == BB_F64 ? 8 : 4;
+  return size_t(bb::kSvalsHeaderBytes) + size_t(bb::kSvalsTreeBytes) + size_t(bb::svals_padded_entries(n)) * es;
+}
+
+// Every count is a chain of 2n dependent pivots, and one wave per SIMD keeps
+// the SIMD busy, so time ~ sum over launches of rounds * max(1, waves/SIMDs).
+// K shared tree levels cost one round of 2^K - 1 lanes; then D levels per
+// round cost a round each, with 2^D lanes per value (one for D = 1).  The
+// cheapest (K, D) wins; ties go to less work (smaller K, then smaller D).
+struct SvalsSplit {
+  int32_t tree, levels;
+};
+
+double split_cost(int F, double simds, int64_t values, int K, int D) {
+  double cost = 0;
+  if (K > 0) cost += std::max(1.0, double(((int64_t(1) << K) - 1 + 63) / 64) / simds);
+  if (F > K) {
+    const int64_t lanes = values * (D == 1 ? 1 : (int64_t(1) << D));
+    cost += double((F - K + D - 1) / D) * std::max(1.0, double((lanes + 63) / 64) / simds);
+  }
+  return cost;
+}
+
+SvalsSplit pick_split(int32_t dtype, int64_t values, int32_t tree, int32_t levels) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const double simds = 4.0 * cus;
+  const int F = bb::bisect_halvings(dtype == BB_F64 ? 1 : 0);
+  SvalsSplit best{0, 1};
+  double best_cost = -1;
+  for (int32_t K = 0; K <= bb::kSvalsMaxTree; ++K) {
+    if ((tree > 0 && K != tree) || (tree < 0 && K != 0)) continue;
+    for (int32_t D = 1; D <= 6; ++D) {
+      if (levels > 0 && D != levels) continue;
+      const double c = split_cost(F, simds, values, K, D);
+      if (best_cost < 0 || c < best_cost - 1e-9) {
+        best = {K, D};
+        best_cost = c;
+      }
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 extern "C" {
+
+bb_status bb_svals_workspace_bytes(int64_t n, int32_t dtype, size_t *bytes) {
+  if (!bytes || (dtype != BB_F32 && dtype != BB_F64) || n < 0 || n > kMaxSvalsN) return BB_ERR_ARG;
+  *bytes = svals_bytes(n, dtype);
+  return BB_OK;
+}
+
+bb_status bb_svals(const void *d, const void *e, int64_t n, int32_t dtype, int64_t i0, int64_t i1,
+                   int32_t tree_levels, int32_t levels, void *sigma, void *work, size_t work_bytes, void *stream) {
+  if ((dtype != BB_F32 && dtype != BB_F64) || n < 0 || n > kMaxSvalsN) return BB_ERR_ARG;
+  if (i0 < 0 || i1 < i0 || i1 > n || levels < 0 || levels > 6) return BB_ERR_ARG;
+  if (tree_levels < -1 || tree_levels > bb::kSvalsMaxTree) return BB_ERR_ARG;
+  if (n == 0 || i1 == i0) return BB_OK;
+  const size_t es = dtype == BB_F64 ? 8 : 4;
+  if (!d || (n > 1 && !e) || !sigma || !work) return BB_ERR_ARG;
+  if (!aligned(d, es) || (n > 1 && !aligned(e, es)) || !aligned(sigma, es) || !aligned(work, 256))
+    return BB_ERR_ARG;
+  if (work_bytes < svals_bytes(n, dtype)) return BB_ERR_WORKSPACE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int code = dtype == BB_F64 ? 1 : 0;
+  const SvalsSplit sp = pick_split(dtype, i1 - i0, tree_levels, levels);
+  if (bb::launch_gk_prep(code, d, n > 1 ? e : nullptr, n, work, st) != hipSuccess) return BB_ERR_HIP;
+  return hip_status(bb::launch_svals(code, sp.tree, sp.levels, work, n, i0, i1, sigma, st));
+}
+
+bb_status bb_svals_split(int64_t values, int32_t dtype, int32_t *tree_levels, int32_t *levels) {
+  if (!tree_levels || !levels || (dtype != BB_F32 && dtype != BB_F64) || values < 0) return BB_ERR_ARG;
+  const SvalsSplit sp = pick_split(dtype, values, 0, 0);
+  *tree_levels = sp.tree;
+  *levels = sp.levels;
+  return BB_OK;
+}
 
 bb_status bb_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, bb_plan_info *out) {
   if (!out || !valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;

@@ -35,4 +35,22 @@ hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, 
 // tile maxm.
 size_t stage_lds_bytes(int dtype, int maxm, int b, int t);
 
+// Singular values of the bidiagonal by bisection (bb_svals.hip).  The
+// workspace holds a header {lo, hi, pivmin} in its first kSvalsHeaderBytes,
+// the counts of the shared top of the bisection tree (int32, heap order, up
+// to kSvalsMaxTree levels) in the next kSvalsTreeBytes, then
+// svals_padded_entries(n) squared off-diagonal entries.
+constexpr int kSvalsHeaderBytes = 256;
+constexpr int kSvalsMaxTree = 16;
+constexpr int kSvalsTreeBytes = 4 << kSvalsMaxTree;
+constexpr int kPrepThreads = 1024;
+constexpr int kBisectThreads = 256;
+int64_t svals_padded_entries(int64_t n);
+int bisect_halvings(int dtype);
+hipError_t launch_gk_prep(int dtype, const void *d, const void *e, int64_t n, void *work, hipStream_t st);
+// tree_levels = K shared levels counted once (0: none, <= kSvalsMaxTree);
+// levels = D levels resolved per round afterwards (1..6).
+hipError_t launch_svals(int dtype, int tree_levels, int levels, void *work, int64_t n, int64_t i0, int64_t i1,
+                        void *sigma, hipStream_t st);
+
 }  // namespace bb

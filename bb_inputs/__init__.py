@@ -16,6 +16,10 @@ Recipe (every workload is synthetic; the pages name no public dataset):
     their band entries set to +0.0 (exercises zero reflectors);
   * cast once to the workload's dtype.  Both the oracle and the GPU consume
     the same cast array.
+
+Bidiagonals for the singular-value step (make_bidiag): d (n) then e (n-1)
+drawn from one default_rng(seed) stream, N(0,1) ('normal'), the same times
+10**(-6 i / n) for entry i ('graded'), or all ones ('ones'); cast once.
 """
 from __future__ import annotations
 
@@ -75,6 +79,21 @@ def make_band(n: int, bw: int, dtype: str = "f64", dist: str = "normal", seed: i
         rows = rng.choice(n, nz, replace=False)
         a[rows, :] = 0.0
     return np.ascontiguousarray(a.astype(np_dtype(dtype)))
+
+
+def make_bidiag(n: int, dtype: str = "f64", dist: str = "normal", seed: int = 0):
+    """Seeded upper bidiagonal (d, e) for the singular-value step."""
+    rng = np.random.default_rng(seed)
+    if dist == "ones":
+        d, e = np.ones(n), np.ones(max(n - 1, 0))
+    elif dist in ("normal", "graded"):
+        d, e = rng.standard_normal(n), rng.standard_normal(max(n - 1, 0))
+        if dist == "graded":
+            d *= 10.0 ** (-6.0 * np.arange(n) / max(n, 1))
+            e *= 10.0 ** (-6.0 * np.arange(e.size) / max(n, 1))
+    else:
+        raise ValueError("unknown distribution %r" % dist)
+    return d.astype(np_dtype(dtype)), e.astype(np_dtype(dtype))
 
 
 def make_workload(w: Workload | str) -> np.ndarray:

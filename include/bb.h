@@ -154,6 +154,44 @@ bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, in
  * BB_ERR_HIP. */
 bb_status bb_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream);
 
+/* ---- Singular values of the bidiagonal (the step after the reduction) ----
+ *
+ * Defined by the page "A two-stage reduction on an Apple M5 Pro", section 7:
+ * the singular values of the upper bidiagonal B (diagonal d, superdiagonal e)
+ * are the non-negative eigenvalues of the 2n x 2n Golub-Kahan tridiagonal
+ * (zero diagonal, off-diagonal d_0, e_0, d_1, ..., d_{n-1}); each is found by
+ * bisection from its Gershgorin interval with a fixed number of halvings
+ * (26 in fp32, 55 in fp64), each a Sturm count with LAPACK's pivmin guard.
+ * The result is absolutely accurate: within a few ulps of max sigma.  It is
+ * the same to the bit for every `levels`, and deterministic.
+ */
+
+/* Device workspace bytes for bb_svals on an order-n bidiagonal.
+ * Errors: BB_ERR_ARG (n < 0, n > 2^29, bad dtype, bytes NULL). */
+bb_status bb_svals_workspace_bytes(int64_t n, int32_t dtype, size_t *bytes);
+
+/* Singular values i0 .. i1-1 of B in descending order (sigma_0 is the
+ * largest), 0 <= i0 <= i1 <= n, written to sigma[0 .. i1-i0-1].
+ *   d      device, n elements of dtype; e device, n-1 elements (unused, may
+ *          be NULL, when n == 1).  Signs of d and e do not matter.
+ *   tree_levels  the first K halvings, shared by every value, are counted
+ *          once for all 2^K - 1 nodes of the top of the bisection tree
+ *          (1 .. 16); -1 = none, 0 = chosen for the size.
+ *   levels then D halvings per round, a group of 2^D lanes per value
+ *          (1 .. 6); 0 = chosen for the size.
+ *          Only the speed depends on K and D: the values are the same bits.
+ *   work   device workspace of work_bytes >= bb_svals_workspace_bytes(),
+ *          256-byte aligned, owned by the caller, overwritten.
+ * Enqueues up to three kernels on `stream`; nothing when n == 0 or i0 == i1.
+ * Errors: BB_ERR_ARG (sizes, range, NULL or misaligned pointers, K, D),
+ * BB_ERR_WORKSPACE, BB_ERR_HIP. */
+bb_status bb_svals(const void *d, const void *e, int64_t n, int32_t dtype, int64_t i0, int64_t i1,
+                   int32_t tree_levels, int32_t levels, void *sigma, void *work, size_t work_bytes, void *stream);
+
+/* The (tree_levels, levels) bb_svals picks for `values` singular values on
+ * the current device.  Errors: BB_ERR_ARG. */
+bb_status bb_svals_split(int64_t values, int32_t dtype, int32_t *tree_levels, int32_t *levels);
+
 /* Static description of a status code. */
 const char *bb_status_str(int32_t status);
 

@@ -138,3 +138,38 @@ def test_staged_entry_points_validate_on_host():
     assert L.bb_extract(fake, big, 10, 4, 2, 0, None, fake, None) == _lib.BB_ERR_ARG
     assert L.bb_extract(fake, big, 10, 4, 2, 0, fake, None, None) == _lib.BB_ERR_ARG
     assert L.bb_extract(fake, big, 10, 4, 2, 1, ctypes.c_void_p((1 << 20) + 4), fake, None) == _lib.BB_ERR_ARG
+
+
+def test_svals_validation_without_a_gpu():
+    # argument errors are reported before anything touches a device
+    import ctypes
+    L = bbm.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    big = 1 << 24
+    cases = [
+        ((fake, fake, -1, 0, 0, 0, 0, 0, fake, fake, big, None), 1),
+        ((fake, fake, 8, 2, 0, 1, 0, 0, fake, fake, big, None), 1),     # bad dtype
+        ((fake, fake, 8, 0, 0, 9, 0, 0, fake, fake, big, None), 1),     # i1 > n
+        ((fake, fake, 8, 0, 3, 2, 0, 0, fake, fake, big, None), 1),     # i1 < i0
+        ((fake, fake, 8, 0, 0, 8, 0, 7, fake, fake, big, None), 1),     # levels
+        ((fake, fake, 8, 0, 0, 8, 17, 0, fake, fake, big, None), 1),    # tree levels
+        ((fake, fake, 8, 0, 0, 8, -2, 0, fake, fake, big, None), 1),    # tree levels
+        ((None, fake, 8, 0, 0, 8, 0, 0, fake, fake, big, None), 1),     # d NULL
+        ((fake, fake, 8, 0, 0, 8, 0, 0, fake, fake, 16, None), 2),      # workspace
+        ((fake, fake, 1 << 30, 0, 0, 1, 0, 0, fake, fake, 1 << 40, None), 1),  # n too large
+        ((None, None, 0, 0, 0, 0, 0, 0, None, None, 0, None), 0),       # nothing to do
+        ((None, None, 8, 0, 4, 4, 0, 0, None, None, 0, None), 0),       # empty range
+    ]
+    for args, want in cases:
+        assert L.bb_svals(*args) == want, args
+    assert bbm.bb_svals_workspace_bytes(16384, 0) == 256 + (4 << 16) + (32768 + 64) * 4
+    assert bbm.bb_svals_workspace_bytes(1, 1) == 256 + (4 << 16) + 128 * 8
+    with pytest.raises(bbm.BBError):
+        bbm.bb_svals_workspace_bytes(-1, 0)
+    # split for the size (256 CUs when no device answers): the 16 shared tree
+    # levels fill 1024 SIMDs in one round; then 2 levels per round with 4 lanes
+    # per value fill them again at 16384 values
+    assert bbm.bb_svals_split(16384, 0) == (16, 2)
+    # one value: the deepest rounds, and the smallest tree that reaches the
+    # same round count (55 halvings = 13 tree levels + 7 rounds of 6)
+    assert bbm.bb_svals_split(1, 1) == (13, 6)
