@@ -12,6 +12,10 @@ Prints one JSON line:
                   kernels run on), against the published HBM3E peak
   cpu_baseline    the CPU oracle (one thread) timed on a bounded prefix of the
                   same reduction, in the same unit
+  svals           the step after the path: singular values of the workload's
+                  bidiagonal by bisection on the GPU (bb_svals), its ALU
+                  roofline in Sturm pivots per second, and the bisection
+                  oracle timed on a sample of the values
   cpu_threaded    the oracle's cycles with each pass's sweeps on all host
                   cores (at most 16), on the whole reduction when it fits the
                   time bound, else on its first pass
@@ -93,6 +97,63 @@ def cpu_baseline(band, w, seconds):
                       f"({nbytes / 1e9:.2f} GB algorithmic, {dt:.1f} s, one thread)"}
 
 
+# Pivots of one Sturm count step, VALU instructions in the issued code without
+# the operand broadcast: the correctly rounded division (10 fp32 / 11 fp64),
+# the shift subtraction, the pivmin guard (compare, select: 2 / 3) and the
+# count (compare, add).  Peak = the chip's vector FMA lane rate for the dtype
+# (fp32 157.3 TFLOP/s, fp64 78.6 TFLOP/s, two flops per FMA) over that count.
+PIVOT_OPS = {"f32": 15, "f64": 17}
+LANE_OPS_PER_S = {"f32": 157.3e12 / 2, "f64": 78.6e12 / 2}
+
+
+def measure_svals(bbm, torch, d, e, w, steps, stream, cpu_seconds, with_cpu):
+    dev = d.device
+    dt = bbm.dtype_code(d.dtype)
+    n = w.n
+    halvings = 26 if w.dtype == "f32" else 55
+    work = torch.empty(bbm.bb_svals_workspace_bytes(n, dt), dtype=torch.uint8, device=dev)
+    sig = torch.empty(n, dtype=d.dtype, device=dev)
+    tree, levels = bbm.bb_svals_split(n, dt)
+    sp = stream.cuda_stream
+
+    def run():
+        bbm.bb_svals(d.data_ptr(), e.data_ptr(), n, dt, 0, n, 0, 0, sig.data_ptr(), work.data_ptr(), work.numel(),
+                     sp)
+
+    run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+    # the method's work: every value bisected on its own, `halvings` counts
+    # of 2n pivots each
+    pivots = float(n) * halvings * 2 * n
+    rate = pivots / (ms * 1e-3) / 1e9
+    peak = LANE_OPS_PER_S[w.dtype] / PIVOT_OPS[w.dtype] / 1e9
+    out = {"kernel": "k_gk_prep + k_tree + k_bisect", "ms": round(ms, 4), "values": n,
+           "split": {"tree_levels": tree, "levels": levels}, "halvings": halvings,
+           "roofline": {"bound": "alu", "achieved": round(rate, 2), "peak": round(peak, 1), "unit": "Gpivot/s",
+                        "frac": round(rate / peak, 4)}}
+    if with_cpu:
+        import oracle
+        oracle.build_svals()
+        dh, eh = d.cpu().numpy(), e.cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.svals(dh, eh, 0, 8)
+        per_value = (time.perf_counter() - t0) / 8
+        m = int(max(8, min(n, cpu_seconds / max(per_value, 1e-9))))
+        t0 = time.perf_counter()
+        oracle.svals(dh, eh, 0, m)
+        dtc = time.perf_counter() - t0
+        out["cpu_oracle"] = {"value": round(m * halvings * 2.0 * n / dtc / 1e9, 4), "unit": "Gpivot/s", "cores": 1,
+                             "kind": "oracle", "sample": f"the {m} largest of {n} values ({dtc:.1f} s, one thread)"}
+    return out
+
+
 def host_cores() -> int:
     """Host threads for the threaded CPU chaser: the cores this process may
     run on, at most 16 (the host share that goes with one GPU).  The chaser
@@ -131,11 +192,15 @@ def cpu_threaded(band, w, seconds):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: stored counter readings are only valid for it."""
+    """Hash of the sources of the reduction's kernels and their launch set-up
+    (every HIP source but the singular-value step's): stored counter readings
+    are only valid for it."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "band_bidiagonal_bulge_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f.startswith("bb_svals"):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -182,6 +247,7 @@ def main():
     ap.add_argument("--workload", default=bb_inputs.HEADLINE)
     ap.add_argument("--scheduler", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-svals", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
@@ -287,6 +353,8 @@ def main():
                     "GBps": round(ab / (statistics.median(pass_ms[i]) * 1e-3) / 1e9, 2)}
                    for i, (b, t, ab) in enumerate(passes)],
     }
+    if not args.no_svals:
+        out["svals"] = measure_svals(bbm, torch, d, e, w, args.steps, stream, args.cpu_seconds / 3, not args.no_cpu)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(band, w, args.cpu_seconds)
         out["cpu_threaded"] = cpu_threaded(band, w, args.cpu_seconds)
