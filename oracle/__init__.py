@@ -36,9 +36,46 @@ _MT_LIB_PATH = os.path.join(_HERE, "libbb_oracle_mt.so")
 _SV_SRC = [os.path.join(_HERE, "bb_oracle_svals.c"), os.path.join(_HERE, "bb_oracle_svals_body.h")]
 _SV_LIB_PATH = os.path.join(_HERE, "libbb_oracle_svals.so")
 
+_SYM_SRC = [os.path.join(_HERE, "bb_oracle_sym.c"), os.path.join(_HERE, "bb_oracle_sym_body.h")]
+_SYM_LIB_PATH = os.path.join(_HERE, "libbb_oracle_sym.so")
+
 _lib = None
 _mt_lib = None
 _sv_lib = None
+_sym_lib = None
+
+
+def build_sym(force: bool = False) -> str:
+    """Compile the symmetric band -> tridiagonal oracle."""
+    stale = not os.path.exists(_SYM_LIB_PATH) or any(
+        os.path.getmtime(s) > os.path.getmtime(_SYM_LIB_PATH) for s in _SYM_SRC)
+    if force or stale:
+        tmp = _SYM_LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", *_CFLAGS, "-o", tmp, _SYM_SRC[0], "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SYM_LIB_PATH)
+    return _SYM_LIB_PATH
+
+
+def sym_lib():
+    global _sym_lib
+    if _sym_lib is None:
+        if not _cpu_has_fma():
+            raise RuntimeError("oracle build uses the FMA instruction; this host CPU lacks it")
+        path = _SYM_LIB_PATH if os.path.exists(_SYM_LIB_PATH) else build_sym()
+        L = ctypes.CDLL(path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        for suf in ("f64", "f32"):
+            f = getattr(L, "bb_oracle_sym_reduce_" + suf)
+            f.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp]
+            f.restype = i32
+            g = getattr(L, "bb_oracle_sym_run_cycles_" + suf)
+            g.argtypes = [vp, i64, i64, i32, i32, vp, i64, vp]
+            g.restype = i32
+        L.bb_oracle_sym_ld.argtypes = [i64, i32, i32]
+        L.bb_oracle_sym_ld.restype = i64
+        _sym_lib = L
+    return _sym_lib
 
 
 def build_svals(force: bool = False) -> str:
@@ -293,3 +330,41 @@ def gk_count(d: np.ndarray, e: np.ndarray, x: float, pivmin: float) -> int:
     d, e = _bidiag_args(d, e)
     f = getattr(svals_lib(), "bb_oracle_gk_count_" + _suffix(d.dtype))
     return int(f(d.ctypes.data, e.ctypes.data if e.size else None, d.size, x, pivmin))
+
+
+def sym_working_ld(n: int, bw: int, tw: int) -> int:
+    """Stored superdiagonals of the symmetric working band (BW + T + 1)."""
+    return int(sym_lib().bb_oracle_sym_ld(n, bw, tw))
+
+
+def sym_reduce(band: np.ndarray, bw: int, tw: int, compute: str | None = None, return_band: bool = False):
+    """Symmetric band -> tridiagonal.  band: (n, >= bw+1), row i holds
+    A(i, i..i+bw) = A(i..i+bw, i).  Returns (d, e) or (d, e, working_band)."""
+    band = np.asarray(band)
+    n = band.shape[0]
+    cdt = _np_dtype(compute) if compute else band.dtype
+    a = np.ascontiguousarray(band, dtype=cdt)
+    d = np.zeros(n, dtype=cdt)
+    e = np.zeros(max(n - 1, 0), dtype=cdt)
+    out = np.zeros((n, sym_working_ld(n, bw, tw)), dtype=cdt) if return_band else None
+    f = getattr(sym_lib(), "bb_oracle_sym_reduce_" + _suffix(cdt))
+    rc = f(a.ctypes.data, a.shape[1], n, bw, tw, d.ctypes.data, e.ctypes.data if e.size else None,
+           out.ctypes.data if out is not None else None)
+    if rc != 0:
+        raise ValueError("symmetric oracle rejected arguments (rc=%d)" % rc)
+    return (d, e, out) if return_band else (d, e)
+
+
+def sym_run_cycles(band: np.ndarray, bw: int, tw: int, order, compute: str | None = None):
+    """Runs the given (pass, R, k) cycles in order; returns the working band."""
+    band = np.asarray(band)
+    n = band.shape[0]
+    cdt = _np_dtype(compute) if compute else band.dtype
+    a = np.ascontiguousarray(band, dtype=cdt)
+    o = np.ascontiguousarray(np.asarray(order, dtype=np.int32).reshape(-1, 3))
+    out = np.zeros((n, sym_working_ld(n, bw, tw)), dtype=cdt)
+    f = getattr(sym_lib(), "bb_oracle_sym_run_cycles_" + _suffix(cdt))
+    rc = f(a.ctypes.data, a.shape[1], n, bw, tw, o.ctypes.data, o.shape[0], out.ctypes.data)
+    if rc != 0:
+        raise ValueError("symmetric oracle rejected the cycle list (rc=%d)" % rc)
+    return out
