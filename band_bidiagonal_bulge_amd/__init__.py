@@ -10,12 +10,14 @@ from __future__ import annotations
 from ._lib import (BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
                    BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
-                   bb_run_pass, bb_status_str, bb_svals, bb_svals_split, bb_svals_workspace_bytes, bb_tuning,
+                   bb_run_pass, bb_status_str, bb_svals, bb_svals_split, bb_svals_workspace_bytes, bb_sym_device_status,
+                   bb_sym_export_band, bb_sym_reduce, bb_sym_workspace_bytes, bb_tuning,
                    bb_workspace_bytes, lib)
 
 __all__ = ["reduce", "export_band", "workspace", "tuning", "dtype_code", "bb_plan", "bb_workspace_bytes",
            "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band", "bb_device_status", "bb_svals", "bb_svals_workspace_bytes", "bb_svals_split",
-           "bb_status_str", "svals", "BBError", "EXPORTS"]
+           "bb_sym_workspace_bytes", "bb_sym_reduce", "bb_sym_export_band", "bb_sym_device_status",
+           "bb_status_str", "svals", "sym_reduce", "sym_workspace", "BBError", "EXPORTS"]
 
 
 def dtype_code(torch_dtype) -> int:
@@ -93,3 +95,27 @@ def svals(d, e, i0: int = 0, i1: int | None = None, levels: int = 0, tree_levels
     bb_svals(d.data_ptr(), e.data_ptr() if n > 1 else 0, n, dt, i0, i1, tree_levels, levels,
              out.data_ptr() if out.numel() else 0, work.data_ptr(), work.numel(), s.cuda_stream)
     return out
+
+
+def sym_workspace(n: int, bw: int, tw: int, torch_dtype, device="cuda"):
+    """Device workspace for bb_sym_reduce as a uint8 tensor."""
+    import torch
+    return torch.empty(bb_sym_workspace_bytes(n, bw, tw, dtype_code(torch_dtype)), dtype=torch.uint8, device=device)
+
+
+def sym_reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, stream=None):
+    """Symmetric band -> tridiagonal of a device band (n, >= bw+1), row i
+    holding A(i, i..i+bw); returns (d, e) device tensors."""
+    import torch
+    if not band.is_cuda or band.dim() != 2 or band.stride(1) != 1:
+        raise ValueError("band must be a 2-D device tensor with unit column stride")
+    n = band.shape[0]
+    dt = dtype_code(band.dtype)
+    if work is None:
+        work = sym_workspace(n, bw, tw, band.dtype, band.device)
+    d = torch.empty(n, dtype=band.dtype, device=band.device)
+    e = torch.empty(max(n - 1, 0), dtype=band.dtype, device=band.device)
+    s = stream if stream is not None else torch.cuda.current_stream(band.device)
+    bb_sym_reduce(band.data_ptr(), band.stride(0), n, bw, tw, dt, d.data_ptr(), e.data_ptr() if n > 1 else 0,
+                  work.data_ptr(), work.numel(), tun, s.cuda_stream)
+    return d, e

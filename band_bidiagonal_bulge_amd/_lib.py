@@ -18,7 +18,8 @@ BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT, BB_SCHED_GROUP = 0, 1, 2, 
 
 # Every symbol include/bb.h declares.
 EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band",
-           "bb_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split", "bb_status_str")
+           "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce", "bb_sym_export_band",
+           "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split", "bb_status_str")
 
 
 class bb_tuning(ctypes.Structure):
@@ -57,13 +58,18 @@ def lib():
         L.bb_extract.argtypes = [vp, sz, i64, i32, i32, i32, vp, vp, vp]
         L.bb_export_band.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         L.bb_device_status.argtypes = [vp, i64, i32, i32, i32, vp]
+        L.bb_sym_workspace_bytes.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
+        L.bb_sym_reduce.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, sz, ctypes.POINTER(bb_tuning), vp]
+        L.bb_sym_export_band.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+        L.bb_sym_device_status.argtypes = [vp, i64, i32, i32, i32, vp]
         L.bb_svals_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.bb_svals.argtypes = [vp, vp, i64, i32, i64, i64, i32, i32, vp, vp, sz, vp]
         L.bb_svals_split.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.bb_status_str.argtypes = [i32]
         L.bb_status_str.restype = ctypes.c_char_p
         for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract",
-                  "bb_export_band", "bb_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split"):
+                  "bb_export_band", "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce",
+                  "bb_sym_export_band", "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -127,6 +133,32 @@ def bb_export_band(work_ptr: int, n: int, bw: int, tw: int, dtype: int, dst_ptr:
 
 def bb_device_status(work_ptr: int, n: int, bw: int, tw: int, dtype: int, stream: int) -> int:
     return int(lib().bb_device_status(work_ptr, n, bw, tw, dtype, stream or None))
+
+
+def bb_sym_workspace_bytes(n: int, bw: int, tw: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().bb_sym_workspace_bytes(n, bw, tw, dtype, ctypes.byref(out))
+    if rc != BB_OK:
+        raise BBError(rc, "bb_sym_workspace_bytes")
+    return int(out.value)
+
+
+def bb_sym_reduce(band_ptr: int, ld_band: int, n: int, bw: int, tw: int, dtype: int, d_ptr: int, e_ptr: int,
+                  work_ptr: int, work_bytes: int, tuning: bb_tuning | None, stream: int) -> None:
+    rc = lib().bb_sym_reduce(band_ptr, ld_band, n, bw, tw, dtype, d_ptr, e_ptr or None, work_ptr, work_bytes,
+                             ctypes.byref(tuning) if tuning is not None else None, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_sym_reduce")
+
+
+def bb_sym_export_band(work_ptr: int, n: int, bw: int, tw: int, dtype: int, dst_ptr: int, stream: int) -> None:
+    rc = lib().bb_sym_export_band(work_ptr, n, bw, tw, dtype, dst_ptr, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_sym_export_band")
+
+
+def bb_sym_device_status(work_ptr: int, n: int, bw: int, tw: int, dtype: int, stream: int) -> int:
+    return int(lib().bb_sym_device_status(work_ptr, n, bw, tw, dtype, stream or None))
 
 
 def bb_svals_workspace_bytes(n: int, dtype: int) -> int:

@@ -210,6 +210,44 @@ bb_status run_pass(void *work, const bb::Geometry &g, const bb::Pass &p, const b
   return run_persistent_pass(work, g, p, tu, sync, st);
 }
 
+// Symmetric band -> tridiagonal: validation and the passes.
+bool sym_supported(const bb::SymGeometry &g) {
+  if (g.maxt > kMaxTile) return false;
+  return uint64_t(g.n) * uint64_t(g.stride) * uint64_t(g.esize) < (uint64_t(1) << 31);
+}
+
+bb_status check_sym_work(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const void *work, size_t work_bytes,
+                         bb::SymGeometry *g) {
+  if (!valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  *g = bb::make_sym_geometry(n, bw, tw, dtype);
+  if (!sym_supported(*g)) return BB_ERR_UNSUPPORTED;
+  if (!work || !aligned(work, 256)) return BB_ERR_ARG;
+  if (work_bytes < g->total_bytes) return BB_ERR_WORKSPACE;
+  return BB_OK;
+}
+
+int sym_maxm(int32_t t) {
+  if (t + 1 <= 9) return 9;
+  if (t + 1 <= 17) return 17;
+  if (t + 1 <= 33) return 33;
+  return 65;
+}
+
+bb_status run_sym_pass(void *work, const bb::SymGeometry &g, const bb::Pass &p, const bb_tuning &tu,
+                       hipStream_t st) {
+  uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
+  const int64_t ns = bb::sweeps_of(g.n, p);
+  if (ns == 0) return BB_OK;
+  if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
+      bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
+    return BB_ERR_HIP;
+  const int nt = tu.threads_per_block ? tu.threads_per_block : 256;
+  int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(device_cus());
+  grid = std::min<int64_t>(grid, ns);
+  const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+  return hip_status(bb::launch_sym_persist(sym_maxm(p.t), work, g, p.b, p.t, ns, sync, int(grid), nt, spin, st));
+}
+
 // Bisection of the Golub-Kahan tridiagonal: sizes, and how it is split.
 constexpr int64_t kMaxSvalsN = int64_t(1) << 29;  // 2n pivots indexed in 32 bits
 
@@ -263,6 +301,55 @@ SvalsSplit pick_split(int32_t dtype, int64_t values, int32_t tree, int32_t level
 }  // namespace
 
 extern "C" {
+
+bb_status bb_sym_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes) {
+  if (!bytes || !valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  const bb::SymGeometry g = bb::make_sym_geometry(n, bw, tw, dtype);
+  if (!sym_supported(g)) return BB_ERR_UNSUPPORTED;
+  *bytes = g.total_bytes;
+  return BB_OK;
+}
+
+bb_status bb_sym_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
+                        void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream) {
+  bb::SymGeometry g;
+  bb_status rc = check_sym_work(n, bw, tw, dtype, work, work_bytes, &g);
+  if (rc != BB_OK && rc != BB_ERR_WORKSPACE) return rc;
+  if (!band || !d || (n > 1 && !e) || ld_band < int64_t(bw) + 1) return BB_ERR_ARG;
+  if (!aligned(band, g.esize) || !aligned(d, g.esize) || (n > 1 && !aligned(e, g.esize))) return BB_ERR_ARG;
+  if (rc != BB_OK) return rc;
+  bb_tuning tu;
+  if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
+  if (tu.scheduler != BB_SCHED_DEFAULT && tu.scheduler != BB_SCHED_PERSISTENT) return BB_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
+  if (bb::launch_sym_pack(band, ld_band, work, g, st) != hipSuccess ||
+      bb::launch_fill_u32(sync, int64_t(g.sync_words), 0u, st) != hipSuccess)
+    return BB_ERR_HIP;
+  for (const bb::Pass &p : bb::pass_list(bw, tw))
+    if ((rc = run_sym_pass(work, g, p, tu, st)) != BB_OK) return rc;
+  return hip_status(bb::launch_sym_extract(work, g, d, n > 1 ? e : nullptr, st));
+}
+
+bb_status bb_sym_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,
+                             void *stream) {
+  if (!valid_shape(n, bw, tw, dtype) || !work || !dst) return BB_ERR_ARG;
+  const bb::SymGeometry g = bb::make_sym_geometry(n, bw, tw, dtype);
+  const size_t row = size_t(g.ld) * size_t(g.esize);
+  return hip_status(hipMemcpy2DAsync(dst, row, work, size_t(g.stride) * size_t(g.esize), row, size_t(n),
+                                     hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+}
+
+bb_status bb_sym_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream) {
+  if (!valid_shape(n, bw, tw, dtype) || !work) return BB_ERR_ARG;
+  const bb::SymGeometry g = bb::make_sym_geometry(n, bw, tw, dtype);
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return BB_ERR_HIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, static_cast<const char *>(work) + g.sync_offset, sizeof(word), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return BB_ERR_HIP;
+  return word == 0 ? BB_OK : BB_ERR_TIMEOUT;
+}
 
 bb_status bb_svals_workspace_bytes(int64_t n, int32_t dtype, size_t *bytes) {
   if (!bytes || (dtype != BB_F32 && dtype != BB_F64) || n < 0 || n > kMaxSvalsN) return BB_ERR_ARG;

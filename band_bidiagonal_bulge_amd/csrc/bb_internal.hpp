@@ -35,6 +35,15 @@ hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, 
 // tile maxm.
 size_t stage_lds_bytes(int dtype, int maxm, int b, int t);
 
+// Symmetric band -> tridiagonal (bb_sym.hip).  pack: user upper rows into the
+// working band (fill region zeroed); persist: one pass, `grid` workgroups of
+// nt threads claiming sweeps in order, sync as for launch_persist; extract:
+// d = diagonal, e = first superdiagonal.
+hipError_t launch_sym_pack(const void *band, int64_t ld_band, void *wband, const SymGeometry &g, hipStream_t st);
+hipError_t launch_sym_persist(int maxm, void *wband, const SymGeometry &g, int b, int t, int64_t nsweeps,
+                              uint32_t *sync, int grid, int nt, int64_t spin_limit, hipStream_t st);
+hipError_t launch_sym_extract(const void *wband, const SymGeometry &g, void *d, void *e, hipStream_t st);
+
 // Singular values of the bidiagonal by bisection (bb_svals.hip).  The
 // workspace holds a header {lo, hi, pivmin} in its first kSvalsHeaderBytes,
 // the counts of the shared top of the bisection tree (int32, heap order, up

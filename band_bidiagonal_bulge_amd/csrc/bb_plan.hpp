@@ -175,4 +175,40 @@ inline int64_t group_ring_rows(int64_t n, const Pass &p, int G) {
   return need;
 }
 
+// Symmetric band -> tridiagonal: the upper triangle of the band with room
+// for the fill, which reaches bw + T superdiagonals (T = t of the first
+// pass).  Element (i, j), 0 <= j-i <= W = bw + T, at band[i*stride + j-i];
+// stride = W+1 padded to 16 bytes.  Counters follow as for the general band.
+struct SymGeometry {
+  int64_t n = 0;
+  int32_t bw = 0, tw = 0, dtype = 0, esize = 0;
+  int32_t maxt = 0, W = 0, ld = 0, stride = 0;
+  size_t band_bytes = 0, sync_offset = 0, sync_words = 0, total_bytes = 0;
+};
+
+inline SymGeometry make_sym_geometry(int64_t n, int32_t bw, int32_t tw, int32_t dtype) {
+  SymGeometry g;
+  g.n = n;
+  g.bw = bw;
+  g.tw = tw;
+  g.dtype = dtype;
+  g.esize = dtype == 1 ? 8 : 4;
+  g.maxt = bw > 1 ? std::min(tw, bw - 1) : 0;
+  g.W = bw + g.maxt;
+  g.ld = g.W + 1;
+  const int32_t per16 = 16 / g.esize;
+  g.stride = (g.ld + per16 - 1) / per16 * per16;
+  g.band_bytes = (size_t(n) * size_t(g.stride) * size_t(g.esize) + 255) / 256 * 256;
+  g.sync_offset = g.band_bytes;
+  g.sync_words = size_t(kSyncHeader + (n + 1) * kLine);
+  g.total_bytes = g.sync_offset + (g.sync_words * 4 + 255) / 256 * 256;
+  return g;
+}
+
+// Cycles of sweep R that must be complete in sweep R-1 before cycle k of
+// sweep R may start in the symmetric reduction: k + L, L = 2 when b' >= 2
+// and 3 when b' = 1, capped at all of R-1 (a sweep publishes its final count
+// after its predecessor's, so "R-1 complete" implies every earlier sweep is).
+inline int sym_lag_of(const Pass &p) { return p.b - p.t >= 2 ? 2 : 3; }
+
 }  // namespace bb

@@ -193,13 +193,14 @@ def cpu_threaded(band, w, seconds):
 
 def kernel_source_hash() -> str:
     """Hash of the sources of the reduction's kernels and their launch set-up
-    (every HIP source but the singular-value step's): stored counter readings
+    (every HIP source but the singular-value step's and the symmetric
+    reduction's): stored counter readings
     are only valid for it."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "band_bidiagonal_bulge_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.startswith("bb_svals"):
+        if f.startswith("bb_svals") or f.startswith("bb_sym"):
             continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())

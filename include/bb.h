@@ -154,6 +154,44 @@ bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, in
  * BB_ERR_HIP. */
 bb_status bb_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream);
 
+/* ---- Symmetric band -> tridiagonal ----
+ *
+ * Defined by the page "A two-stage reduction on an Apple M5 Pro", section 6
+ * (the band chase with the symmetric-band kernels): a symmetric n x n matrix
+ * of bandwidth BW (A(i,j) = 0 for |i-j| > BW) is reduced to tridiagonal form
+ * T = Q^T A Q by the same passes (b -> b - t, t = min(TW, b-1); TW >= BW-1 is
+ * one pass), sweeps and cycles as the general band, with one reflector per
+ * cycle applied from both sides: from the row segment A(p, c..ch) to rows
+ * p+1..c-1 and the symmetric block c..ch and columns ch+1..ch+b.
+ *   band   device, row i (stride ld_band >= bw+1 elements) holds
+ *          A(i, i..i+bw) = A(i..i+bw, i); entries past n are ignored.
+ *   d, e   device outputs: d[i] = T(i,i) (n), e[i] = T(i,i+1) (n-1; may be
+ *          NULL when n == 1).  e is determined up to sign.
+ *   work   device workspace, 256-byte aligned, of bb_sym_workspace_bytes();
+ *          the working band (row i at i*stride, element (i,j) at offset j-i,
+ *          W+1 = bw + min(tw,bw-1) + 1 entries in use) and counters.
+ *   tuning NULL or {scheduler DEFAULT or PERSISTENT, max_blocks,
+ *          threads_per_block, spin_limit}; other fields as for bb_reduce.
+ * Same arithmetic contract as bb_reduce; the reduction of the symmetric
+ * block uses LAPACK's rank-2 form y = tau B v, alpha = -(tau/2) y.v,
+ * z = y + alpha v, B -= v z^T + z v^T, every sum serial with fma.
+ * Errors: BB_ERR_ARG, BB_ERR_UNSUPPORTED (tile width > 64, band of 2 GiB or
+ * more, a scheduler other than DEFAULT/PERSISTENT), BB_ERR_WORKSPACE,
+ * BB_ERR_HIP.  bb_sym_device_status reports BB_ERR_TIMEOUT after a bounded
+ * wait expired. */
+bb_status bb_sym_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes);
+bb_status bb_sym_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
+                        void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream);
+
+/* Copies the symmetric working band left in `work` to dst (device, n rows
+ * of W+1 elements, row i = A(i, i..i+W)).  Errors: BB_ERR_ARG, BB_ERR_HIP. */
+bb_status bb_sym_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,
+                             void *stream);
+
+/* Synchronises `stream`; BB_OK or BB_ERR_TIMEOUT for the last bb_sym_reduce
+ * on `work`.  Errors: BB_ERR_ARG, BB_ERR_HIP. */
+bb_status bb_sym_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream);
+
 /* ---- Singular values of the bidiagonal (the step after the reduction) ----
  *
  * Defined by the page "A two-stage reduction on an Apple M5 Pro", section 7:

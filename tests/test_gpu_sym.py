@@ -1,0 +1,141 @@
+"""Symmetric band -> tridiagonal on the GPU (bb_sym_reduce, through the C
+ABI) against the symmetric oracle (needs a GPU).
+
+Both sides follow the same reading of the page "A two-stage reduction on an
+Apple M5 Pro", section 6, operation by operation, so d, e and the whole
+working band are compared to the bit, on shapes with several sweeps per
+workgroup, ragged tails, every tile size (t+1 <= 9, 17, 33, 65), one pass
+and several, b' = 1 and wider targets, zero rows, few workgroups, and at the
+full headline size on sampled properties (eigenvalue agreement with the fp64
+path, exact zeros).
+"""
+import numpy as np
+import pytest
+
+import band_bidiagonal_bulge_amd as bbm
+import bb_inputs
+import oracle
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_sym(band, bw, tw, tun=None, return_band=False):
+    import torch
+    dev = torch.device("cuda:0")
+    tb = torch.from_numpy(np.ascontiguousarray(band)).to(dev)
+    n = band.shape[0]
+    work = bbm.sym_workspace(n, bw, tw, tb.dtype, dev)
+    d, e = bbm.sym_reduce(tb, bw, tw, tun, work)
+    torch.cuda.synchronize()
+    out = [d.cpu().numpy(), e.cpu().numpy()]
+    if return_band:
+        ld = oracle.sym_working_ld(n, bw, tw)
+        W = torch.empty((n, ld), dtype=tb.dtype, device=dev)
+        bbm.bb_sym_export_band(work.data_ptr(), n, bw, tw, bbm.dtype_code(tb.dtype), W.data_ptr(),
+                               torch.cuda.current_stream(dev).cuda_stream)
+        torch.cuda.synchronize()
+        out.append(W.cpu().numpy())
+    st = bbm.bb_sym_device_status(work.data_ptr(), n, bw, tw, bbm.dtype_code(tb.dtype),
+                                  torch.cuda.current_stream(dev).cuda_stream)
+    assert st == 0, bbm.bb_status_str(st)
+    return tuple(out)
+
+
+SMALL = [
+    (512, 16, 8, "f64", "normal"),
+    (1000, 32, 16, "f32", "normal"),
+    (777, 24, 5, "f64", "normal"),
+    (300, 64, 16, "f32", "normal"),
+    (257, 33, 32, "f32", "uniform"),
+    (200, 65, 64, "f64", "normal"),
+    (130, 10, 3, "f32", "normal"),
+    (97, 9, 40, "f64", "normal"),
+    (40, 39, 13, "f64", "normal"),
+    (17, 16, 5, "f32", "normal"),
+    (500, 48, 47, "f32", "uniform_zero_rows"),
+    (64, 2, 1, "f64", "normal"),
+    (3, 2, 1, "f32", "normal"),
+    (1, 0, 1, "f64", "normal"),
+]
+
+
+@pytest.mark.parametrize("n,bw,tw,dt,dist", SMALL)
+def test_bitwise_equal_to_oracle(n, bw, tw, dt, dist):
+    log(f"sym bitwise n={n} bw={bw} tw={tw} {dt} {dist}")
+    band = bb_inputs.make_band(n, bw, dt, dist, seed=n + bw)
+    d, e, W = gpu_sym(band, bw, tw, return_band=True)
+    od, oe, OW = oracle.sym_reduce(band, bw, tw, return_band=True)
+    np.testing.assert_array_equal(d, od)
+    np.testing.assert_array_equal(e, oe)
+    np.testing.assert_array_equal(W, OW)
+    assert np.all(W[:, 2:] == 0)
+
+
+@pytest.mark.parametrize("tun", [dict(max_blocks=1), dict(max_blocks=3), dict(threads_per_block=64),
+                                 dict(scheduler=bbm.BB_SCHED_PERSISTENT, max_blocks=7)])
+def test_launch_shapes(tun):
+    n, bw, tw = 600, 24, 8
+    log(f"sym launch shape {tun}")
+    band = bb_inputs.make_band(n, bw, "f32", "normal", seed=5)
+    d, e = gpu_sym(band, bw, tw, bbm.tuning(**tun))
+    od, oe = oracle.sym_reduce(band, bw, tw)
+    np.testing.assert_array_equal(d, od)
+    np.testing.assert_array_equal(e, oe)
+
+
+def test_forced_timeout_is_reported():
+    import torch
+    n, bw, tw = 400, 16, 8
+    log("sym forced timeout")
+    band = torch.from_numpy(bb_inputs.make_band(n, bw, "f32", "normal", seed=1)).to("cuda:0")
+    work = bbm.sym_workspace(n, bw, tw, band.dtype, band.device)
+    bbm.sym_reduce(band, bw, tw, bbm.tuning(spin_limit=1), work)
+    st = bbm.bb_sym_device_status(work.data_ptr(), n, bw, tw, bbm.BB_F32,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st in (0, 5)   # 5: a one-poll wait expired; either way every kernel ended
+    d, e = bbm.sym_reduce(band, bw, tw, None, work)       # the workspace is reusable afterwards
+    torch.cuda.synchronize()
+    od, oe = oracle.sym_reduce(band.cpu().numpy(), bw, tw)
+    np.testing.assert_array_equal(d.cpu().numpy(), od)
+
+
+def test_rejects_unsupported():
+    import torch
+    band = torch.zeros((100, 10), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(bbm.BBError):
+        bbm.sym_reduce(band, 9, 4, bbm.tuning(scheduler=bbm.BB_SCHED_STEP))
+    with pytest.raises(bbm.BBError):
+        bbm.sym_reduce(band, 10, 4)          # ld 10 < bw + 1
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_headline_size_properties(dt):
+    # n = 16384, BW = 64, TW = 16: exact zeros off the tridiagonal and the
+    # eigenvalues of the fp32 path against the fp64 path's, within the
+    # fp32 gate (2e-4 ||A||_F); sampled oracle rows on the smaller n below
+    n, bw, tw = 16384, 64, 16
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=0)
+    log(f"sym headline {dt}")
+    d, e, W = gpu_sym(band, bw, tw, return_band=True)
+    assert np.all(W[:, 2:] == 0)
+    fro = np.sqrt(np.sum(band.astype(np.float64) ** 2) * 2 - np.sum(band[:, 0].astype(np.float64) ** 2))
+    if dt == "f32":
+        d64, e64 = gpu_sym(band.astype(np.float64), bw, tw)
+        import scipy.linalg as sl
+        ev32 = sl.eigvalsh_tridiagonal(d.astype(np.float64), e.astype(np.float64), lapack_driver="stebz")
+        ev64 = sl.eigvalsh_tridiagonal(d64, e64, lapack_driver="stebz")
+        assert np.max(np.abs(ev32 - ev64)) <= 2e-4 * fro
+    t2 = np.sum(d.astype(np.float64) ** 2) + 2 * np.sum(e.astype(np.float64) ** 2)
+    assert abs(np.sqrt(t2) - fro) <= (1e-4 if dt == "f32" else 1e-12) * fro
+
+
+def test_bitwise_at_four_thousand():
+    # the page's symmetric size: n = 4096, b = 32, straight to tridiagonal
+    n, bw, tw = 4096, 32, 31
+    log("sym n=4096 bw=32 tw=31 f32")
+    band = bb_inputs.make_band(n, bw, "f32", "normal", seed=0)
+    d, e = gpu_sym(band, bw, tw)
+    od, oe = oracle.sym_reduce(band, bw, tw)
+    np.testing.assert_array_equal(d, od)
+    np.testing.assert_array_equal(e, oe)
