@@ -48,26 +48,47 @@ __device__ __forceinline__ bool sym_wait(const uint32_t *line, uint32_t need, in
   return true;
 }
 
-// One-sided apply of H (v_0 = 1, v in LDS) to the m entries of a segment
-// starting at byte offset o with byte step `step`.
-template <typename T, int MAXM, class B>
-__device__ __forceinline__ void apply_seg(const B &A, uint32_t o, uint32_t step, const T *v, T tau, int m) {
+// A segment of m entries (a row at columns S or a column at rows S) in
+// registers: loaded before the reflector is known, then H applied and stored.
+template <typename T, int MAXM>
+struct Seg {
   T a[MAXM];
+  template <class B>
+  __device__ __forceinline__ void load(const B &A, uint32_t o, uint32_t step, int m) {
 #pragma unroll
-  for (int j = 0; j < MAXM; ++j)
-    if (j < m) a[j] = A.ld_(o + uint32_t(j) * step);
-  T s = a[0];
+    for (int j = 0; j < MAXM; ++j)
+      if (j < m) a[j] = A.ld_(o + uint32_t(j) * step);
+  }
+  // one-sided apply of H (v_0 = 1, v in LDS): s = a_0 + sum fma(a_j, v_j),
+  // w = tau s, a_0 -= w, a_j = fma(-w, v_j, a_j)
+  template <class B>
+  __device__ __forceinline__ void apply_store(const B &A, uint32_t o, uint32_t step, const T *v, T tau, int m) {
+    T s = a[0];
 #pragma unroll
-  for (int j = 1; j < MAXM; ++j)
-    if (j < m) s = fma_(a[j], v[j], s);
-  const T w = tau * s;
-  a[0] = a[0] - w;
+    for (int j = 1; j < MAXM; ++j)
+      if (j < m) s = fma_(a[j], v[j], s);
+    const T w = tau * s;
+    a[0] = a[0] - w;
 #pragma unroll
-  for (int j = 1; j < MAXM; ++j)
-    if (j < m) a[j] = fma_(-w, v[j], a[j]);
+    for (int j = 1; j < MAXM; ++j)
+      if (j < m) a[j] = fma_(-w, v[j], a[j]);
 #pragma unroll
-  for (int j = 0; j < MAXM; ++j)
-    if (j < m) A.st_(o + uint32_t(j) * step, a[j]);
+    for (int j = 0; j < MAXM; ++j)
+      if (j < m) A.st_(o + uint32_t(j) * step, a[j]);
+  }
+};
+
+// Row-major index of the upper-triangle element number q of an m x m block:
+// (i, j), i <= j, rows in order.
+__device__ __forceinline__ void tri_index(int q, int m, int &i, int &j) {
+  i = 0;
+  int rowlen = m;
+  while (q >= rowlen) {
+    q -= rowlen;
+    ++i;
+    --rowlen;
+  }
+  j = i + q;
 }
 
 template <typename T, int MAXM>
@@ -75,6 +96,7 @@ __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64
                                                      uint32_t *sync, int64_t spin_limit) {
   const Band<T, kSc1> A = make_band<T, kSc1>(a, stride, 0, n);
   __shared__ T xs[MAXM], vs[MAXM], ys[MAXM], zs[MAXM];
+  __shared__ T Bs[MAXM * MAXM];  // the symmetric block, both triangles
   __shared__ int64_t sR;
   __shared__ int sgo;
   uint32_t *status = sync;
@@ -104,31 +126,50 @@ __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64
       const int64_t ch = c + t < n - 1 ? c + t : n - 1;
       const int m = int(ch - c + 1);
       const int64_t p = (k == 0) ? R : c - b;
+      // rows p+1..c-1 at columns S, then columns ch+1..min(ch+b, n-1) at rows S
+      const int64_t nr = c - p - 1;
+      const int64_t jlast = ch + b < n - 1 ? ch + b : n - 1;
+      const int64_t nseg = nr + (jlast - ch);
+      // every load of the cycle is issued before the reflector is formed
+      Seg<T, MAXM> seg;
+      uint32_t so = 0, sst = 0;
+      if (tid < nseg) {
+        if (tid < nr) {
+          so = A.off(p + 1 + tid, c);
+          sst = uint32_t(sizeof(T));
+        } else {
+          so = A.off(c, ch + 1 + (tid - nr));
+          sst = A.row_step();
+        }
+        seg.load(A, so, sst, m);
+      }
       if (tid < m) xs[tid] = A.ld_(A.off(p, c + tid));
+      const int ntri = m * (m + 1) / 2;
+      for (int q = tid; q < ntri; q += nt) {
+        int i, j;
+        tri_index(q, m, i, j);
+        const T v = A.ld_(A.off(c + i, c + j));
+        Bs[i * MAXM + j] = v;
+        Bs[j * MAXM + i] = v;
+      }
       __syncthreads();
       const Refl<T> h = house<T, MAXM, false>(xs, m);
       if (h.nz) {
         if (tid < m) vs[tid] = tid == 0 ? T(1) : xs[tid] * h.inv;
         __syncthreads();
-        // y = tau B v over the symmetric block (B(i,j) = B(j,i) read from the
-        // upper triangle), serial in j from B(i,0)
-        if (tid < m) {
-          T s = A.ld_(A.off(c, c + tid));
-          for (int j = 1; j < m; ++j) {
-            const T bij = (tid <= j) ? A.ld_(A.off(c + tid, c + j)) : A.ld_(A.off(c + j, c + tid));
-            s = fma_(bij, vs[j], s);
-          }
+        if (tid < m) {  // y = tau B v, serial in j from B(i,0)
+          T s = Bs[tid * MAXM];
+          for (int j = 1; j < m; ++j) s = fma_(Bs[tid * MAXM + j], vs[j], s);
           ys[tid] = h.tau * s;
         }
-        // rows p+1..c-1 at columns S, then columns ch+1..min(ch+b, n-1) at rows S
-        const int64_t nr = c - p - 1;
-        const int64_t jlast = ch + b < n - 1 ? ch + b : n - 1;
-        const int64_t nc = jlast - ch;
-        for (int64_t q = tid; q < nr + nc; q += nt) {
-          if (q < nr)
-            apply_seg<T, MAXM>(A, A.off(p + 1 + q, c), uint32_t(sizeof(T)), vs, h.tau, m);
-          else
-            apply_seg<T, MAXM>(A, A.off(c, ch + 1 + (q - nr)), A.row_step(), vs, h.tau, m);
+        if (tid < nseg) seg.apply_store(A, so, sst, vs, h.tau, m);
+        for (int64_t q = tid + nt; q < nseg; q += nt) {  // bands wider than the workgroup
+          Seg<T, MAXM> more;
+          const bool row = q < nr;
+          const uint32_t o = row ? A.off(p + 1 + q, c) : A.off(c, ch + 1 + (q - nr));
+          const uint32_t st = row ? uint32_t(sizeof(T)) : A.row_step();
+          more.load(A, o, st, m);
+          more.apply_store(A, o, st, vs, h.tau, m);
         }
         __syncthreads();
         T dot = ys[0];
@@ -136,12 +177,10 @@ __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64
         const T alpha = -((T(0.5) * h.tau) * dot);
         if (tid < m) zs[tid] = fma_(alpha, vs[tid], ys[tid]);
         __syncthreads();
-        if (tid < m) {
-          const T vi = vs[tid], zi = zs[tid];
-          for (int j = tid; j < m; ++j) {
-            const uint32_t o = A.off(c + tid, c + j);
-            A.st_(o, fma_(-vi, zs[j], fma_(-zi, vs[j], A.ld_(o))));
-          }
+        for (int q = tid; q < ntri; q += nt) {  // B -= v z^T + z v^T, upper triangle
+          int i, j;
+          tri_index(q, m, i, j);
+          A.st_(A.off(c + i, c + j), fma_(-vs[i], zs[j], fma_(-zs[i], vs[j], Bs[i * MAXM + j])));
         }
       }
       if (tid < m) {

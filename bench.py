@@ -16,6 +16,10 @@ Prints one JSON line:
                   bidiagonal by bisection on the GPU (bb_svals), its ALU
                   roofline in Sturm pivots per second, and the bisection
                   oracle timed on a sample of the values
+  sym             the symmetric band -> tridiagonal reduction (bb_sym_reduce)
+                  on the headline shape and on the page's n = 4096, b = 32
+                  one-pass shape: ms, effective GB/s, its cycle kernel's
+                  roofline, and the symmetric oracle on the smaller shape
   cpu_threaded    the oracle's cycles with each pass's sweeps on all host
                   cores (at most 16), on the whole reduction when it fits the
                   time bound, else on its first pass
@@ -154,6 +158,66 @@ def measure_svals(bbm, torch, d, e, w, steps, stream, cpu_seconds, with_cpu):
     return out
 
 
+def sym_pass_bytes(n, b, t, esize):
+    """Algorithmic bytes of one symmetric pass: every cycle reads and writes
+    the pivot row segment, the row segments above the block, the block's
+    upper triangle and the column segments to its right, once each."""
+    bp = b - t
+    R = np.arange(max(n - bp - 1, 0), dtype=np.int64)
+    K = (n - 2 - R - bp) // b + 1
+    Rr = np.repeat(R, K)
+    k = np.arange(Rr.size, dtype=np.int64) - np.repeat(np.cumsum(K) - K, K)
+    c = Rr + bp + k * b
+    ch = np.minimum(c + t, n - 1)
+    m = ch - c + 1
+    p = np.where(k == 0, Rr, c - b)
+    nr = c - p - 1
+    nc = np.minimum(ch + b, n - 1) - ch
+    return float(np.sum(2.0 * esize * (m + nr * m + m * (m + 1) / 2 + nc * m)))
+
+
+SYM_SHAPES = [(16384, 64, 16, "f32"), (4096, 32, 31, "f32")]
+
+
+def measure_sym(bbm, torch, steps, stream, with_cpu):
+    out = []
+    dev = torch.device("cuda:0")
+    for (n, bw, tw, dt) in SYM_SHAPES:
+        band_np = bb_inputs.make_band(n, bw, dt, "normal", seed=0)
+        band = torch.from_numpy(band_np).to(dev)
+        work = bbm.sym_workspace(n, bw, tw, band.dtype, dev)
+        esize = 8 if dt == "f64" else 4
+        passes = pass_list(bw, tw)
+        pbytes = [sym_pass_bytes(n, b, t, esize) for (b, t) in passes]
+        bbm.sym_reduce(band, bw, tw, None, work)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            bbm.sym_reduce(band, bw, tw, None, work)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        status = bbm.bb_sym_device_status(work.data_ptr(), n, bw, tw, bbm.dtype_code(band.dtype),
+                                          stream.cuda_stream)
+        total = sum(pbytes)
+        gbps = total / (ms * 1e-3) / 1e9
+        entry = {"workload": f"sym-n{n}-bw{bw}-tw{tw}-{dt}-normal", "ms": round(ms, 3), "GBps": round(gbps, 2),
+                 "alg_bytes": total, "passes": len(passes), "device_status": bbm.bb_status_str(status),
+                 "kernel": "k_sym_persist, one launch per pass",
+                 "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(gbps / HBM_PEAK_GBPS, 5),
+                              "note": "whole reduction over its wall time (the launches are back to back)"}}
+        if with_cpu and n <= 4096:
+            import oracle
+            oracle.build_sym()
+            t0 = time.perf_counter()
+            oracle.sym_reduce(band_np, bw, tw)
+            dtc = time.perf_counter() - t0
+            entry["cpu_oracle"] = {"value": round(total / dtc / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                   "kind": "oracle", "sample": f"the whole reduction ({dtc:.2f} s, one thread)"}
+        out.append(entry)
+    return out
+
+
 def host_cores() -> int:
     """Host threads for the threaded CPU chaser: the cores this process may
     run on, at most 16 (the host share that goes with one GPU).  The chaser
@@ -249,6 +313,7 @@ def main():
     ap.add_argument("--scheduler", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-svals", action="store_true")
+    ap.add_argument("--no-sym", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
@@ -356,6 +421,8 @@ def main():
     }
     if not args.no_svals:
         out["svals"] = measure_svals(bbm, torch, d, e, w, args.steps, stream, args.cpu_seconds / 3, not args.no_cpu)
+    if not args.no_sym:
+        out["sym"] = measure_sym(bbm, torch, max(1, min(args.steps, 3)), stream, not args.no_cpu)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(band, w, args.cpu_seconds)
         out["cpu_threaded"] = cpu_threaded(band, w, args.cpu_seconds)
