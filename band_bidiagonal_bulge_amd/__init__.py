@@ -7,7 +7,7 @@ for device memory and the stream only).
 """
 from __future__ import annotations
 
-from ._lib import (BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
+from ._lib import (BB_F16, BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
                    BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
                    bb_run_pass, bb_status_str, bb_svals, bb_svals_split, bb_svals_workspace_bytes, bb_sym_device_status,
@@ -26,7 +26,9 @@ def dtype_code(torch_dtype) -> int:
         return BB_F32
     if torch_dtype == torch.float64:
         return BB_F64
-    raise TypeError("band must be float32 or float64")
+    if torch_dtype == torch.float16:
+        return BB_F16
+    raise TypeError("band must be float16, float32 or float64")
 
 
 def tuning(scheduler: int = 0, stagger: int = 0, max_blocks: int = 0, threads_per_block: int = 0,

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbb.so")
 
-BB_F32, BB_F64 = 0, 1
+BB_F32, BB_F64, BB_F16 = 0, 1, 2
 BB_OK, BB_ERR_ARG, BB_ERR_WORKSPACE, BB_ERR_HIP, BB_ERR_UNSUPPORTED, BB_ERR_TIMEOUT = range(6)
 BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT, BB_SCHED_GROUP = 0, 1, 2, 3
 

@@ -19,7 +19,7 @@ constexpr int64_t kMaxN = int64_t(1) << 30;
 constexpr int32_t kMaxTile = 64;  // t+1 entries per row/column held in VGPRs
 
 bool valid_shape(int64_t n, int32_t bw, int32_t tw, int32_t dtype) {
-  if (dtype != BB_F32 && dtype != BB_F64) return false;
+  if (dtype != BB_F32 && dtype != BB_F64 && dtype != BB_F16) return false;
   if (n < 1 || n > kMaxN || bw < 0 || tw < 1) return false;
   if (bw > 4096) return false;
   return true;
@@ -202,6 +202,10 @@ bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
 // in LDS (else PERSISTENT); DEFAULT = GROUP where it fits.
 bb_status run_pass(void *work, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu, hipStream_t st) {
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
+  if (g.dtype == BB_F16) {  // half precision: the persistent scheduler only
+    if (tu.scheduler != BB_SCHED_DEFAULT && tu.scheduler != BB_SCHED_PERSISTENT) return BB_ERR_UNSUPPORTED;
+    return run_persistent_pass(work, g, p, tu, sync, st);
+  }
   if (tu.scheduler == BB_SCHED_STEP) return run_step_pass(work, g, p, tu, st);
   if (tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP) {
     const GroupPlan gp = group_plan(g, p, tu.group_sweeps);
@@ -219,6 +223,7 @@ bool sym_supported(const bb::SymGeometry &g) {
 bb_status check_sym_work(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const void *work, size_t work_bytes,
                          bb::SymGeometry *g) {
   if (!valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  if (dtype == BB_F16) return BB_ERR_UNSUPPORTED;
   *g = bb::make_sym_geometry(n, bw, tw, dtype);
   if (!sym_supported(*g)) return BB_ERR_UNSUPPORTED;
   if (!work || !aligned(work, 256)) return BB_ERR_ARG;
@@ -304,6 +309,7 @@ extern "C" {
 
 bb_status bb_sym_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes) {
   if (!bytes || !valid_shape(n, bw, tw, dtype)) return BB_ERR_ARG;
+  if (dtype == BB_F16) return BB_ERR_UNSUPPORTED;
   const bb::SymGeometry g = bb::make_sym_geometry(n, bw, tw, dtype);
   if (!sym_supported(g)) return BB_ERR_UNSUPPORTED;
   *bytes = g.total_bytes;

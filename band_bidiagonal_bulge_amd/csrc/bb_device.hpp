@@ -27,6 +27,24 @@ __device__ __forceinline__ float fma_(float a, float b, float c) { return __buil
 __device__ __forceinline__ double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
 __device__ __forceinline__ float sqrt_(float a) { return __builtin_sqrtf(a); }
 __device__ __forceinline__ double sqrt_(double a) { return __builtin_sqrt(a); }
+__device__ __forceinline__ float div_(float a, float b) { return a / b; }
+__device__ __forceinline__ double div_(double a, double b) { return a / b; }
+// Half precision: fma is the fp16 instruction (one rounding); sqrt and
+// division are the correctly rounded fp32 operations rounded once to fp16,
+// which equals the correctly rounded fp16 result (24 >= 2*11 + 2 bits).  The
+// empty asm keeps the compiler from rewriting the fp32 operation into its own
+// fp16 sequence.
+__device__ __forceinline__ _Float16 fma_(_Float16 a, _Float16 b, _Float16 c) { return __builtin_fmaf16(a, b, c); }
+__device__ __forceinline__ _Float16 sqrt_(_Float16 a) {
+  float r = __builtin_sqrtf(float(a));
+  asm volatile("" : "+v"(r));
+  return _Float16(r);
+}
+__device__ __forceinline__ _Float16 div_(_Float16 a, _Float16 b) {
+  float q = float(a) / float(b);
+  asm volatile("" : "+v"(q));
+  return _Float16(q);
+}
 
 template <typename T>
 struct Refl {
@@ -53,8 +71,8 @@ __device__ __forceinline__ Refl<T> house(const T *x, int m) {
   }
   const T nrm = sqrt_(fma_(alpha, alpha, s));
   h.beta = (alpha >= T(0)) ? -nrm : nrm;
-  h.tau = (h.beta - alpha) / h.beta;
-  h.inv = T(1) / (alpha - h.beta);
+  h.tau = div_(h.beta - alpha, h.beta);
+  h.inv = div_(T(1), alpha - h.beta);
   h.nz = true;
   return h;
 }
@@ -85,7 +103,9 @@ struct Band {
   // (same column) +(ld-1)*sizeof(T)
   __device__ __forceinline__ uint32_t row_step() const { return uint32_t((ld - 1) * int64_t(sizeof(T))); }
   __device__ __forceinline__ T ld_(uint32_t o) const {
-    if constexpr (sizeof(T) == 4)
+    if constexpr (sizeof(T) == 2)
+      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, AUX));
+    else if constexpr (sizeof(T) == 4)
       return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, AUX));
     else
       return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, AUX));
@@ -93,7 +113,9 @@ struct Band {
   __device__ __forceinline__ u32x4 ld4_(uint32_t o) const { return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, AUX); }
   __device__ __forceinline__ void st4_(uint32_t o, u32x4 v) const { __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, AUX); }
   __device__ __forceinline__ void st_(uint32_t o, T v) const {
-    if constexpr (sizeof(T) == 4)
+    if constexpr (sizeof(T) == 2)
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, o, 0, AUX);
+    else if constexpr (sizeof(T) == 4)
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, o, 0, AUX);
     else
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, o, 0, AUX);

@@ -430,12 +430,14 @@ hipError_t persist_dispatch(int maxm, void *wband, const Geometry &g, int b, int
 size_t stage_lds_bytes(int dtype, int maxm, int b, int t) {
   (void)b;
   (void)t;
-  return size_t(2 * maxm) * (dtype == 1 ? 8 : 4);
+  return size_t(2 * maxm) * (dtype == 1 ? 8 : (dtype == 2 ? 2 : 4));
 }
 
 hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
                           int grid, int nt, int64_t spin_limit, hipStream_t st) {
   if (g.dtype == 1) return persist_dispatch<double>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
+  if (g.dtype == 2)
+    return persist_dispatch<_Float16>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
   return persist_dispatch<float>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
 }
 
@@ -445,6 +447,9 @@ hipError_t launch_pack(const void *band, int64_t ld_band, void *wband, const Geo
   if (g.dtype == 1)
     hipLaunchKernelGGL(k_pack<double>, dim3(grid), dim3(block), 0, st, static_cast<const double *>(band), ld_band,
                        g.n, g.bw, static_cast<double *>(wband), int64_t(g.stride), g.sub);
+  else if (g.dtype == 2)
+    hipLaunchKernelGGL(k_pack<_Float16>, dim3(grid), dim3(block), 0, st, static_cast<const _Float16 *>(band),
+                       ld_band, g.n, g.bw, static_cast<_Float16 *>(wband), int64_t(g.stride), g.sub);
   else
     hipLaunchKernelGGL(k_pack<float>, dim3(grid), dim3(block), 0, st, static_cast<const float *>(band), ld_band,
                        g.n, g.bw, static_cast<float *>(wband), int64_t(g.stride), g.sub);
@@ -457,6 +462,9 @@ hipError_t launch_extract(const void *wband, const Geometry &g, void *d, void *e
   if (g.dtype == 1)
     hipLaunchKernelGGL(k_extract<double>, dim3(grid), dim3(block), 0, st, static_cast<const double *>(wband),
                        int64_t(g.stride), g.sub, g.n, static_cast<double *>(d), static_cast<double *>(e));
+  else if (g.dtype == 2)
+    hipLaunchKernelGGL(k_extract<_Float16>, dim3(grid), dim3(block), 0, st, static_cast<const _Float16 *>(wband),
+                       int64_t(g.stride), g.sub, g.n, static_cast<_Float16 *>(d), static_cast<_Float16 *>(e));
   else
     hipLaunchKernelGGL(k_extract<float>, dim3(grid), dim3(block), 0, st, static_cast<const float *>(wband),
                        int64_t(g.stride), g.sub, g.n, static_cast<float *>(d), static_cast<float *>(e));
@@ -472,6 +480,7 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t count, uint32_t v, hipStream_t s
 hipError_t launch_step(int maxm, void *wband, const Geometry &g, int b, int t, int64_t L, int s, int64_t Rlo,
                        int64_t nblk, int nt, hipStream_t st) {
   if (g.dtype == 1) return step_dispatch<double>(maxm, wband, g, b, t, L, s, Rlo, nblk, nt, st);
+  if (g.dtype == 2) return hipErrorInvalidValue;  // fp16 runs on the persistent scheduler only
   return step_dispatch<float>(maxm, wband, g, b, t, L, s, Rlo, nblk, nt, st);
 }
 

@@ -87,7 +87,7 @@ inline Geometry make_geometry(int64_t n, int32_t bw, int32_t tw, int32_t dtype) 
   g.bw = bw;
   g.tw = tw;
   g.dtype = dtype;
-  g.esize = dtype == 1 ? 8 : 4;
+  g.esize = dtype == 1 ? 8 : (dtype == 2 ? 2 : 4);
   g.maxt = bw > 1 ? std::min(tw, bw - 1) : 0;
   g.sub = g.maxt;
   g.ld = g.sub + bw + g.maxt + 1;
@@ -192,7 +192,7 @@ inline SymGeometry make_sym_geometry(int64_t n, int32_t bw, int32_t tw, int32_t 
   g.bw = bw;
   g.tw = tw;
   g.dtype = dtype;
-  g.esize = dtype == 1 ? 8 : 4;
+  g.esize = dtype == 1 ? 8 : (dtype == 2 ? 2 : 4);
   g.maxt = bw > 1 ? std::min(tw, bw - 1) : 0;
   g.W = bw + g.maxt;
   g.ld = g.W + 1;

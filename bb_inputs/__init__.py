@@ -17,6 +17,16 @@ Recipe (every workload is synthetic; the pages name no public dataset):
   * cast once to the workload's dtype.  Both the oracle and the GPU consume
     the same cast array.
 
+Bands with known singular values (known_spectrum_band), for the accuracy
+study of the reduced-precision reduction: A = U diag(sigma) V^T with U, V
+the Q factors of seeded Gaussian matrices (signs fixed by R's diagonal),
+sigma in [0, 1] from one of three spectra ('arithmetic': 1 - i/n;
+'logarithmic': 10**(-6 i/(n-1)); 'quarter_circle': n draws from the density
+(4/pi) sqrt(1 - s^2) on [0, 1], by rejection, sorted), reduced to an upper
+band of bandwidth bw in fp64 by the classical block Householder first stage
+(QR of each column panel, then LQ of the row panel to its right), entries
+beyond the band dropped (they are rounding noise).
+
 Bidiagonals for the singular-value step (make_bidiag): d (n) then e (n-1)
 drawn from one default_rng(seed) stream, N(0,1) ('normal'), the same times
 10**(-6 i / n) for entry i ('graded'), or all ones ('ones'); cast once.
@@ -55,7 +65,7 @@ HEADLINE = "n16384-bw64-tw16-f32-normal"
 
 
 def np_dtype(name: str):
-    return {"f32": np.float32, "f64": np.float64}[name]
+    return {"f16": np.float16, "f32": np.float32, "f64": np.float64}[name]
 
 
 def make_band(n: int, bw: int, dtype: str = "f64", dist: str = "normal", seed: int = 0) -> np.ndarray:
@@ -94,6 +104,55 @@ def make_bidiag(n: int, dtype: str = "f64", dist: str = "normal", seed: int = 0)
     else:
         raise ValueError("unknown distribution %r" % dist)
     return d.astype(np_dtype(dtype)), e.astype(np_dtype(dtype))
+
+
+SPECTRA = ("arithmetic", "logarithmic", "quarter_circle")
+
+
+def _orthogonal(n: int, rng) -> np.ndarray:
+    q, r = np.linalg.qr(rng.standard_normal((n, n)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def known_spectrum(n: int, spectrum: str, rng) -> np.ndarray:
+    i = np.arange(n, dtype=np.float64)
+    if spectrum == "arithmetic":
+        return 1.0 - i / n
+    if spectrum == "logarithmic":
+        return 10.0 ** (-6.0 * i / max(n - 1, 1))
+    if spectrum == "quarter_circle":
+        out = []
+        while len(out) < n:
+            s, u = rng.uniform(0.0, 1.0, 2 * n), rng.uniform(0.0, 1.0, 2 * n)
+            out.extend(s[u <= np.sqrt(1.0 - s * s)].tolist())
+        return np.sort(np.asarray(out[:n]))[::-1].copy()
+    raise ValueError("unknown spectrum %r" % spectrum)
+
+
+def dense_to_band(A: np.ndarray, bw: int) -> np.ndarray:
+    """Upper band (n, bw+1), row i = A'(i, i..i+bw), of A' = Q^T A P from
+    block Householder panels of width bw (fp64)."""
+    A = np.array(A, dtype=np.float64)
+    n = A.shape[0]
+    for j in range(0, n, bw):
+        q, _ = np.linalg.qr(A[j:, j:j + bw], mode="complete")
+        A[j:, j:] = q.T @ A[j:, j:]
+        if j + bw < n:
+            q2, _ = np.linalg.qr(A[j:j + bw, j + bw:].T, mode="complete")
+            A[:, j + bw:] = A[:, j + bw:] @ q2
+    band = np.zeros((n, bw + 1))
+    for o in range(bw + 1):
+        band[:n - o, o] = np.diagonal(A, o)
+    return band
+
+
+def known_spectrum_band(n: int, bw: int, spectrum: str, seed: int = 0):
+    """(band in fp64, sigma descending) with the band's singular values sigma."""
+    rng = np.random.default_rng(seed)
+    sigma = known_spectrum(n, spectrum, rng)
+    U, V = _orthogonal(n, rng), _orthogonal(n, rng)
+    A = (U * sigma[None, :]) @ V.T
+    return dense_to_band(A, bw), sigma
 
 
 def make_workload(w: Workload | str) -> np.ndarray:

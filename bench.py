@@ -20,6 +20,8 @@ Prints one JSON line:
                   on the headline shape and on the page's n = 4096, b = 32
                   one-pass shape: ms, effective GB/s, its cycle kernel's
                   roofline, and the symmetric oracle on the smaller shape
+  f16             the same reduction of the headline band in half precision
+                  (persistent scheduler): ms and effective GB/s
   cpu_threaded    the oracle's cycles with each pass's sweeps on all host
                   cores (at most 16), on the whole reduction when it fits the
                   time bound, else on its first pass
@@ -218,6 +220,71 @@ def measure_sym(bbm, torch, steps, stream, with_cpu):
     return out
 
 
+def measure_f16(bbm, torch, w, steps, stream):
+    """The headline band reduced in half precision (fp16 storage and
+    arithmetic, persistent scheduler)."""
+    band = torch.from_numpy(bb_inputs.make_band(w.n, w.bw, "f16", w.dist, w.seed)).to("cuda:0")
+    work = bbm.workspace(w.n, w.bw, w.tw, band.dtype, band.device)
+    info = bbm.bb_plan(w.n, w.bw, w.tw, bbm.BB_F16)
+    bbm.reduce(band, w.bw, w.tw, None, work)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bbm.reduce(band, w.bw, w.tw, None, work)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    status = bbm.bb_device_status(work.data_ptr(), w.n, w.bw, w.tw, bbm.BB_F16, stream.cuda_stream)
+    gbps = info.alg_bytes / (ms * 1e-3) / 1e9
+    return {"workload": f"n{w.n}-bw{w.bw}-tw{w.tw}-f16-{w.dist}", "ms": round(ms, 3), "GBps": round(gbps, 2),
+            "alg_bytes": info.alg_bytes, "kernel": "k_persist<_Float16>, one launch per pass",
+            "device_status": bbm.bb_status_str(status),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 5),
+                         "note": "whole reduction over its wall time (the launches are back to back)"}}
+
+
+def accuracy_study(n, bw, tw, instances, out_md):
+    """Relative singular-value error ||sigma - Sigma|| / ||Sigma|| of the GPU
+    reduction in fp64, fp32 and fp16 on bands with known singular values
+    (fp64 first stage, fp64 bisection afterwards): the study of the page
+    "Accelerating Bidiagonalization of Banded Matrices through Memory-Aware
+    Bulge-Chasing on GPUs" (known-spectrum accuracy passage)."""
+    import torch
+    import band_bidiagonal_bulge_amd as bbm
+    dev = torch.device("cuda:0")
+    rows = []
+    for spectrum in bb_inputs.SPECTRA:
+        for seed in range(instances):
+            band64, sigma = bb_inputs.known_spectrum_band(n, bw, spectrum, seed=seed)
+            for dt in ("f64", "f32", "f16"):
+                tb = torch.from_numpy(band64.astype(bb_inputs.np_dtype(dt))).to(dev)
+                d, e = bbm.reduce(tb, bw, tw)
+                sv = bbm.svals(d.double(), e.double()).cpu().numpy()
+                rows.append((spectrum, seed, dt, float(np.linalg.norm(sv - sigma) / np.linalg.norm(sigma))))
+    summary = {}
+    for dt in ("f64", "f32", "f16"):
+        errs = sorted(r[3] for r in rows if r[2] == dt)
+        summary[dt] = {"min": errs[0], "median": float(np.median(errs)), "max": errs[-1]}
+        for sp in bb_inputs.SPECTRA:
+            summary[dt][sp + "_median"] = float(np.median([r[3] for r in rows if r[2] == dt and r[0] == sp]))
+    lines = [f"# Accuracy study: n = {n}, BW = {bw}, TW = {tw}, {instances} instances per spectrum", "",
+             "Command (repo root, MI355X): `python bench.py --accuracy-study "
+             f"--study-n {n} --study-bw {bw} --study-tw {tw} --study-instances {instances}`", "",
+             "Relative error ||sigma - Sigma||_2 / ||Sigma||_2 of the singular values after the GPU reduction in",
+             "each precision (fp64 first stage, fp64 bisection of the bidiagonal):", "",
+             "| precision | min | median | max | arithmetic (median) | logarithmic (median) | quarter-circle (median) |",
+             "|---|---|---|---|---|---|---|"]
+    for dt, v in summary.items():
+        lines.append(f"| {dt} | {v['min']:.2e} | {v['median']:.2e} | {v['max']:.2e} | {v['arithmetic_median']:.2e} | "
+                     f"{v['logarithmic_median']:.2e} | {v['quarter_circle_median']:.2e} |")
+    lines += ["", "Every instance:", "", "| spectrum | seed | precision | relative error |", "|---|---|---|---|"]
+    lines += [f"| {sp} | {sd} | {dt} | {er:.3e} |" for (sp, sd, dt, er) in rows]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps({"accuracy_study": {"n": n, "bw": bw, "tw": tw, "instances_per_spectrum": instances,
+                                         "summary": summary}}), flush=True)
+
+
 def host_cores() -> int:
     """Host threads for the threaded CPU chaser: the cores this process may
     run on, at most 16 (the host share that goes with one GPU).  The chaser
@@ -314,6 +381,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-svals", action="store_true")
     ap.add_argument("--no-sym", action="store_true")
+    ap.add_argument("--no-f16", action="store_true")
+    ap.add_argument("--accuracy-study", action="store_true",
+                    help="run the known-spectrum accuracy study instead of the bench (writes --study-out)")
+    ap.add_argument("--study-n", type=int, default=512)
+    ap.add_argument("--study-bw", type=int, default=32)
+    ap.add_argument("--study-tw", type=int, default=16)
+    ap.add_argument("--study-instances", type=int, default=10)
+    ap.add_argument("--study-out", default=os.path.join("gpurun_out", "accuracy_study.md"))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
@@ -322,6 +397,10 @@ def main():
     args = ap.parse_args()
     if args.ingest_counters:
         ingest_counters(args.workload, *args.ingest_counters, args.copy_probe_mib)
+        return
+    if args.accuracy_study:
+        os.makedirs(os.path.dirname(os.path.abspath(args.study_out)), exist_ok=True)
+        accuracy_study(args.study_n, args.study_bw, args.study_tw, args.study_instances, args.study_out)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this reduction runs on one GPU: one matrix is one dependent chain of "
@@ -421,6 +500,8 @@ def main():
     }
     if not args.no_svals:
         out["svals"] = measure_svals(bbm, torch, d, e, w, args.steps, stream, args.cpu_seconds / 3, not args.no_cpu)
+    if not args.no_f16:
+        out["f16"] = measure_f16(bbm, torch, w, max(1, min(args.steps, 3)), stream)
     if not args.no_sym:
         out["sym"] = measure_sym(bbm, torch, max(1, min(args.steps, 3)), stream, not args.no_cpu)
     if not args.no_cpu:

@@ -24,8 +24,8 @@
  *   - Arguments are validated on the host before anything is enqueued; an
  *     invalid call returns an error and enqueues nothing.  No C++ exception
  *     crosses this interface.
- *   - dtype is BB_F32 or BB_F64 and is both the storage and the arithmetic
- *     precision of the reduction.
+ *   - dtype is BB_F32, BB_F64 or BB_F16 (see bb_dtype) and is both the
+ *     storage and the arithmetic precision of the reduction.
  *   - Values are not checked for NaN/Inf; non-finite input propagates.
  */
 #ifndef BB_H_
@@ -38,7 +38,15 @@
 extern "C" {
 #endif
 
-typedef enum { BB_F32 = 0, BB_F64 = 1 } bb_dtype;
+/* Storage and arithmetic precision.  BB_F16 (IEEE binary16) is the
+ * reduced-precision variant of the band -> bidiagonal reduction (page
+ * "Accelerating Bidiagonalization of Banded Matrices through Memory-Aware
+ * Bulge-Chasing on GPUs", the accuracy study run in FP64, FP32 and FP16):
+ * bb_reduce and its staged entry points only, on the persistent scheduler;
+ * each operation rounded once to fp16 (fma fused, sqrt and division
+ * correctly rounded).  The symmetric reduction and bb_svals take BB_F32 and
+ * BB_F64. */
+typedef enum { BB_F32 = 0, BB_F64 = 1, BB_F16 = 2 } bb_dtype;
 
 typedef enum {
   BB_OK = 0,

@@ -39,10 +39,53 @@ _SV_LIB_PATH = os.path.join(_HERE, "libbb_oracle_svals.so")
 _SYM_SRC = [os.path.join(_HERE, "bb_oracle_sym.c"), os.path.join(_HERE, "bb_oracle_sym_body.h")]
 _SYM_LIB_PATH = os.path.join(_HERE, "libbb_oracle_sym.so")
 
+_F16_SRC = [os.path.join(_HERE, "bb_oracle_f16.cpp")] + _SRC
+_F16_LIB_PATH = os.path.join(_HERE, "libbb_oracle_f16.so")
+
 _lib = None
 _mt_lib = None
 _sv_lib = None
 _sym_lib = None
+_f16_lib = None
+
+
+def build_f16(force: bool = False) -> str:
+    """Compile the fp16 oracle (the same body on an emulated binary16 type)."""
+    stale = not os.path.exists(_F16_LIB_PATH) or any(
+        os.path.getmtime(s) > os.path.getmtime(_F16_LIB_PATH) for s in _F16_SRC)
+    if force or stale:
+        tmp = _F16_LIB_PATH + ".tmp%d" % os.getpid()
+        flags = [f for f in _CFLAGS if f != "-std=c99"]
+        cmd = ["g++", *flags, "-std=c++17", "-o", tmp, _F16_SRC[0], "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _F16_LIB_PATH)
+    return _F16_LIB_PATH
+
+
+def f16_lib():
+    global _f16_lib
+    if _f16_lib is None:
+        if not _cpu_has_fma():
+            raise RuntimeError("oracle build uses the FMA instruction; this host CPU lacks it")
+        path = _F16_LIB_PATH if os.path.exists(_F16_LIB_PATH) else build_f16()
+        L = ctypes.CDLL(path)
+        i64, i32, vp, u16 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint16
+        L.bb_oracle_reduce_f16.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i64, ctypes.POINTER(i64)]
+        L.bb_oracle_reduce_f16.restype = i32
+        L.bb_oracle_h16_from_double.argtypes = [ctypes.c_double]
+        L.bb_oracle_h16_from_double.restype = u16
+        L.bb_oracle_h16_to_double.argtypes = [u16]
+        L.bb_oracle_h16_to_double.restype = ctypes.c_double
+        for f in ("bb_oracle_h16_fma",):
+            getattr(L, f).argtypes = [u16, u16, u16]
+            getattr(L, f).restype = u16
+        for f in ("bb_oracle_h16_div",):
+            getattr(L, f).argtypes = [u16, u16]
+            getattr(L, f).restype = u16
+        L.bb_oracle_h16_sqrt.argtypes = [u16]
+        L.bb_oracle_h16_sqrt.restype = u16
+        _f16_lib = L
+    return _f16_lib
 
 
 def build_sym(force: bool = False) -> str:
@@ -187,11 +230,11 @@ def lib():
 
 
 def _np_dtype(name):
-    return {"f32": np.float32, "f64": np.float64}[name]
+    return {"f16": np.float16, "f32": np.float32, "f64": np.float64}[name]
 
 
 def _suffix(dt):
-    return "f32" if np.dtype(dt) == np.float32 else "f64"
+    return {np.dtype(np.float16): "f16", np.dtype(np.float32): "f32"}.get(np.dtype(dt), "f64")
 
 
 def working_ld(n: int, bw: int, tw: int) -> int:
@@ -208,9 +251,9 @@ def reduce(band: np.ndarray, bw: int, tw: int, compute: str | None = None,
     """Sequential bulge-chasing reduction of an upper band.
 
     band     (n, >= bw+1) array, row i holds A(i, i..i+bw); entries past n
-             are ignored.  Its dtype (f32/f64) is the storage precision.
-    compute  'f32' or 'f64' (default: the band's dtype).  An fp32 band with
-             compute='f64' is widened exactly before the reduction.
+             are ignored.  Its dtype (f16/f32/f64) is the storage precision.
+    compute  'f16', 'f32' or 'f64' (default: the band's dtype).  A band of
+             lower precision is widened exactly before the reduction.
     Returns (d, e) or (d, e, working_band, T) with return_band.
     With max_cycles >= 0 the reduction stops early (bench sampling only) and
     the third return value is the number of cycles executed.
@@ -224,7 +267,8 @@ def reduce(band: np.ndarray, bw: int, tw: int, compute: str | None = None,
     ld = working_ld(n, bw, tw)
     out = np.zeros((n, ld), dtype=cdt) if return_band else None
     done = ctypes.c_int64(0)
-    f = getattr(lib(), "bb_oracle_reduce_" + _suffix(cdt))
+    suf = _suffix(cdt)
+    f = getattr(f16_lib() if suf == "f16" else lib(), "bb_oracle_reduce_" + suf)
     rc = f(a.ctypes.data, a.shape[1], n, bw, tw, d.ctypes.data,
            e.ctypes.data if e.size else None,
            out.ctypes.data if out is not None else None, max_cycles, ctypes.byref(done))

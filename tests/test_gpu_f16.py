@@ -1,0 +1,98 @@
+"""Half-precision band -> bidiagonal on the GPU (dtype BB_F16, through the C
+ABI) against the fp16 oracle, and the accuracy study of the page
+"Accelerating Bidiagonalization of Banded Matrices through Memory-Aware
+Bulge-Chasing on GPUs" (known singular values, reduction in FP64 / FP32 /
+FP16, singular values in fp64) on a small scale (needs a GPU).
+"""
+import numpy as np
+import pytest
+
+import band_bidiagonal_bulge_amd as bbm
+import bb_inputs
+import oracle
+from gpu_util import gpu_reduce, log
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(512, 16, 8), (300, 64, 16), (257, 33, 32), (130, 10, 3), (97, 9, 40), (40, 39, 13), (17, 16, 5),
+          (600, 32, 16), (200, 65, 64)]
+
+
+@pytest.mark.parametrize("n,bw,tw", SHAPES)
+def test_bitwise_equal_to_fp16_oracle(n, bw, tw):
+    log(f"f16 bitwise n={n} bw={bw} tw={tw}")
+    band = bb_inputs.make_band(n, bw, "f16", "normal", seed=n + bw)
+    d, e, W, sub = gpu_reduce(band, bw, tw, return_band=True)
+    od, oe, OW, osub = oracle.reduce(band, bw, tw, return_band=True)
+    assert d.dtype == np.float16 and sub == osub
+    np.testing.assert_array_equal(d.view(np.uint16), od.view(np.uint16))
+    np.testing.assert_array_equal(e.view(np.uint16), oe.view(np.uint16))
+    np.testing.assert_array_equal(W.view(np.uint16), OW.view(np.uint16))
+
+
+def test_launch_shapes_and_zero_rows():
+    n, bw, tw = 400, 24, 8
+    band = bb_inputs.make_band(n, bw, "f16", "uniform_zero_rows", seed=3)
+    od, oe = oracle.reduce(band, bw, tw)
+    for tun in (dict(max_blocks=1), dict(max_blocks=5, threads_per_block=64),
+                dict(scheduler=bbm.BB_SCHED_PERSISTENT)):
+        log(f"f16 launch shape {tun}")
+        d, e = gpu_reduce(band, bw, tw, bbm.tuning(**tun))
+        np.testing.assert_array_equal(d.view(np.uint16), od.view(np.uint16))
+        np.testing.assert_array_equal(e.view(np.uint16), oe.view(np.uint16))
+
+
+def test_unsupported_combinations():
+    import torch
+    band = torch.zeros((64, 9), dtype=torch.float16, device="cuda:0")
+    for sched in (bbm.BB_SCHED_STEP, bbm.BB_SCHED_GROUP):
+        with pytest.raises(bbm.BBError):
+            bbm.reduce(band, 8, 4, bbm.tuning(scheduler=sched))
+    with pytest.raises(bbm.BBError):
+        bbm.sym_reduce(band, 8, 4)
+    d = torch.ones(8, dtype=torch.float16, device="cuda:0")
+    with pytest.raises((bbm.BBError, TypeError)):
+        bbm.svals(d, d[:7])
+
+
+def test_headline_shape_in_half_precision():
+    n, bw, tw = 16384, 64, 16
+    band = bb_inputs.make_band(n, bw, "f16", "normal", seed=0)
+    log("f16 headline shape")
+    d, e, W, sub = gpu_reduce(band, bw, tw, return_band=True)
+    assert np.all(np.isfinite(d)) and np.all(np.isfinite(e))
+    off = [o for o in range(W.shape[1]) if o - sub not in (0, 1)]
+    assert np.all(W[:, off] == 0)
+    d64, e64 = gpu_reduce(band.astype(np.float64), bw, tw)
+    fro = np.linalg.norm(band.astype(np.float64))
+    err = max(np.max(np.abs(np.abs(d.astype(np.float64)) - np.abs(d64))),
+              np.max(np.abs(np.abs(e.astype(np.float64)) - np.abs(e64))))
+    log(f"f16 headline: max | |d|,|e| - fp64 | / ||A||_F = {err / fro:.3e}")
+    assert err <= 0.05 * fro
+
+
+def test_accuracy_study_small():
+    # each precision's relative singular-value error on known spectra, with
+    # the fp16 and fp32 GPU bits equal to the oracle's on the first instance
+    import torch
+    n, bw, tw = 192, 16, 8
+    worst = {}
+    for spectrum in bb_inputs.SPECTRA:
+        for seed in range(2):
+            band64, sigma = bb_inputs.known_spectrum_band(n, bw, spectrum, seed=seed)
+            for dt in ("f64", "f32", "f16"):
+                band = band64.astype(bb_inputs.np_dtype(dt))
+                log(f"accuracy {spectrum} seed={seed} {dt}")
+                d, e = gpu_reduce(band, bw, tw)
+                if seed == 0:
+                    od, oe = oracle.reduce(band, bw, tw)
+                    np.testing.assert_array_equal(d, od)
+                    np.testing.assert_array_equal(e, oe)
+                td = torch.from_numpy(d.astype(np.float64)).to("cuda:0")
+                te = torch.from_numpy(e.astype(np.float64)).to("cuda:0")
+                sv = bbm.svals(td, te).cpu().numpy()
+                rel = np.linalg.norm(sv - sigma) / np.linalg.norm(sigma)
+                worst[dt] = max(worst.get(dt, 0.0), rel)
+    log(f"accuracy worst relative errors: {worst}")
+    assert worst["f64"] < 1e-13 and worst["f32"] < 1e-5 and worst["f16"] < 5e-2
+    assert worst["f64"] < worst["f32"] < worst["f16"]
