@@ -238,11 +238,65 @@ int sym_maxm(int32_t t) {
   return 65;
 }
 
+int64_t sym_ring_rows_cached(int64_t n, const bb::Pass &p, int G) {
+  static std::mutex mu;
+  static std::map<std::tuple<int64_t, int, int, int>, int64_t> cache;
+  const auto key = std::make_tuple(n, p.b, p.t, G);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const int64_t rows = bb::sym_group_ring_rows(n, p, G);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = rows;
+  return rows;
+}
+
+// Symmetric sweep groups: register tiles 9 and 17 (fp32 also 33), the
+// largest G <= 4 whose ring fits in LDS (a symmetric half-cycle does more
+// work per wave than a general one; beyond four sweeps per workgroup the
+// waves slow each other more than the shorter hand-offs gain: measured).
+constexpr int kSymGroupDefaultSweeps = 4;
+
+GroupPlan sym_group_plan(const bb::SymGeometry &g, const bb::Pass &p, int requested_g) {
+  GroupPlan gp;
+  const int maxm = sym_maxm(p.t);
+  if (maxm > (g.dtype == BB_F32 ? 33 : 17)) return gp;
+  const int64_t row_bytes = int64_t(g.stride) * g.esize;
+  const size_t ys_bytes = size_t(kGroupMaxSweeps) * size_t(maxm) * size_t(g.esize);
+  const int64_t W = std::min<int64_t>(int64_t(kGroupLdsBytes - ys_bytes) / row_bytes, g.n);
+  const int lo = requested_g > 0 ? requested_g : 1;
+  const int hi = requested_g > 0 ? requested_g : kSymGroupDefaultSweeps;
+  for (int G = hi; G >= lo; --G) {
+    if (sym_ring_rows_cached(g.n, p, G) <= W) {
+      gp.G = G;
+      gp.W = int(W);
+      return gp;
+    }
+  }
+  return gp;
+}
+
 bb_status run_sym_pass(void *work, const bb::SymGeometry &g, const bb::Pass &p, const bb_tuning &tu,
                        hipStream_t st) {
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
   const int64_t ns = bb::sweeps_of(g.n, p);
   if (ns == 0) return BB_OK;
+  if (tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP) {
+    const GroupPlan gp = sym_group_plan(g, p, tu.group_sweeps);
+    if (gp.G > 0) {
+      const int64_t ngroups = (ns + gp.G - 1) / gp.G;
+      if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
+          bb::launch_fill_u32(sync + bb::kSyncHeader, ngroups * bb::kLine, 0u, st) != hipSuccess)
+        return BB_ERR_HIP;
+      int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
+      grid = std::min<int64_t>(grid, ngroups);
+      const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+      return hip_status(bb::launch_sym_group(sym_maxm(p.t), work, g, p.b, p.t, bb::lag_of(p), ns, gp.G, gp.W,
+                                             sync, int(grid), spin, st));
+    }
+  }
   if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
       bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
     return BB_ERR_HIP;
@@ -326,7 +380,7 @@ bb_status bb_sym_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw
   if (rc != BB_OK) return rc;
   bb_tuning tu;
   if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
-  if (tu.scheduler != BB_SCHED_DEFAULT && tu.scheduler != BB_SCHED_PERSISTENT) return BB_ERR_UNSUPPORTED;
+  if (tu.scheduler == BB_SCHED_STEP) return BB_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
   if (bb::launch_sym_pack(band, ld_band, work, g, st) != hipSuccess ||

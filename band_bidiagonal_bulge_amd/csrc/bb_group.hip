@@ -447,6 +447,167 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
   BB_P(pr.flush(sync, lane);)
 }
 
+// ---- the symmetric reduction on the same ring ----------------------------
+//
+// The symmetric cycle (page "A two-stage reduction on an Apple M5 Pro",
+// section 6; the steps and the arithmetic of bb_sym.hip) on ring rows, run
+// by one wave in two half-cycles:
+//   half A (rows p..c-1): the reflector from row p at columns c..ch, applied
+//     to the row segments of rows p+1..c-1 (one lane each, in rounds of 64);
+//     row p becomes (beta, 0, ..., 0);
+//   half B (rows c..ch): the column segments of columns ch+1..min(ch+b, n-1)
+//     and the symmetric block c..ch (lane i: row i of y = tau B v, then row
+//     i's upper part of B -= v z^T + z v^T; the block is read in full before
+//     any lane writes it, y passes between lanes through ys).
+// The reflector passes from half A to half B in registers.  Ring rows are
+// working-band rows: element (i, j), j >= i, at offset j - i.
+template <typename T, int MAXM>
+__device__ __forceinline__ void ring_seg_apply(T (&a)[MAXM], const T (&v)[MAXM], T tau, int m) {
+  T s = a[0];
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j)
+    if (j < m) s = fma_(a[j], v[j], s);
+  const T w = tau * s;
+  a[0] = a[0] - w;
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j)
+    if (j < m) a[j] = fma_(-w, v[j], a[j]);
+}
+
+template <typename T, int MAXM>
+__device__ void ring_sym_half_a(const Ring<T> &A, int32_t c, int m, int32_t p, int lane, Refl<T> &h,
+                                T (&v)[MAXM], T &myv) {
+  const int32_t S = A.S;
+  T *L = A.L;
+  const int32_t sp = A.slot(p);
+  T *px = L + sp * S + (c - p);
+  T x[MAXM];
+#pragma unroll
+  for (int j = 0; j < MAXM; ++j) x[j] = j < m ? px[j] : T(0);
+  T sn = T(0);
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j)
+    if (j < m) sn = fma_(x[j], x[j], sn);
+  h = house_from(x[0], sn);
+  myv = T(0);
+  if (h.nz) {
+    v[0] = T(1);
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j) v[j] = x[j] * h.inv;
+    if (lane < m) myv = lane == 0 ? T(1) : px[lane] * h.inv;  // v_lane
+    const int32_t nr = c - p - 1;  // rows p+1..c-1 at columns c..ch
+    for (int32_t q = lane; q < nr; q += 64) {
+      T *pr = L + A.next(sp, 1 + q) * S + (c - (p + 1 + q));
+      T a[MAXM];
+#pragma unroll
+      for (int j = 0; j < MAXM; ++j) a[j] = j < m ? pr[j] : T(0);
+      ring_seg_apply<T, MAXM>(a, v, h.tau, m);
+#pragma unroll
+      for (int j = 0; j < MAXM; ++j)
+        if (j < m) pr[j] = a[j];
+    }
+  }
+  if (lane < m) {
+    if (lane == 0) {
+      if (h.nz) px[0] = h.beta;
+    } else {
+      px[lane] = T(0);
+    }
+  }
+}
+
+template <typename T, int MAXM>
+__device__ void ring_sym_half_b(const Ring<T> &A, T *ys, int32_t n, int b, int32_t c, int m, int lane,
+                                const Refl<T> &h, const T (&v)[MAXM], T myv) {
+  if (!h.nz) return;
+  const int32_t S = A.S;
+  T *L = A.L;
+  const int32_t sc = A.slot(c), ch = c + m - 1;
+  // y_i = tau (B(i,0) + sum_j B(i,j) v_j), B(i,j) = row c+min(i,j), offset |i-j|
+  T yi = T(0);
+  const int32_t si = A.next(sc, lane < m ? lane : 0);
+  if (lane < m) {
+    T s = L[sc * S + lane];
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j)
+      if (j < m) s = fma_(lane <= j ? L[si * S + (j - lane)] : L[A.next(sc, j) * S + (lane - j)], v[j], s);
+    yi = h.tau * s;
+    ys[lane] = yi;
+  }
+  const int32_t nc = min(ch + b, n - 1) - ch;  // columns ch+1.. at rows c..ch
+  for (int32_t q = lane; q < nc; q += 64) {
+    const int32_t col = ch + 1 + q;
+    T a[MAXM];
+    int32_t s = sc;
+#pragma unroll
+    for (int i = 0; i < MAXM; ++i) {
+      if (i < m) a[i] = L[s * S + (col - c - i)];
+      s = s + 1 == A.W ? 0 : s + 1;
+    }
+    ring_seg_apply<T, MAXM>(a, v, h.tau, m);
+    s = sc;
+#pragma unroll
+    for (int i = 0; i < MAXM; ++i) {
+      if (i < m) L[s * S + (col - c - i)] = a[i];
+      s = s + 1 == A.W ? 0 : s + 1;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  T yv[MAXM];
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) yv[i] = i < m ? ys[i] : T(0);
+  T dot = yv[0];
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i)
+    if (i < m) dot = fma_(yv[i], v[i], dot);
+  const T alpha = -((T(0.5) * h.tau) * dot);
+  if (lane < m) {
+    const T zi = fma_(alpha, myv, yi);
+#pragma unroll
+    for (int j = 0; j < MAXM; ++j)
+      if (j >= lane && j < m) {
+        T *e = L + si * S + (j - lane);
+        *e = fma_(-myv, fma_(alpha, v[j], yv[j]), fma_(-zi, v[j], *e));
+      }
+  }
+}
+
+// One symmetric sweep of the group, run by one wave: half q waits until the
+// previous sweep of the group has done min(q + d, all) halves and until its
+// rows are loaded; the final count waits for the predecessor's final count.
+// Floors: after half A the sweep still touches rows from c, after half B
+// from the next pivot row (c again).
+template <typename T, int MAXM>
+__device__ void sym_group_sweep(const Ring<T> &A, GroupCtl &ctl, T *ys, int32_t n, int b, int t, int d, int32_t R,
+                                int j, int lane, int64_t spin_limit, uint32_t *status) {
+  const int32_t K = int32_t(cycles_of_dev(n, b, t, R));
+  const int32_t Kp = j > 0 ? int32_t(cycles_of_dev(n, b, t, R - 1)) : 0;
+  int32_t known_pred = 0, known_rows = 0;
+  for (int32_t k = 0; k < K; ++k) {
+    const int32_t c = R + (b - t) + k * b;
+    const int32_t ch = min(c + t, n - 1);
+    const int m = ch - c + 1;
+    const int32_t p = k == 0 ? R : c - b;
+    Refl<T> h;
+    T v[MAXM], myv;
+    if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * k + d, 2 * Kp), ctl, spin_limit, status)) return;
+    if (!rows_wait(&ctl.loaded_hi, known_rows, c, ctl, spin_limit, status)) return;
+    ring_sym_half_a<T, MAXM>(A, c, m, p, lane, h, v, myv);
+    if (lane == 0)
+      __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * k + 1, c), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * k + 1 + d, 2 * Kp), ctl, spin_limit, status))
+      return;
+    if (!rows_wait(&ctl.loaded_hi, known_rows, ch + 1, ctl, spin_limit, status)) return;
+    ring_sym_half_b<T, MAXM>(A, ys, n, b, c, m, lane, h, v, myv);
+    if (k + 1 == K && j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, 2 * Kp, ctl, spin_limit, status)) return;
+    if (lane == 0)
+      __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * k + 2, k + 1 < K ? c : n), __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 
@@ -571,8 +732,9 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
 }
 
 // Persistent group kernel: workgroups claim groups in increasing order.
-// blockDim = 64 (G + 2); dynamic LDS = W * S * sizeof(T).
-template <typename T, int MAXM, int SC>
+// blockDim = 64 (G + 2); dynamic LDS = W * S * sizeof(T).  SYM: the sweeps
+// are the symmetric reduction's (by half-cycles, with the same lag d).
+template <typename T, int MAXM, int SC, bool SYM = false>
 __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, int32_t sub, int32_t n, int b,
                                                                  int t, int d, int32_t nsweeps, int G, int W,
                                                                  uint32_t *sync, int64_t spin_limit) {
@@ -605,7 +767,13 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
     }
     __syncthreads();
     if (wave < Gg) {
-      group_sweep<T, MAXM, SC>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
+      if constexpr (SYM) {
+        __shared__ T sym_ys[kGroupMaxSweeps * MAXM];
+        sym_group_sweep<T, MAXM>(A, ctl, sym_ys + wave * MAXM, n, b, t, d, R0 + wave, wave, lane, spin_limit,
+                                 status);
+      } else {
+        group_sweep<T, MAXM, SC>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
+      }
     } else if (wave == G) {
       group_writer<T>(A, ctl, mem, n, R0, Gg, prog + int64_t(g) * kLine, lane, spin_limit, status, sync);
     } else if (wave == G + 1) {
@@ -656,7 +824,34 @@ hipError_t group_dispatch(int maxm, void *wband, const Geometry &g, int b, int t
   }
 }
 
+template <typename T, int MAXM>
+hipError_t sym_group_t(void *wband, const SymGeometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
+                       uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+  const size_t lds = size_t(W) * size_t(g.stride) * sizeof(T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, 0, true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_group<T, MAXM, 0, true>), dim3(unsigned(grid)), dim3(unsigned(64 * (G + 2))), lds, st,
+                     static_cast<T *>(wband), g.stride, 0, int32_t(g.n), b, t, d, int32_t(nsweeps), G, W, sync,
+                     spin_limit);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_sym_group(int maxm, void *wband, const SymGeometry &g, int b, int t, int d, int64_t nsweeps, int G,
+                            int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+  if (g.dtype == 1) {
+    if (maxm == 9) return sym_group_t<double, 9>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    if (maxm == 17) return sym_group_t<double, 17>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    return hipErrorInvalidValue;
+  }
+  if (g.dtype != 0) return hipErrorInvalidValue;
+  if (maxm == 9) return sym_group_t<float, 9>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  if (maxm == 17) return sym_group_t<float, 17>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  if (maxm == 33) return sym_group_t<float, 33>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
                         int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {

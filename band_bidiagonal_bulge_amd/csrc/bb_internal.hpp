@@ -43,6 +43,10 @@ hipError_t launch_sym_pack(const void *band, int64_t ld_band, void *wband, const
 hipError_t launch_sym_persist(int maxm, void *wband, const SymGeometry &g, int b, int t, int64_t nsweeps,
                               uint32_t *sync, int grid, int nt, int64_t spin_limit, hipStream_t st);
 hipError_t launch_sym_extract(const void *wband, const SymGeometry &g, void *d, void *e, hipStream_t st);
+// The symmetric sweeps in LDS-resident groups (the k_group kernel with the
+// symmetric half-cycles): maxm 9 or 17 (fp32 also 33), d = the lag in halves.
+hipError_t launch_sym_group(int maxm, void *wband, const SymGeometry &g, int b, int t, int d, int64_t nsweeps, int G,
+                            int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st);
 
 // Singular values of the bidiagonal by bisection (bb_svals.hip).  The
 // workspace holds a header {lo, hi, pivmin} in its first kSvalsHeaderBytes,

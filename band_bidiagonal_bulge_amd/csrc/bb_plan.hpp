@@ -205,10 +205,63 @@ inline SymGeometry make_sym_geometry(int64_t n, int32_t bw, int32_t tw, int32_t 
   return g;
 }
 
-// Cycles of sweep R that must be complete in sweep R-1 before cycle k of
-// sweep R may start in the symmetric reduction: k + L, L = 2 when b' >= 2
-// and 3 when b' = 1, capped at all of R-1 (a sweep publishes its final count
-// after its predecessor's, so "R-1 complete" implies every earlier sweep is).
-inline int sym_lag_of(const Pass &p) { return p.b - p.t >= 2 ? 2 : 3; }
+// The symmetric reduction runs by half-cycles too: half 2k forms cycle k's
+// reflector and applies it to the pivot row and the row segments above the
+// block (rows p..c-1), half 2k+1 applies it to the block and the column
+// segments (rows c..ch).  The lag between consecutive sweeps is then
+// lag_of(p) half-cycles, as for the general band (derived from the halves'
+// read/write footprints), capped at all of the predecessor; a sweep
+// publishes its final count after its predecessor's.
+
+// Rows symmetric half-cycle q of sweep R touches: [lo, hi].
+inline void sym_half_rows(int64_t n, const Pass &p, int64_t R, int64_t q, int64_t *lo, int64_t *hi) {
+  const int64_t k = q >> 1;
+  const int64_t c = R + (p.b - p.t) + k * p.b;
+  if (q & 1) {
+    *lo = c;
+    *hi = std::min<int64_t>(c + p.t, n - 1);
+  } else {
+    *lo = k == 0 ? R : c - p.b;
+    *hi = c - 1;
+  }
+}
+
+// Ring rows a group of G symmetric sweeps needs (the bound of
+// group_ring_rows with the symmetric halves).
+inline int64_t sym_group_ring_rows(int64_t n, const Pass &p, int G) {
+  const int64_t ns = sweeps_of(n, p);
+  const int d = lag_of(p);
+  int64_t need = 0;
+  std::vector<int64_t> K(size_t(G), 0);
+  for (int64_t R0 = 0; R0 < ns; R0 += G) {
+    const int Gg = int(std::min<int64_t>(G, ns - R0));
+    int64_t steps = 0;
+    for (int j = 0; j < Gg; ++j) {
+      K[size_t(j)] = cycles_of(n, p, R0 + j);
+      steps = std::max<int64_t>(steps, 2 * K[size_t(j)] + int64_t(j) * d);
+    }
+    for (int64_t q0 = 0; q0 < steps; ++q0) {
+      int64_t hi = -1, fl = n;
+      for (int j = 0; j < Gg; ++j) {
+        const int64_t R = R0 + j, twoK = 2 * K[size_t(j)];
+        int64_t lo, h;
+        const int64_t qa = q0 - int64_t(j) * (d - 1);  // most advanced position: rows needed
+        if (qa >= 0 && qa < twoK) {
+          sym_half_rows(n, p, R, qa, &lo, &h);
+          hi = std::max(hi, h);
+        }
+        const int64_t qb = q0 - int64_t(j) * d;  // least advanced position: rows still live
+        if (qb < 0) {
+          fl = std::min(fl, R);
+        } else if (qb < twoK) {
+          sym_half_rows(n, p, R, qb, &lo, &h);
+          fl = std::min(fl, lo);
+        }
+      }
+      if (hi >= 0) need = std::max(need, hi - fl + 1);
+    }
+  }
+  return need;
+}
 
 }  // namespace bb

@@ -18,10 +18,14 @@
 // the index-0 term; nothing else is contracted; sqrt and division are
 // correctly rounded.
 //
-// Scheduling: the persistent design of the general band.  Workgroups claim
-// sweeps in increasing order; before cycle k a workgroup waits until sweep
-// R-1 has completed min(k + L, all) cycles (L = 2 when b' >= 2, else 3) and
-// afterwards publishes k + 1, the final count only once R-1's is final.  Band
+// Scheduling: the persistent design of the general band, by half-cycles:
+// half 2k forms cycle k's reflector and applies it to the pivot row and the
+// row segments (rows p..c-1), half 2k+1 applies it to the block and the
+// column segments (rows c..ch).  Workgroups claim sweeps in increasing
+// order; before half q a workgroup waits until sweep R-1 has completed
+// min(q + d, all) halves (d = 2, 3, 4 for b' >= 3, 2, 1, the same lag as the
+// general band, derived from the halves' footprints) and afterwards
+// publishes q + 1, the final count only once R-1's is final.  Band
 // accesses are agent-coherent (sc1): sweeps hand entries to workgroups on
 // other XCDs, whose L2 caches are not coherent with each other.
 
@@ -103,7 +107,8 @@ __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64
   uint32_t *claim = sync + kClaim;
   uint32_t *prog = sync + kSyncHeader;
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int L = (b - t >= 2) ? 2 : 3;
+  const int bp = b - t;
+  const int d = bp >= 3 ? 2 : (bp == 2 ? 3 : 4);  // half-cycles between consecutive sweeps
   if (tid == 0) sgo = 1;
   for (;;) {
     if (tid == 0) sR = int64_t(atomicAdd(claim, 1u));
@@ -114,73 +119,62 @@ __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64
     const int64_t Kp = R > 0 ? cycles_of_dev(n, b, t, R - 1) : 0;
     const uint32_t *pred = prog + (R - 1) * kLine;
     for (int64_t k = 0; k < K; ++k) {
-      if (R > 0) {
-        if (tid == 0) {
-          const int64_t need = k + L < Kp ? k + L : Kp;
-          sgo = sym_wait(pred, uint32_t(need), spin_limit, status);
-        }
-        __syncthreads();
-        if (!sgo) return;
-      }
-      const int64_t c = R + (b - t) + k * b;
+      const int64_t c = R + bp + k * b;
       const int64_t ch = c + t < n - 1 ? c + t : n - 1;
       const int m = int(ch - c + 1);
       const int64_t p = (k == 0) ? R : c - b;
-      // rows p+1..c-1 at columns S, then columns ch+1..min(ch+b, n-1) at rows S
-      const int64_t nr = c - p - 1;
-      const int64_t jlast = ch + b < n - 1 ? ch + b : n - 1;
-      const int64_t nseg = nr + (jlast - ch);
-      // every load of the cycle is issued before the reflector is formed
-      Seg<T, MAXM> seg;
-      uint32_t so = 0, sst = 0;
-      if (tid < nseg) {
-        if (tid < nr) {
-          so = A.off(p + 1 + tid, c);
-          sst = uint32_t(sizeof(T));
-        } else {
-          so = A.off(c, ch + 1 + (tid - nr));
-          sst = A.row_step();
+      // wait for half q's predecessor progress, or publish q + 1 (every
+      // wave's stores complete, then one thread moves the counter; the final
+      // count waits for the predecessor's final count)
+      auto wait_half = [&](int64_t q) -> bool {
+        if (R > 0) {
+          if (tid == 0) {
+            const int64_t need = q + d < 2 * Kp ? q + d : 2 * Kp;
+            sgo = sym_wait(pred, uint32_t(need), spin_limit, status);
+          }
+          __syncthreads();
+          if (!sgo) return false;
         }
-        seg.load(A, so, sst, m);
+        return true;
+      };
+      auto publish_half = [&](int64_t q) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (tid == 0) {
+          bool go = true;
+          if (R > 0 && q + 1 == 2 * K) go = sym_wait(pred, uint32_t(2 * Kp), spin_limit, status);
+          if (go)
+            __hip_atomic_store(prog + R * kLine, uint32_t(q + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            sgo = 0;
+        }
+      };
+      // half A: the reflector from the pivot row, the row segments of rows
+      // p+1..c-1 (loads issued before the reflector is formed), the pivot
+      // row becomes (beta, 0, ..., 0)
+      if (!wait_half(2 * k)) return;
+      Refl<T> h;
+      {
+        const int64_t nr = c - p - 1;
+        Seg<T, MAXM> seg;
+        const uint32_t so = tid < nr ? A.off(p + 1 + tid, c) : 0u;
+        if (tid < nr) seg.load(A, so, uint32_t(sizeof(T)), m);
+        if (tid < m) xs[tid] = A.ld_(A.off(p, c + tid));
+        __syncthreads();
+        h = house<T, MAXM, false>(xs, m);
+        if (h.nz) {
+          if (tid < m) vs[tid] = tid == 0 ? T(1) : xs[tid] * h.inv;
+          __syncthreads();
+          if (tid < nr) seg.apply_store(A, so, uint32_t(sizeof(T)), vs, h.tau, m);
+        }
       }
-      if (tid < m) xs[tid] = A.ld_(A.off(p, c + tid));
-      const int ntri = m * (m + 1) / 2;
-      for (int q = tid; q < ntri; q += nt) {
-        int i, j;
-        tri_index(q, m, i, j);
-        const T v = A.ld_(A.off(c + i, c + j));
-        Bs[i * MAXM + j] = v;
-        Bs[j * MAXM + i] = v;
-      }
-      __syncthreads();
-      const Refl<T> h = house<T, MAXM, false>(xs, m);
       if (h.nz) {
-        if (tid < m) vs[tid] = tid == 0 ? T(1) : xs[tid] * h.inv;
-        __syncthreads();
-        if (tid < m) {  // y = tau B v, serial in j from B(i,0)
-          T s = Bs[tid * MAXM];
-          for (int j = 1; j < m; ++j) s = fma_(Bs[tid * MAXM + j], vs[j], s);
-          ys[tid] = h.tau * s;
-        }
-        if (tid < nseg) seg.apply_store(A, so, sst, vs, h.tau, m);
-        for (int64_t q = tid + nt; q < nseg; q += nt) {  // bands wider than the workgroup
+        const int64_t nr = c - p - 1;
+        for (int64_t r = tid + nt; r < nr; r += nt) {  // bands wider than the workgroup
           Seg<T, MAXM> more;
-          const bool row = q < nr;
-          const uint32_t o = row ? A.off(p + 1 + q, c) : A.off(c, ch + 1 + (q - nr));
-          const uint32_t st = row ? uint32_t(sizeof(T)) : A.row_step();
-          more.load(A, o, st, m);
-          more.apply_store(A, o, st, vs, h.tau, m);
-        }
-        __syncthreads();
-        T dot = ys[0];
-        for (int i = 1; i < m; ++i) dot = fma_(ys[i], vs[i], dot);
-        const T alpha = -((T(0.5) * h.tau) * dot);
-        if (tid < m) zs[tid] = fma_(alpha, vs[tid], ys[tid]);
-        __syncthreads();
-        for (int q = tid; q < ntri; q += nt) {  // B -= v z^T + z v^T, upper triangle
-          int i, j;
-          tri_index(q, m, i, j);
-          A.st_(A.off(c + i, c + j), fma_(-vs[i], zs[j], fma_(-zs[i], vs[j], Bs[i * MAXM + j])));
+          const uint32_t o = A.off(p + 1 + r, c);
+          more.load(A, o, uint32_t(sizeof(T)), m);
+          more.apply_store(A, o, uint32_t(sizeof(T)), vs, h.tau, m);
         }
       }
       if (tid < m) {
@@ -190,18 +184,52 @@ __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64
           A.st_(A.off(p, c + tid), T(0));
         }
       }
-      // publish: every wave's stores complete, then one thread moves the
-      // counter; the final count waits for the predecessor's final count
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      if (tid == 0) {
-        bool go = true;
-        if (R > 0 && k == K - 1) go = sym_wait(pred, uint32_t(Kp), spin_limit, status);
-        if (go)
-          __hip_atomic_store(prog + R * kLine, uint32_t(k + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
-          sgo = 0;
+      publish_half(2 * k);
+      // half B: the column segments of columns ch+1..min(ch+b, n-1) and the
+      // symmetric block (staged in LDS, both triangles)
+      if (!wait_half(2 * k + 1)) return;
+      if (h.nz) {
+        const int64_t jlast = ch + b < n - 1 ? ch + b : n - 1;
+        const int64_t nc = jlast - ch;
+        const int ntri = m * (m + 1) / 2;
+        {
+          Seg<T, MAXM> seg;
+          const uint32_t so = tid < nc ? A.off(c, ch + 1 + tid) : 0u;
+          if (tid < nc) seg.load(A, so, A.row_step(), m);
+          for (int qq = tid; qq < ntri; qq += nt) {
+            int i, j;
+            tri_index(qq, m, i, j);
+            const T v = A.ld_(A.off(c + i, c + j));
+            Bs[i * MAXM + j] = v;
+            Bs[j * MAXM + i] = v;
+          }
+          __syncthreads();
+          if (tid < m) {  // y = tau B v, serial in j from B(i,0)
+            T s = Bs[tid * MAXM];
+            for (int j = 1; j < m; ++j) s = fma_(Bs[tid * MAXM + j], vs[j], s);
+            ys[tid] = h.tau * s;
+          }
+          if (tid < nc) seg.apply_store(A, so, A.row_step(), vs, h.tau, m);
+        }
+        for (int64_t r = tid + nt; r < nc; r += nt) {
+          Seg<T, MAXM> more;
+          const uint32_t o = A.off(c, ch + 1 + r);
+          more.load(A, o, A.row_step(), m);
+          more.apply_store(A, o, A.row_step(), vs, h.tau, m);
+        }
+        __syncthreads();
+        T dot = ys[0];
+        for (int i = 1; i < m; ++i) dot = fma_(ys[i], vs[i], dot);
+        const T alpha = -((T(0.5) * h.tau) * dot);
+        if (tid < m) zs[tid] = fma_(alpha, vs[tid], ys[tid]);
+        __syncthreads();
+        for (int qq = tid; qq < ntri; qq += nt) {  // B -= v z^T + z v^T, upper triangle
+          int i, j;
+          tri_index(qq, m, i, j);
+          A.st_(A.off(c + i, c + j), fma_(-vs[i], zs[j], fma_(-zs[i], vs[j], Bs[i * MAXM + j])));
+        }
       }
+      publish_half(2 * k + 1);
     }
     __syncthreads();  // sR is rewritten by the next claim
   }

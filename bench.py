@@ -204,7 +204,8 @@ def measure_sym(bbm, torch, steps, stream, with_cpu):
         gbps = total / (ms * 1e-3) / 1e9
         entry = {"workload": f"sym-n{n}-bw{bw}-tw{tw}-{dt}-normal", "ms": round(ms, 3), "GBps": round(gbps, 2),
                  "alg_bytes": total, "passes": len(passes), "device_status": bbm.bb_status_str(status),
-                 "kernel": "k_sym_persist, one launch per pass",
+                 "kernel": "symmetric cycle kernel (k_group with the symmetric half-cycles where the pass's LDS "
+                           "ring fits, else k_sym_persist), one launch per pass",
                  "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(gbps / HBM_PEAK_GBPS, 5),
                               "note": "whole reduction over its wall time (the launches are back to back)"}}

@@ -178,13 +178,16 @@ bb_status bb_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, 
  *   work   device workspace, 256-byte aligned, of bb_sym_workspace_bytes();
  *          the working band (row i at i*stride, element (i,j) at offset j-i,
  *          W+1 = bw + min(tw,bw-1) + 1 entries in use) and counters.
- *   tuning NULL or {scheduler DEFAULT or PERSISTENT, max_blocks,
- *          threads_per_block, spin_limit}; other fields as for bb_reduce.
+ *   tuning NULL or as for bb_reduce: DEFAULT and GROUP run sweep groups
+ *          resident in LDS where the pass fits (tile widths up to 16, or 32
+ *          in fp32), else PERSISTENT; STEP is not available.
  * Same arithmetic contract as bb_reduce; the reduction of the symmetric
  * block uses LAPACK's rank-2 form y = tau B v, alpha = -(tau/2) y.v,
  * z = y + alpha v, B -= v z^T + z v^T, every sum serial with fma.
+ * The sweeps run by half-cycles (the pivot row and the row segments; the
+ * block and the column segments) with the lag of the general band.
  * Errors: BB_ERR_ARG, BB_ERR_UNSUPPORTED (tile width > 64, band of 2 GiB or
- * more, a scheduler other than DEFAULT/PERSISTENT), BB_ERR_WORKSPACE,
+ * more, the STEP scheduler, BB_F16), BB_ERR_WORKSPACE,
  * BB_ERR_HIP.  bb_sym_device_status reports BB_ERR_TIMEOUT after a bounded
  * wait expired. */
 bb_status bb_sym_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes);

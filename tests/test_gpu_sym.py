@@ -73,7 +73,11 @@ def test_bitwise_equal_to_oracle(n, bw, tw, dt, dist):
 
 
 @pytest.mark.parametrize("tun", [dict(max_blocks=1), dict(max_blocks=3), dict(threads_per_block=64),
-                                 dict(scheduler=bbm.BB_SCHED_PERSISTENT, max_blocks=7)])
+                                 dict(scheduler=bbm.BB_SCHED_PERSISTENT, max_blocks=7),
+                                 dict(scheduler=bbm.BB_SCHED_PERSISTENT),
+                                 dict(scheduler=bbm.BB_SCHED_GROUP, group_sweeps=1),
+                                 dict(scheduler=bbm.BB_SCHED_GROUP, group_sweeps=2, max_blocks=2),
+                                 dict(scheduler=bbm.BB_SCHED_GROUP, group_sweeps=6, max_blocks=5)])
 def test_launch_shapes(tun):
     n, bw, tw = 600, 24, 8
     log(f"sym launch shape {tun}")
@@ -84,16 +88,30 @@ def test_launch_shapes(tun):
     np.testing.assert_array_equal(e, oe)
 
 
+@pytest.mark.parametrize("n,bw,tw,dt", [(512, 16, 8, "f64"), (1000, 32, 16, "f32"), (300, 64, 16, "f32"),
+                                        (257, 33, 32, "f32"), (130, 10, 3, "f32"), (500, 48, 47, "f32")])
+def test_group_and_persistent_agree_to_the_bit(n, bw, tw, dt):
+    log(f"sym group vs persistent n={n} bw={bw} tw={tw} {dt}")
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=2 * n + bw)
+    dg, eg, Wg = gpu_sym(band, bw, tw, bbm.tuning(scheduler=bbm.BB_SCHED_GROUP), return_band=True)
+    dp, ep, Wp = gpu_sym(band, bw, tw, bbm.tuning(scheduler=bbm.BB_SCHED_PERSISTENT), return_band=True)
+    np.testing.assert_array_equal(Wg, Wp)
+    od, oe = oracle.sym_reduce(band, bw, tw)
+    np.testing.assert_array_equal(dg, od)
+    np.testing.assert_array_equal(eg, oe)
+
+
 def test_forced_timeout_is_reported():
     import torch
     n, bw, tw = 400, 16, 8
     log("sym forced timeout")
     band = torch.from_numpy(bb_inputs.make_band(n, bw, "f32", "normal", seed=1)).to("cuda:0")
     work = bbm.sym_workspace(n, bw, tw, band.dtype, band.device)
-    bbm.sym_reduce(band, bw, tw, bbm.tuning(spin_limit=1), work)
-    st = bbm.bb_sym_device_status(work.data_ptr(), n, bw, tw, bbm.BB_F32,
-                                  torch.cuda.current_stream().cuda_stream)
-    assert st in (0, 5)   # 5: a one-poll wait expired; either way every kernel ended
+    for sched in (bbm.BB_SCHED_PERSISTENT, bbm.BB_SCHED_GROUP):
+        bbm.sym_reduce(band, bw, tw, bbm.tuning(scheduler=sched, spin_limit=1), work)
+        st = bbm.bb_sym_device_status(work.data_ptr(), n, bw, tw, bbm.BB_F32,
+                                      torch.cuda.current_stream().cuda_stream)
+        assert st in (0, 5)   # 5: a one-poll wait expired; either way every kernel ended
     d, e = bbm.sym_reduce(band, bw, tw, None, work)       # the workspace is reusable afterwards
     torch.cuda.synchronize()
     od, oe = oracle.sym_reduce(band.cpu().numpy(), bw, tw)

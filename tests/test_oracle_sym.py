@@ -11,9 +11,11 @@ facts other than itself:
   * schedules: the footprints of the cycles (every entry a cycle reads or
     writes) show that sweep R may run cycle k once sweep R-1 has completed
     min(k + L, all) cycles, L = 2 when b' >= 2 and 3 when b' = 1, with the
-    final count published after the predecessor's; one cycle less is not
-    enough; and an order that runs concurrent cycles in reverse reproduces
-    the sequential result to the bit.
+    final count published after the predecessor's; split into half-cycles
+    (pivot row and row segments; block and column segments) the lag is
+    d = 2, 3, 4 halves for b' >= 3, 2, 1; one unit less is never enough; and
+    an order that runs concurrent cycles in reverse reproduces the
+    sequential result to the bit.
 Planted mistakes in a copy of the oracle each fail this battery
 (test_planted_mistake_is_caught).
 """
@@ -188,6 +190,49 @@ def test_wait_rule_orders_every_conflict(n, b, t):
     L = 2 if b - t >= 2 else 3
     assert conflicts_unordered(n, b, t, L) == []
     assert conflicts_unordered(n, b, t, L - 1) != []   # one cycle less is not enough
+
+
+def half_footprint(n, b, t, R, q):
+    """Entries half q of sweep R reads or writes: half 2k is the pivot row
+    and the row segments above the block, half 2k+1 the block and the
+    column segments to its right (both of cycle k)."""
+    k, h = divmod(q, 2)
+    c = R + (b - t) + k * b
+    ch = min(c + t, n - 1)
+    p = R if k == 0 else c - b
+    out = set()
+    if h == 0:
+        for i in range(p, c):
+            out.update((i, j) for j in range(c, ch + 1))
+    else:
+        for i in range(c, ch + 1):
+            out.update((i, j) for j in range(i, min(ch + b, n - 1) + 1))
+    return out
+
+
+def half_conflicts_unordered(n, b, t, d):
+    ns = max(n - (b - t) - 1, 0)
+    K2 = [2 * cycles_of(n, b, t, R) for R in range(ns)]
+    fp = {(R, q): half_footprint(n, b, t, R, q) for R in range(ns) for q in range(K2[R])}
+    bad = []
+    for (R2, q2), f2 in fp.items():
+        for R1 in range(max(0, R2 - 8), R2):
+            done = done_when_starting(K2, d, R2, q2, R1)
+            for q1 in range(done, K2[R1]):
+                if fp[(R1, q1)] & f2:
+                    bad.append(((R1, q1), (R2, q2)))
+    return bad
+
+
+@pytest.mark.parametrize("n,b,t", [(40, 6, 2), (40, 6, 4), (45, 8, 7), (30, 5, 3), (36, 4, 1), (33, 3, 2),
+                                   (40, 2, 1), (60, 16, 13), (60, 16, 14), (60, 16, 15)])
+def test_half_cycle_rule_orders_every_conflict(n, b, t):
+    # at half-cycle granularity the lag is d = 2 / 3 / 4 half-cycles for
+    # b' >= 3 / 2 / 1, the rule of the general band; one less is not enough
+    bp = b - t
+    d = 2 if bp >= 3 else (3 if bp == 2 else 4)
+    assert half_conflicts_unordered(n, b, t, d) == []
+    assert half_conflicts_unordered(n, b, t, d - 1) != []
 
 
 @pytest.mark.parametrize("n,bw,tw", [(40, 8, 3), (33, 6, 5), (30, 5, 1)])

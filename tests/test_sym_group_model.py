@@ -1,0 +1,266 @@
+"""Host emulation of the sweep-group protocol for the symmetric reduction
+(no GPU): the group kernel's rules (rows released between groups through
+X_g, in-group waits of d half-cycles, floors, a ring of W rows) with the
+symmetric half-cycle as the unit of work: half 2k forms cycle k's reflector
+and applies it to the pivot row and the row segments above the block, half
+2k+1 applies it to the block and the column segments (the reflector passes
+between the two halves in the wave's registers).
+
+As in test_group_model.py, the real cycle arithmetic runs (numpy, the same
+code for both sides) under random interleavings of every enabled action,
+each group on private copies of its rows (as in LDS) that reach the shared
+matrix only through write-backs, and the test checks that the result equals
+the sequential reduction to the bit and that no interleaving deadlocks with
+the ring size the library computes (re-derived here).
+"""
+import numpy as np
+import pytest
+
+from refs import pass_list
+
+
+def cycles_of(n, b, t, R):
+    last = n - 2 - R - (b - t)
+    return 0 if last < 0 else last // b + 1
+
+
+def lag(b, t):
+    """Half-cycles of separation (d)."""
+    bp = b - t
+    return 2 if bp >= 3 else (3 if bp == 2 else 4)
+
+
+def cyc_geom(n, b, t, R, k):
+    c = R + (b - t) + k * b
+    ch = min(c + t, n - 1)
+    p = R if k == 0 else c - b
+    return c, ch, p
+
+
+def half_rows(n, b, t, R, q):
+    """Rows half q of sweep R touches: half 2k = rows p..c-1 (pivot row and
+    the row segments), half 2k+1 = rows c..ch (block, column segments)."""
+    c, ch, p = cyc_geom(n, b, t, R, q // 2)
+    return (p, c - 1) if q % 2 == 0 else (c, ch)
+
+
+def half_floor(n, b, t, R, q, K):
+    """Lowest row sweep R still touches after q halves."""
+    if q >= 2 * K:
+        return n
+    c, ch, p = cyc_geom(n, b, t, R, q // 2)
+    return p if q % 2 == 0 else c
+
+
+def do_half(rows, refl, n, b, t, R, q):
+    """Half q of sweep R on dense upper rows; refl carries v and tau from
+    half 2k to half 2k+1 (as the wave's registers do)."""
+    c, ch, p = cyc_geom(n, b, t, R, q // 2)
+    m = ch - c + 1
+    if q % 2 == 0:
+        x = rows[p][c:ch + 1].copy()
+        s = float(np.dot(x[1:], x[1:]))
+        refl[R] = None
+        if s != 0.0:
+            alpha = x[0]
+            nrm = np.sqrt(alpha * alpha + s)
+            beta = -nrm if alpha >= 0 else nrm
+            tau = (beta - alpha) / beta
+            v = x / (alpha - beta)
+            v[0] = 1.0
+            refl[R] = (tau, v)
+            for i in range(p + 1, c):
+                a = rows[i][c:ch + 1]
+                w = tau * (a[0] + float(np.dot(a[1:], v[1:])))
+                a[0] -= w
+                a[1:] -= w * v[1:]
+            rows[p][c] = beta
+        rows[p][c + 1:ch + 1] = 0.0
+        return
+    if refl[R] is None:
+        return
+    tau, v = refl[R]
+    for j in range(ch + 1, min(ch + b, n - 1) + 1):
+        a = np.array([rows[c + i][j] for i in range(m)])
+        w = tau * (a[0] + float(np.dot(a[1:], v[1:])))
+        a[0] -= w
+        a[1:] -= w * v[1:]
+        for i in range(m):
+            rows[c + i][j] = a[i]
+    B = np.array([[rows[c + min(i, j)][c + max(i, j)] for j in range(m)] for i in range(m)])
+    y = tau * (B @ v)
+    alpha2 = -(0.5 * tau) * float(y @ v)
+    z = y + alpha2 * v
+    for i in range(m):
+        for j in range(i, m):
+            rows[c + i][c + j] = B[i, j] - v[i] * z[j] - z[i] * v[j]
+
+
+def sequential(A, b, t):
+    n = A.shape[0]
+    rows = {i: A[i].copy() for i in range(n)}
+    refl = {}
+    for R in range(max(n - (b - t) - 1, 0)):
+        for q in range(2 * cycles_of(n, b, t, R)):
+            do_half(rows, refl, n, b, t, R, q)
+    return np.array([rows[i] for i in range(n)])
+
+
+def sym_group_ring_rows(n, b, t, G):
+    """The library's ring size (bb_plan.hpp sym_group_ring_rows), re-derived."""
+    ns = max(n - (b - t) - 1, 0)
+    d = lag(b, t)
+    need = 0
+    for R0 in range(0, ns, G):
+        Gg = min(G, ns - R0)
+        K2 = [2 * cycles_of(n, b, t, R0 + j) for j in range(Gg)]
+        steps = max(K2[j] + j * d for j in range(Gg))
+        for q0 in range(steps):
+            hi, fl = -1, n
+            for j in range(Gg):
+                qa = q0 - j * (d - 1)
+                if 0 <= qa < K2[j]:
+                    hi = max(hi, half_rows(n, b, t, R0 + j, qa)[1])
+                qb = q0 - j * d
+                if qb < 0:
+                    fl = min(fl, R0 + j)
+                elif qb < K2[j]:
+                    fl = min(fl, half_rows(n, b, t, R0 + j, qb)[0])
+            if hi >= 0:
+                need = max(need, hi - fl + 1)
+    return need
+
+
+class Group:
+    def __init__(self, g, G, ns, n, b, t):
+        self.g, self.R0 = g, g * G
+        self.Gg = min(G, ns - self.R0)
+        self.K = [2 * cycles_of(n, b, t, self.R0 + j) for j in range(self.Gg)]
+        self.Kp = [2 * cycles_of(n, b, t, self.R0 + j - 1) if j > 0 else 0 for j in range(self.Gg)]
+        self.refl = {}
+        self.prog = [0] * self.Gg
+        self.done = [0] * self.Gg
+        self.floor = [self.R0 + j for j in range(self.Gg)]
+        self.loaded = self.written = self.R0
+        self.X = 0
+        self.lds = {}
+
+
+def emulate(A, b, t, G, W, rng, max_live=None, d=None):
+    n = A.shape[0]
+    L = lag(b, t) if d is None else d   # half-cycles
+    ns = max(n - (b - t) - 1, 0)
+    mem = {i: A[i].copy() for i in range(n)}
+    groups = [Group(g, G, ns, n, b, t) for g in range((ns + G - 1) // G)]
+    started = 0 if max_live else len(groups)
+    while True:
+        live = [gr for gr in groups[:started] if gr.X < n]
+        if max_live and len(live) < max_live and started < len(groups):
+            started += 1
+            continue
+        if not live:
+            break
+        acts = []
+        for gr in live:
+            xprev = n if gr.g == 0 else groups[gr.g - 1].X
+            for j in range(gr.Gg):
+                q = gr.done[j]
+                if q == gr.prog[j] and q < gr.K[j]:
+                    lo, hi = half_rows(n, b, t, gr.R0 + j, q)
+                    pred_ok = j == 0 or gr.prog[j - 1] >= min(q + L, gr.Kp[j])
+                    if pred_ok and gr.loaded > hi:
+                        acts.append(("cycle", gr, j))
+                elif gr.done[j] == gr.prog[j] + 1:
+                    final = gr.done[j] == gr.K[j]
+                    if not final or j == 0 or gr.prog[j - 1] >= gr.Kp[j]:
+                        acts.append(("publish", gr, j))
+            dead = min(gr.floor) if gr.Gg else n
+            if min(dead, gr.loaded) > gr.written:
+                acts.append(("writeback", gr, None))
+            if min(xprev, gr.written + W, n) > gr.loaded:
+                acts.append(("load", gr, None))
+            if min(gr.written, xprev) > gr.X:
+                acts.append(("announce", gr, None))
+        if not acts:
+            raise RuntimeError("deadlock")
+        kind, gr, j = acts[rng.integers(len(acts))]
+        xprev = n if gr.g == 0 else groups[gr.g - 1].X
+        if kind == "cycle":
+            R, q = gr.R0 + j, gr.done[j]
+            lo, hi = half_rows(n, b, t, R, q)
+            assert all(i in gr.lds for i in range(lo, hi + 1)) and lo >= gr.written
+            do_half(gr.lds, gr.refl, n, b, t, R, q)
+            gr.done[j] += 1
+        elif kind == "publish":
+            q = gr.done[j]
+            gr.floor[j] = half_floor(n, b, t, gr.R0 + j, q, gr.K[j] // 2)
+            gr.prog[j] = q
+        elif kind == "writeback":
+            wb = min(min(gr.floor), gr.loaded)
+            for i in range(gr.written, wb):
+                mem[i] = gr.lds.pop(i).copy()
+            gr.written = wb
+        elif kind == "load":
+            lim = min(xprev, gr.written + W, n)
+            for i in range(gr.loaded, lim):
+                gr.lds[i] = mem[i].copy()
+            gr.loaded = lim
+            assert len(gr.lds) <= W
+        else:
+            gr.X = min(gr.written, xprev)
+    return np.array([mem[i] for i in range(n)])
+
+
+SHAPES = [(40, 8, 3, 2), (40, 8, 3, 3), (36, 6, 5, 3), (45, 6, 2, 4), (30, 4, 1, 3), (33, 7, 6, 5), (50, 10, 4, 2)]
+
+
+@pytest.mark.parametrize("n,bw,tw,G", SHAPES)
+def test_sym_group_protocol_matches_sequential(n, bw, tw, G):
+    rng = np.random.default_rng(n * 10 + bw)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))   # upper rows of a symmetric band
+    for (b, t) in pass_list(bw, tw):
+        ref = sequential(A, b, t)
+        W = sym_group_ring_rows(n, b, t, G)
+        for trial in range(3):
+            out = emulate(A, b, t, G, W, np.random.default_rng(trial), max_live=(None if trial == 0 else 2))
+            assert np.array_equal(out, ref), (b, t, trial)
+        A = ref
+    T = A
+    assert np.all(np.triu(T, 2) == 0)
+
+
+def test_cycle_is_the_oracles():
+    # the emulation's numpy cycle reduces to the same tridiagonal as the
+    # symmetric oracle (up to rounding: different summation order)
+    import oracle
+    n, bw, tw = 30, 6, 2
+    rng = np.random.default_rng(5)
+    band = rng.standard_normal((n, bw + 1))
+    A = np.zeros((n, n))
+    for i in range(n):
+        for o in range(bw + 1):
+            if i + o < n:
+                A[i, i + o] = band[i, o]
+    for (b, t) in pass_list(bw, tw):
+        A = sequential(A, b, t)
+    d, e = oracle.sym_reduce(band, bw, tw)
+    assert np.allclose(np.diag(A), d, atol=1e-12) and np.allclose(np.abs(np.diag(A, 1)), np.abs(e), atol=1e-12)
+
+
+def test_emulation_detects_a_broken_rule():
+    # one half-cycle less of separation inside the groups gives wrong results
+    n, bw, tw, G = 40, 8, 3, 4
+    rng = np.random.default_rng(3)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    b, t = pass_list(bw, tw)[0]
+    ref = sequential(A, b, t)
+    W = sym_group_ring_rows(n, b, t, G)
+    bad = 0
+    for trial in range(6):
+        try:
+            out = emulate(A, b, t, G, W + 8, np.random.default_rng(trial), d=lag(b, t) - 1)
+        except (RuntimeError, AssertionError):
+            bad += 1
+            continue
+        bad += not np.array_equal(out, ref)
+    assert bad > 0
