@@ -202,10 +202,7 @@ bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
 // in LDS (else PERSISTENT); DEFAULT = GROUP where it fits.
 bb_status run_pass(void *work, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu, hipStream_t st) {
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
-  if (g.dtype == BB_F16) {  // half precision: the persistent scheduler only
-    if (tu.scheduler != BB_SCHED_DEFAULT && tu.scheduler != BB_SCHED_PERSISTENT) return BB_ERR_UNSUPPORTED;
-    return run_persistent_pass(work, g, p, tu, sync, st);
-  }
+  if (g.dtype == BB_F16 && tu.scheduler == BB_SCHED_STEP) return BB_ERR_UNSUPPORTED;  // no fp16 step kernel
   if (tu.scheduler == BB_SCHED_STEP) return run_step_pass(work, g, p, tu, st);
   if (tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP) {
     const GroupPlan gp = group_plan(g, p, tu.group_sweeps);

@@ -182,8 +182,8 @@ __device__ __forceinline__ Refl<T> house_from(T alpha, T sn) {
   if (h.nz) {
     const T nrm = sqrt_(fma_(alpha, alpha, sn));
     h.beta = (alpha >= T(0)) ? -nrm : nrm;
-    h.tau = (h.beta - alpha) / h.beta;
-    h.inv = T(1) / (alpha - h.beta);
+    h.tau = div_(h.beta - alpha, h.beta);
+    h.inv = div_(T(1), alpha - h.beta);
   }
   return h;
 }
@@ -803,6 +803,9 @@ hipError_t group_t(void *wband, const Geometry &g, int b, int t, int d, int64_t 
 template <typename T, int MAXM>
 hipError_t group_stride(void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
                         uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {  // half precision: the generic ring code only
+    return group_t<T, MAXM, 0>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  } else {
   if (sizeof(T) == 4 && g.stride == 100)
     return group_t<T, MAXM, 100>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
   if (sizeof(T) == 4 && g.stride == 68)
@@ -810,6 +813,7 @@ hipError_t group_stride(void *wband, const Geometry &g, int b, int t, int d, int
   if (sizeof(T) == 8 && g.stride == 34)
     return group_t<T, MAXM, 34>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
   return group_t<T, MAXM, 0>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  }
 }
 
 template <typename T>
@@ -856,6 +860,8 @@ hipError_t launch_sym_group(int maxm, void *wband, const SymGeometry &g, int b, 
 hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
                         int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
   if (g.dtype == 1) return group_dispatch<double>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  if (g.dtype == 2)
+    return group_dispatch<_Float16>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
   return group_dispatch<float>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
 }
 

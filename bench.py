@@ -20,8 +20,8 @@ Prints one JSON line:
                   on the headline shape and on the page's n = 4096, b = 32
                   one-pass shape: ms, effective GB/s, its cycle kernel's
                   roofline, and the symmetric oracle on the smaller shape
-  f16             the same reduction of the headline band in half precision
-                  (persistent scheduler): ms and effective GB/s
+  f16             the same reduction of the headline band in half precision:
+                  ms and effective GB/s
   cpu_threaded    the oracle's cycles with each pass's sweeps on all host
                   cores (at most 16), on the whole reduction when it fits the
                   time bound, else on its first pass
@@ -223,7 +223,7 @@ def measure_sym(bbm, torch, steps, stream, with_cpu):
 
 def measure_f16(bbm, torch, w, steps, stream):
     """The headline band reduced in half precision (fp16 storage and
-    arithmetic, persistent scheduler)."""
+    arithmetic, the default scheduler)."""
     band = torch.from_numpy(bb_inputs.make_band(w.n, w.bw, "f16", w.dist, w.seed)).to("cuda:0")
     work = bbm.workspace(w.n, w.bw, w.tw, band.dtype, band.device)
     info = bbm.bb_plan(w.n, w.bw, w.tw, bbm.BB_F16)
@@ -237,7 +237,8 @@ def measure_f16(bbm, torch, w, steps, stream):
     status = bbm.bb_device_status(work.data_ptr(), w.n, w.bw, w.tw, bbm.BB_F16, stream.cuda_stream)
     gbps = info.alg_bytes / (ms * 1e-3) / 1e9
     return {"workload": f"n{w.n}-bw{w.bw}-tw{w.tw}-f16-{w.dist}", "ms": round(ms, 3), "GBps": round(gbps, 2),
-            "alg_bytes": info.alg_bytes, "kernel": "k_persist<_Float16>, one launch per pass",
+            "alg_bytes": info.alg_bytes, "kernel": "k_group<_Float16> where the pass's LDS ring fits, "
+                                                 "else k_persist<_Float16>; one launch per pass",
             "device_status": bbm.bb_status_str(status),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 5),

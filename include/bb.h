@@ -42,7 +42,7 @@ extern "C" {
  * reduced-precision variant of the band -> bidiagonal reduction (page
  * "Accelerating Bidiagonalization of Banded Matrices through Memory-Aware
  * Bulge-Chasing on GPUs", the accuracy study run in FP64, FP32 and FP16):
- * bb_reduce and its staged entry points only, on the persistent scheduler;
+ * bb_reduce and its staged entry points only, on every scheduler but STEP;
  * each operation rounded once to fp16 (fma fused, sqrt and division
  * correctly rounded).  The symmetric reduction and bb_svals take BB_F32 and
  * BB_F64. */

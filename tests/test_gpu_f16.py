@@ -35,19 +35,28 @@ def test_launch_shapes_and_zero_rows():
     band = bb_inputs.make_band(n, bw, "f16", "uniform_zero_rows", seed=3)
     od, oe = oracle.reduce(band, bw, tw)
     for tun in (dict(max_blocks=1), dict(max_blocks=5, threads_per_block=64),
-                dict(scheduler=bbm.BB_SCHED_PERSISTENT)):
+                dict(scheduler=bbm.BB_SCHED_PERSISTENT), dict(scheduler=bbm.BB_SCHED_GROUP, group_sweeps=3),
+                dict(scheduler=bbm.BB_SCHED_GROUP, group_sweeps=6, max_blocks=2)):
         log(f"f16 launch shape {tun}")
         d, e = gpu_reduce(band, bw, tw, bbm.tuning(**tun))
         np.testing.assert_array_equal(d.view(np.uint16), od.view(np.uint16))
         np.testing.assert_array_equal(e.view(np.uint16), oe.view(np.uint16))
 
 
+@pytest.mark.parametrize("n,bw,tw", [(600, 32, 16), (300, 64, 16), (512, 16, 8)])
+def test_group_and_persistent_agree_to_the_bit(n, bw, tw):
+    band = bb_inputs.make_band(n, bw, "f16", "normal", seed=n)
+    log(f"f16 group vs persistent n={n} bw={bw} tw={tw}")
+    dg, eg, Wg, _ = gpu_reduce(band, bw, tw, bbm.tuning(scheduler=bbm.BB_SCHED_GROUP), return_band=True)
+    dp, ep, Wp, _ = gpu_reduce(band, bw, tw, bbm.tuning(scheduler=bbm.BB_SCHED_PERSISTENT), return_band=True)
+    np.testing.assert_array_equal(Wg.view(np.uint16), Wp.view(np.uint16))
+
+
 def test_unsupported_combinations():
     import torch
     band = torch.zeros((64, 9), dtype=torch.float16, device="cuda:0")
-    for sched in (bbm.BB_SCHED_STEP, bbm.BB_SCHED_GROUP):
-        with pytest.raises(bbm.BBError):
-            bbm.reduce(band, 8, 4, bbm.tuning(scheduler=sched))
+    with pytest.raises(bbm.BBError):
+        bbm.reduce(band, 8, 4, bbm.tuning(scheduler=bbm.BB_SCHED_STEP))
     with pytest.raises(bbm.BBError):
         bbm.sym_reduce(band, 8, 4)
     d = torch.ones(8, dtype=torch.float16, device="cuda:0")
