@@ -525,18 +525,30 @@ def _read_counter_csv(path, counter):
     return [(k, v) for (_, k, v) in rows]
 
 
+def is_cycle_kernel(name, dtype):
+    """The workload's cycle kernel in a profiler row: the general band's
+    k_group / k_persist / k_step in the workload's element type (not the
+    symmetric sweep groups, not the half-precision run)."""
+    ctype = {"f32": "float", "f64": "double", "f16": "_Float16"}[dtype]
+    for k in ("k_group<", "k_persist<", "k_step<"):
+        if k + ctype + "," in name:
+            return not name.split(k, 1)[1].split(">", 1)[0].endswith("true")
+    return False
+
+
 def ingest_counters(workload, fetch_csv, write_csv, copy_mib):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the cycle kernels, each
     scaled by what the same counter reads for the plain copy of copy_mib MiB
     (which moves exactly copy_mib MiB each way)."""
     if copy_mib <= 0:
         raise SystemExit("--copy-probe-mib is needed to scale the counters")
+    w = bb_inputs.WORKLOADS[workload]
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_probe_mib": copy_mib}
     total = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _read_counter_csv(path, name)
         copy = [v for (k, v) in rows if "copybuffer" in k.lower()]
-        cyc = [v for (k, v) in rows if "k_group" in k or "k_persist" in k or "k_step" in k]
+        cyc = [v for (k, v) in rows if is_cycle_kernel(k, w.dtype)]
         if not copy or not cyc:
             raise SystemExit(f"{path}: no copy-probe or cycle-kernel rows for {name}")
         factor = (copy_mib * 1024.0) / max(copy)  # KiB the copy moves / KiB counted
