@@ -391,6 +391,7 @@ bb_status bb_sym_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw
 bb_status bb_sym_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,
                              void *stream) {
   if (!valid_shape(n, bw, tw, dtype) || !work || !dst) return BB_ERR_ARG;
+  if (dtype == BB_F16) return BB_ERR_UNSUPPORTED;
   const bb::SymGeometry g = bb::make_sym_geometry(n, bw, tw, dtype);
   const size_t row = size_t(g.ld) * size_t(g.esize);
   return hip_status(hipMemcpy2DAsync(dst, row, work, size_t(g.stride) * size_t(g.esize), row, size_t(n),
@@ -399,6 +400,7 @@ bb_status bb_sym_export_band(const void *work, int64_t n, int32_t bw, int32_t tw
 
 bb_status bb_sym_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream) {
   if (!valid_shape(n, bw, tw, dtype) || !work) return BB_ERR_ARG;
+  if (dtype == BB_F16) return BB_ERR_UNSUPPORTED;
   const bb::SymGeometry g = bb::make_sym_geometry(n, bw, tw, dtype);
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return BB_ERR_HIP;
   uint32_t word = 0;

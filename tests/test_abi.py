@@ -173,3 +173,23 @@ def test_svals_validation_without_a_gpu():
     # one value: the deepest rounds, and the smallest tree that reaches the
     # same round count (55 halvings = 13 tree levels + 7 rounds of 6)
     assert bbm.bb_svals_split(1, 1) == (13, 6)
+
+
+def test_sym_and_f16_validation_without_a_gpu():
+    import ctypes
+    L = bbm.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    sz = ctypes.c_size_t(0)
+    # the symmetric reduction takes fp32 and fp64 only
+    assert L.bb_sym_workspace_bytes(100, 8, 4, 2, ctypes.byref(sz)) == 4
+    assert L.bb_sym_workspace_bytes(100, 8, 4, 0, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert L.bb_sym_reduce(fake, 9, 100, 8, 4, 2, fake, fake, fake, 1 << 30, None, None) == 4
+    assert L.bb_sym_export_band(fake, 100, 8, 4, 2, fake, None) == 4
+    # half precision is a valid dtype of the general reduction
+    info = bbm.bb_plan(100, 8, 4, bbm.BB_F16)
+    assert info.passes == 2
+    assert bbm.bb_workspace_bytes(100, 8, 4, bbm.BB_F16) < bbm.bb_workspace_bytes(100, 8, 4, bbm.BB_F32)
+    # STEP has no fp16 kernel: rejected before anything is enqueued
+    tun = bbm.tuning(scheduler=bbm.BB_SCHED_STEP)
+    ws = bbm.bb_workspace_bytes(100, 8, 4, bbm.BB_F16)
+    assert L.bb_run_pass(100, 8, 4, 2, 0, ctypes.c_void_p(1 << 20), ws, ctypes.byref(tun), None) == 4
