@@ -171,11 +171,12 @@ struct Ring {
 
 // The reflector of a half from the tail sum of squares sn = sum_{j>=1} x_j^2
 // (already accumulated in the contract's order) and alpha = x_0; nz false:
-// identity (zero tail).
+// identity (zero tail).  Every lane holds the same x (broadcast loads), so nz
+// is taken from the first lane and every branch on it is a scalar one.
 template <typename T>
 __device__ __forceinline__ Refl<T> house_from(T alpha, T sn) {
   Refl<T> h;
-  h.nz = sn != T(0);
+  h.nz = __builtin_amdgcn_readfirstlane(int(sn != T(0))) != 0;
   h.beta = alpha;
   h.tau = T(0);
   h.inv = T(0);
@@ -188,258 +189,338 @@ __device__ __forceinline__ Refl<T> house_from(T alpha, T sn) {
   return h;
 }
 
-// Row half of a cycle on the ring, one wave.  Row r's entries c..ch (x) give
-// the reflector; it is applied from the right to rows r+1..ch, one lane per
-// row: rows r+1+lane and (TWO) r+65+lane, whose dot products with x are
-// accumulated alongside the norm (neither depends on the reflector), so the
-// serial chains overlap.  Row r becomes (beta, 0, ..., 0), one element per
-// lane.  SC: compile-time row stride (0: the ring's runtime stride).
-//   sr: ring slot of row r; colr = c - r + sub (column c within row r);
-//   nr = ch - r rows below r.
+// Each half-cycle runs in two parts.  The first forms the reflector from the
+// entries that define it (row r at columns c..ch for a row half, column c at
+// rows c..ch for a column half; x[0] = alpha) and writes the pivot's final
+// values (beta, then zeros).  The second applies the reflector to the other
+// rows or columns.  For every half but a sweep's first, the defining entries
+// were last written by the sweep's own previous half, and no other sweep
+// touches them or the pivot until this half is done (the in-group lag keeps
+// the predecessor d halves ahead and the successor d halves behind), so the
+// first part runs right after the previous half is published, while the
+// sweep waits for its predecessor; only the second part is on the chain
+// between sweeps.
+template <typename T, int MAXM>
+struct HalfRefl {
+  Refl<T> h;
+  T x[MAXM];  // defining entries (x[0] unused after the reflector is formed)
+};
+
+// Row half, first part.  sr: ring slot of row r; colr = c - r + sub (column
+// c within row r); FULL: m == MAXM.
+template <typename T, int MAXM, bool FULL, int SC>
+__device__ __forceinline__ void ring_row_prep(const Ring<T> &A, int32_t sr, int32_t colr, int32_t m, int lane,
+                                              HalfRefl<T, MAXM> &P) {
+  const int32_t S = SC ? SC : A.S;
+  T *px = A.L + __umul24(sr, S) + colr;
+#pragma unroll
+  for (int j = 0; j < MAXM; ++j) P.x[j] = (FULL || j < m) ? px[j] : T(0);
+  T sn = T(0);
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j)
+    if (FULL || j < m) sn = fma_(P.x[j], P.x[j], sn);
+  P.h = house_from(P.x[0], sn);
+  if (lane < m) px[lane] = lane > 0 ? T(0) : P.h.beta;  // row r becomes (beta, 0, ..., 0); beta = alpha for a zero tail
+}
+
+// Row half, second part: the reflector applied from the right to rows
+// r+1..ch, one lane per row (rows r+1+lane and, TWO, r+65+lane; wider bands
+// loop), each row's dot product with x serial in j.  nr = ch - r.
 template <typename T, int MAXM, bool FULL, bool TWO, int SC>
-__device__ void ring_row_half(const Ring<T> &A, int32_t sr, int32_t colr, int32_t m, int32_t nr, int lane) {
+__device__ __forceinline__ void ring_row_apply(const Ring<T> &A, int32_t sr, int32_t colr, int32_t m, int32_t nr,
+                                               int lane, const HalfRefl<T, MAXM> &P) {
+  if (!P.h.nz) return;
   const int32_t S = SC ? SC : A.S;
   T *L = A.L;
-  T *px = L + sr * S + colr;
   const int32_t a0 = lane + 1, a1 = lane + 65;
   const bool h0 = a0 <= nr, h1 = a1 <= nr;
   const int32_t i0 = h0 ? a0 : nr, i1 = h1 ? a1 : nr;  // inactive lanes read row ch, store nothing
   int32_t s0 = sr + i0, s1 = sr + i1;
   s0 = s0 >= A.W ? s0 - A.W : s0;
   s1 = s1 >= A.W ? s1 - A.W : s1;
-  T *p0 = L + s0 * S + (colr - i0);
-  T *p1 = L + s1 * S + (colr - i1);
-  T x[MAXM], v0[MAXM], v1[MAXM];
+  T *p0 = L + __umul24(s0, S) + (colr - i0);
+  T *p1 = L + __umul24(s1, S) + (colr - i1);
+  T v0[MAXM], v1[MAXM], xv[MAXM];
 #pragma unroll
   for (int j = 0; j < MAXM; ++j) {
-    x[j] = (FULL || j < m) ? px[j] : T(0);
     v0[j] = (FULL || j < m) ? p0[j] : T(0);
     if (TWO) v1[j] = (FULL || j < m) ? p1[j] : T(0);
   }
-  T sn = T(0), d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j) xv[j] = P.x[j] * P.h.inv;  // the reflector's tail
+  T d0 = T(0), d1 = T(0);
 #pragma unroll
   for (int j = 1; j < MAXM; ++j)
     if (FULL || j < m) {
-      sn = fma_(x[j], x[j], sn);
-      d0 = fma_(v0[j], x[j], d0);
-      if (TWO) d1 = fma_(v1[j], x[j], d1);
+      d0 = fma_(v0[j], P.x[j], d0);
+      if (TWO) d1 = fma_(v1[j], P.x[j], d1);
     }
-  const Refl<T> h = house_from(x[0], sn);
-  if (h.nz) {
-    T xv[MAXM];
+  const T tw0 = P.h.tau * fma_(d0, P.h.inv, v0[0]);
+  if (h0) {
+    p0[0] = v0[0] - tw0;
 #pragma unroll
-    for (int j = 1; j < MAXM; ++j) xv[j] = x[j] * h.inv;
-    const T tw0 = h.tau * fma_(d0, h.inv, v0[0]);
-    if (h0) {
-      p0[0] = v0[0] - tw0;
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) p0[j] = fma_(-tw0, xv[j], v0[j]);
-    }
-    if (TWO && h1) {
-      const T tw1 = h.tau * fma_(d1, h.inv, v1[0]);
-      p1[0] = v1[0] - tw1;
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) p1[j] = fma_(-tw1, xv[j], v1[j]);
-    }
-    for (int32_t i = 129 + lane; i <= nr; i += 64) {  // bands wider than 128 rows
-      int32_t si = sr + i;
-      si = si >= A.W ? si - A.W : si;
-      T *p = L + si * S + (colr - i);
-      T v[MAXM];
-#pragma unroll
-      for (int j = 0; j < MAXM; ++j) v[j] = (FULL || j < m) ? p[j] : T(0);
-      T dd = T(0);
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) dd = fma_(v[j], x[j], dd);
-      const T tw = h.tau * fma_(dd, h.inv, v[0]);
-      p[0] = v[0] - tw;
-#pragma unroll
-      for (int j = 1; j < MAXM; ++j)
-        if (FULL || j < m) p[j] = fma_(-tw, xv[j], v[j]);
-    }
+    for (int j = 1; j < MAXM; ++j)
+      if (FULL || j < m) p0[j] = fma_(-tw0, xv[j], v0[j]);
   }
-  if (lane < m) {
-    if (lane > 0)
-      px[lane] = T(0);
-    else if (h.nz)
-      px[0] = h.beta;
+  if (TWO && h1) {
+    const T tw1 = P.h.tau * fma_(d1, P.h.inv, v1[0]);
+    p1[0] = v1[0] - tw1;
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j)
+      if (FULL || j < m) p1[j] = fma_(-tw1, xv[j], v1[j]);
+  }
+  for (int32_t i = 129 + lane; i <= nr; i += 64) {  // bands wider than 128 rows
+    int32_t si = sr + i;
+    si = si >= A.W ? si - A.W : si;
+    T *p = L + __umul24(si, S) + (colr - i);
+    T v[MAXM];
+#pragma unroll
+    for (int j = 0; j < MAXM; ++j) v[j] = (FULL || j < m) ? p[j] : T(0);
+    T dd = T(0);
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j)
+      if (FULL || j < m) dd = fma_(v[j], P.x[j], dd);
+    const T tw = P.h.tau * fma_(dd, P.h.inv, v[0]);
+    p[0] = v[0] - tw;
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j)
+      if (FULL || j < m) p[j] = fma_(-tw, xv[j], v[j]);
   }
 }
 
-// Column half on the ring, one wave.  Column c's entries in rows c..ch (y)
-// give the reflector; it is applied from the left to columns c+1..jend, one
-// lane per column (c+1+lane and, TWO, c+65+lane), dot products accumulated
-// alongside the norm.  Column c becomes (beta, 0, ..., 0), one element per
-// lane.  Element (c+i, c+jj) sits at base[off(i) + jj], base = (c, c),
-// off(i) = i*(S-1), less W*S for rows past the end of the ring (WRAP; rows
-// i >= iw).
-template <typename T, int MAXM, bool FULL, bool TWO, int SC, bool WRAP>
-__device__ __forceinline__ void ring_col_body(const Ring<T> &A, T *base, int32_t iw, int32_t m, int32_t nc,
-                                              int lane) {
+// Column half on the ring.  Element (c+i, c+jj) sits at base[off(i) + jj],
+// base = (c, c), off(i) = i*(S-1), less W*S for rows past the end of the
+// ring (WRAP; rows i >= iw).
+template <typename T, int MAXM, bool WRAP, int SC>
+__device__ __forceinline__ void col_offsets(const Ring<T> &A, int32_t iw, int32_t (&off)[MAXM]) {
   const int32_t S = SC ? SC : A.S;
-  const int32_t D = S - 1;
   const int32_t WS = A.W * S;
-  int32_t off[MAXM];
 #pragma unroll
-  for (int i = 0; i < MAXM; ++i) off[i] = i * D - ((WRAP && i >= iw) ? WS : 0);
+  for (int i = 0; i < MAXM; ++i) off[i] = i * (S - 1) - ((WRAP && i >= iw) ? WS : 0);
+}
+
+// Column half, first part: x = column c's entries in rows c..ch; column c
+// becomes (beta, 0, ..., 0) (beta = alpha for a zero tail).
+template <typename T, int MAXM, bool FULL, bool WRAP, int SC>
+__device__ __forceinline__ void ring_col_prep(const Ring<T> &A, T *base, int32_t iw, int32_t m, int lane,
+                                              HalfRefl<T, MAXM> &P) {
+  int32_t off[MAXM];
+  col_offsets<T, MAXM, WRAP, SC>(A, iw, off);
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) P.x[i] = (FULL || i < m) ? base[off[i]] : T(0);
+  T sn = T(0);
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i)
+    if (FULL || i < m) sn = fma_(P.x[i], P.x[i], sn);
+  P.h = house_from(P.x[0], sn);
+  if (lane < m) {
+    const int32_t S = SC ? SC : A.S;
+    const int32_t o = lane * (S - 1) - ((WRAP && lane >= iw) ? A.W * S : 0);
+    base[o] = lane > 0 ? T(0) : P.h.beta;
+  }
+}
+
+// Column half, second part: the reflector applied from the left to columns
+// c+1..jend, one lane per column (c+1+lane and, TWO, c+65+lane; wider bands
+// loop).  nc = jend - c.
+template <typename T, int MAXM, bool FULL, bool TWO, int SC, bool WRAP>
+__device__ __forceinline__ void ring_col_apply(const Ring<T> &A, T *base, int32_t iw, int32_t m, int32_t nc,
+                                               int lane, const HalfRefl<T, MAXM> &P) {
+  if (!P.h.nz) return;
+  int32_t off[MAXM];
+  col_offsets<T, MAXM, WRAP, SC>(A, iw, off);
   const int32_t a0 = lane + 1, a1 = lane + 65;
   const bool h0 = a0 <= nc, h1 = a1 <= nc;
   T *q0 = base + (h0 ? a0 : nc), *q1 = base + (h1 ? a1 : nc);
-  T y[MAXM], v0[MAXM], v1[MAXM];
+  T v0[MAXM], v1[MAXM], xv[MAXM];
 #pragma unroll
   for (int i = 0; i < MAXM; ++i) {
-    y[i] = (FULL || i < m) ? base[off[i]] : T(0);
     v0[i] = (FULL || i < m) ? q0[off[i]] : T(0);
     if (TWO) v1[i] = (FULL || i < m) ? q1[off[i]] : T(0);
   }
-  T sn = T(0), d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i) xv[i] = P.x[i] * P.h.inv;  // the reflector's tail
+  T d0 = T(0), d1 = T(0);
 #pragma unroll
   for (int i = 1; i < MAXM; ++i)
     if (FULL || i < m) {
-      sn = fma_(y[i], y[i], sn);
-      d0 = fma_(y[i], v0[i], d0);
-      if (TWO) d1 = fma_(y[i], v1[i], d1);
+      d0 = fma_(P.x[i], v0[i], d0);
+      if (TWO) d1 = fma_(P.x[i], v1[i], d1);
     }
-  const Refl<T> g = house_from(y[0], sn);
-  if (g.nz) {
-    T yv[MAXM];
+  const T tw0 = P.h.tau * fma_(d0, P.h.inv, v0[0]);
+  if (h0) {
+    q0[0] = v0[0] - tw0;
 #pragma unroll
-    for (int i = 1; i < MAXM; ++i) yv[i] = y[i] * g.inv;
-    const T tw0 = g.tau * fma_(d0, g.inv, v0[0]);
-    if (h0) {
-      q0[0] = v0[0] - tw0;
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) q0[off[i]] = fma_(-tw0, yv[i], v0[i]);
-    }
-    if (TWO && h1) {
-      const T tw1 = g.tau * fma_(d1, g.inv, v1[0]);
-      q1[0] = v1[0] - tw1;
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) q1[off[i]] = fma_(-tw1, yv[i], v1[i]);
-    }
-    for (int32_t jj = 129 + lane; jj <= nc; jj += 64) {  // bands wider than 128 columns
-      T *q = base + jj;
-      T v[MAXM];
-#pragma unroll
-      for (int i = 0; i < MAXM; ++i) v[i] = (FULL || i < m) ? q[off[i]] : T(0);
-      T dd = T(0);
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) dd = fma_(y[i], v[i], dd);
-      const T tw = g.tau * fma_(dd, g.inv, v[0]);
-      q[0] = v[0] - tw;
-#pragma unroll
-      for (int i = 1; i < MAXM; ++i)
-        if (FULL || i < m) q[off[i]] = fma_(-tw, yv[i], v[i]);
-    }
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) q0[off[i]] = fma_(-tw0, xv[i], v0[i]);
   }
-  if (lane < m) {
-    const int32_t o = lane * D - ((WRAP && lane >= iw) ? WS : 0);
-    base[o] = lane > 0 ? T(0) : (g.nz ? g.beta : y[0]);
+  if (TWO && h1) {
+    const T tw1 = P.h.tau * fma_(d1, P.h.inv, v1[0]);
+    q1[0] = v1[0] - tw1;
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) q1[off[i]] = fma_(-tw1, xv[i], v1[i]);
+  }
+  for (int32_t jj = 129 + lane; jj <= nc; jj += 64) {  // bands wider than 128 columns
+    T *q = base + jj;
+    T v[MAXM];
+#pragma unroll
+    for (int i = 0; i < MAXM; ++i) v[i] = (FULL || i < m) ? q[off[i]] : T(0);
+    T dd = T(0);
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) dd = fma_(P.x[i], v[i], dd);
+    const T tw = P.h.tau * fma_(dd, P.h.inv, v[0]);
+    q[0] = v[0] - tw;
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i)
+      if (FULL || i < m) q[off[i]] = fma_(-tw, xv[i], v[i]);
   }
 }
 
 // Row half with fewer than MAXM columns where the padding columns are not
-// known to be zero (tile widths below the register tile): out of line.
+// known to be zero (tile widths below the register tile): both parts, out of
+// line.
 template <typename T, int MAXM, int SC>
 __device__ __attribute__((noinline)) void ring_row_half_masked(const Ring<T> &A, int32_t sr, int32_t colr,
                                                                int32_t m, int32_t nr, int lane) {
-  ring_row_half<T, MAXM, false, true, SC>(A, sr, colr, m, nr, lane);
+  HalfRefl<T, MAXM> P;
+  ring_row_prep<T, MAXM, false, SC>(A, sr, colr, m, lane, P);
+  ring_row_apply<T, MAXM, false, true, SC>(A, sr, colr, m, nr, lane, P);
 }
 
-// The rare column halves, out of line so that the common one keeps its
-// registers: rows that wrap around the ring (about m/W of the halves) and
-// the truncated last cycle of a sweep (m < MAXM).
+// The rare column halves, both parts, out of line so that the common one
+// keeps its registers: rows that wrap around the ring (about m/W of the
+// halves) and the truncated last cycle of a sweep (m < MAXM).
 template <typename T, int MAXM, int SC>
 __device__ __attribute__((noinline)) void ring_col_half_rare(const Ring<T> &A, int32_t sc, int32_t m, int32_t nc,
                                                              int lane) {
   const int32_t S = SC ? SC : A.S;
-  T *base = A.L + sc * S + A.sub;
+  T *base = A.L + __umul24(sc, S) + A.sub;
   const int32_t iw = A.W - sc;  // rows c+i with i >= iw wrap to the start of the ring
+  HalfRefl<T, MAXM> P;
   if (m == MAXM) {
+    ring_col_prep<T, MAXM, true, true, SC>(A, base, iw, m, lane, P);
     if (nc > 64)
-      ring_col_body<T, MAXM, true, true, SC, true>(A, base, iw, m, nc, lane);
+      ring_col_apply<T, MAXM, true, true, SC, true>(A, base, iw, m, nc, lane, P);
     else
-      ring_col_body<T, MAXM, true, false, SC, true>(A, base, iw, m, nc, lane);
+      ring_col_apply<T, MAXM, true, false, SC, true>(A, base, iw, m, nc, lane, P);
   } else {
-    ring_col_body<T, MAXM, false, true, SC, true>(A, base, iw, m, nc, lane);
+    ring_col_prep<T, MAXM, false, true, SC>(A, base, iw, m, lane, P);
+    ring_col_apply<T, MAXM, false, true, SC, true>(A, base, iw, m, nc, lane, P);
   }
 }
 
-//   sc: ring slot of row c; nc = jend - c columns right of c.
-template <typename T, int MAXM, int SC>
-__device__ __forceinline__ void ring_col_half(const Ring<T> &A, int32_t sc, int32_t m, int32_t nc, int lane) {
-  const int32_t S = SC ? SC : A.S;
-  const int32_t iw = A.W - sc;  // rows c+i with i >= iw wrap to the start of the ring
-  if (m != MAXM || iw < MAXM) {
-    ring_col_half_rare<T, MAXM, SC>(A, sc, m, nc, lane);
-    return;
-  }
-  T *base = A.L + sc * S + A.sub;
-  if (nc > 64)
-    ring_col_body<T, MAXM, true, true, SC, false>(A, base, iw, m, nc, lane);
-  else
-    ring_col_body<T, MAXM, true, false, SC, false>(A, base, iw, m, nc, lane);
+// Whether a half takes the common path (full register tile, no wrap for a
+// column half), whose first part may run ahead of the waits.
+template <int MAXM>
+__device__ __forceinline__ bool row_common(int32_t m, int t) {
+  // With an exact register tile (MAXM = t+1) a truncated last cycle
+  // (m < MAXM) runs the full-width code: the entries it also reads lie past
+  // column n-1 but inside the row's stored range, hold +0, leave every sum
+  // and update unchanged to the bit, and get +0 written back.
+  return m == MAXM || MAXM == t + 1;
+}
+template <typename T, int MAXM>
+__device__ __forceinline__ bool col_common(const Ring<T> &A, int32_t sc, int32_t m) {
+  return m == MAXM && A.W - sc >= MAXM;
 }
 
 // One sweep of the group, run by one wave.  Cycle geometry and ring slots
 // advance incrementally (c by b per cycle, the slot of c likewise).
+//
+// Progress is published in steps: two per half-cycle done, plus one once the
+// next half's first part (reflector and pivot) is done ahead of its waits.
+// For b' <= 2 the second part of the predecessor's half q+d-1 touches
+// nothing that this sweep's half q, or the next sweep's half q-d, touches
+// (only its first part does), so half q waits for 2(q+d-1)+1 steps; for
+// b' >= 3 the two second parts overlap and half q waits for 2(q+d) steps.
+// Either way it waits for all 4 Kp steps once the predecessor has no half
+// q+d-1 left.
 template <typename T, int MAXM, int SC>
 __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, int t, int d, int32_t R, int j,
                             int lane, int64_t spin_limit, uint32_t *status, uint32_t *sync) {
+  const int32_t S = SC ? SC : A.S;
   const int32_t K = int32_t(cycles_of_dev(n, b, t, R));
   const int32_t Kp = j > 0 ? int32_t(cycles_of_dev(n, b, t, R - 1)) : 0;
   int32_t c = R + (b - t);
   int32_t sc = A.slot(c);
-  const int32_t sR = A.slot(R);
   int32_t known_pred = 0, known_rows = 0;
+  const bool mark = b - t <= 2;                   // publish the first-part step
+  const int32_t lag_steps = mark ? 2 * d - 1 : 2 * d;
   BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g);)
+  // Waits before half q (rows up to `hi` resident); false: abort.
+  auto wait_half = [&](int32_t q, int32_t hi) -> bool {
+    if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * q + lag_steps, 4 * Kp), ctl, spin_limit, status))
+      return false;
+    BB_P(pr.tick(0);)
+    if (!rows_wait(&ctl.loaded_hi, known_rows, hi + 1, ctl, spin_limit, status)) return false;
+    BB_P(pr.tick(1); if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2] = uint32_t(pr.mark);)
+    return true;
+  };
+  // Publishes half q done; the sweep's lowest row from then on is `fl`.
+  // The final count waits for the predecessor's.  False: abort.
+  auto publish = [&](int32_t q, int32_t fl) -> bool {
+    BB_P(pr.tick(2 + (q & 1));)
+    if (q + 1 == 2 * K && j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, 4 * Kp, ctl, spin_limit, status))
+      return false;
+    if (lane == 0)  // one release: the half's LDS writes are complete before either word moves
+      __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * (q + 1), fl), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    BB_P(pr.tick(4); pr.add(5, 1);
+         if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2 + 1] = uint32_t(pr.mark);)
+    return true;
+  };
+  // Publishes that the first part of half q (q halves done) is done.
+  auto publish_first = [&](int32_t q, int32_t fl) {
+    if (mark && lane == 0)  // release: the pivot's LDS writes are complete
+      __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * q + 1, fl), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
   for (int32_t k = 0; k < K; ++k) {
     const int32_t ch = min(c + t, n - 1);
     const int32_t m = ch - c + 1;
     const int32_t r = k == 0 ? R : c - b;
-    int32_t sr = sR;
-    if (k > 0) sr = sc - b < 0 ? sc - b + A.W : sc - b;
+    const int32_t sr = k == 0 ? A.slot(R) : (sc - b < 0 ? sc - b + A.W : sc - b);
     const int32_t jend = min(c + t + b, n - 1);
-    for (int h = 0; h < 2; ++h) {
-      const int32_t q = 2 * k + h;
-      if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(q + d, 2 * Kp), ctl, spin_limit, status)) return;
-      BB_P(pr.tick(0);)
-      if (!rows_wait(&ctl.loaded_hi, known_rows, ch + 1, ctl, spin_limit, status)) return;
-      BB_P(pr.tick(1); if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2] = uint32_t(pr.mark);)
-      if (h == 0) {
-        // With an exact register tile (MAXM = t+1) a truncated last cycle
-        // (m < MAXM) runs the full-width code: the entries it also reads lie
-        // past column n-1 but inside the row's stored range, hold +0, leave
-        // every sum and update unchanged to the bit, and get +0 written back.
-        const int32_t nr = ch - r, colr = c - r + A.sub;
-        if (m == MAXM || MAXM == t + 1) {
-          if (nr > 64)
-            ring_row_half<T, MAXM, true, true, SC>(A, sr, colr, MAXM, nr, lane);
-          else
-            ring_row_half<T, MAXM, true, false, SC>(A, sr, colr, MAXM, nr, lane);
-        } else {
-          ring_row_half_masked<T, MAXM, SC>(A, sr, colr, m, nr, lane);
-        }
-      } else {
-        ring_col_half<T, MAXM, SC>(A, sc, m, jend - c, lane);
-      }
-      BB_P(pr.tick(2 + h);)
-      // The next half (this cycle's column half, or the next cycle's row
-      // half) starts at row c; after the last half the sweep touches nothing.
-      const int32_t fl = q + 1 < 2 * K ? c : n;
-      if (q + 1 == 2 * K && j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, 2 * Kp, ctl, spin_limit, status))
-        return;
-      if (lane == 0)  // one release: the half's LDS writes are complete before either word moves
-        __hip_atomic_store(&ctl.sweep[j], sweep_word(q + 1, fl), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      BB_P(pr.tick(4); pr.add(5, 1);
-           if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2 + 1] = uint32_t(pr.mark);)
+    const int32_t nr = ch - r, colr = c - r + A.sub, nc = jend - c;
+    // Row half 2k.  Its reflector comes from row r: for k > 0 the sweep's
+    // previous column half left it final, so it is formed before the wait;
+    // the first one (row R) may still be updated by the predecessor.
+    HalfRefl<T, MAXM> Pr;
+    const bool row_fast = row_common<MAXM>(m, t);
+    if (k > 0 && row_fast) {
+      ring_row_prep<T, MAXM, true, SC>(A, sr, colr, MAXM, lane, Pr);
+      publish_first(2 * k, r);  // the floor since the previous half: row c - b = r
     }
+    if (!wait_half(2 * k, ch)) return;
+    if (row_fast) {
+      if (k == 0) ring_row_prep<T, MAXM, true, SC>(A, sr, colr, MAXM, lane, Pr);
+      if (nr > 64)
+        ring_row_apply<T, MAXM, true, true, SC>(A, sr, colr, MAXM, nr, lane, Pr);
+      else
+        ring_row_apply<T, MAXM, true, false, SC>(A, sr, colr, MAXM, nr, lane, Pr);
+    } else {
+      ring_row_half_masked<T, MAXM, SC>(A, sr, colr, m, nr, lane);
+    }
+    if (!publish(2 * k, c)) return;
+    // Column half 2k+1: its reflector (column c, final after the row half)
+    // is formed before the wait.
+    HalfRefl<T, MAXM> Pc;
+    T *base = A.L + __umul24(sc, S) + A.sub;
+    const bool col_fast = col_common<T, MAXM>(A, sc, m);
+    if (col_fast) {
+      ring_col_prep<T, MAXM, true, false, SC>(A, base, 0, MAXM, lane, Pc);
+      publish_first(2 * k + 1, c);
+    }
+    if (!wait_half(2 * k + 1, ch)) return;
+    if (col_fast) {
+      if (nc > 64)
+        ring_col_apply<T, MAXM, true, true, SC, false>(A, base, 0, MAXM, nc, lane, Pc);
+      else
+        ring_col_apply<T, MAXM, true, false, SC, false>(A, base, 0, MAXM, nc, lane, Pc);
+    } else {
+      ring_col_half_rare<T, MAXM, SC>(A, sc, m, nc, lane);
+    }
+    if (!publish(2 * k + 1, k + 1 < K ? c : n)) return;
     c += b;
     sc += b;
     while (sc >= A.W) sc -= A.W;
@@ -633,7 +714,12 @@ __device__ void ring_fill(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t 
 }
 
 // Writes rows [lo, hi) from their ring slots back to memory (agent-coherent
-// 16-byte stores).  Complete once vmcnt reaches zero.
+// 16-byte stores).  Complete once vmcnt reaches zero.  The LDS reads of a
+// round (up to kDrainChunks 16-byte chunks per lane) are all issued before
+// its stores, so the round waits for LDS once; lanes past the end of the run
+// repeat its last chunk (the same bytes to the same address), so no lane is
+// masked off.
+constexpr int kDrainChunks = 16;
 template <typename T>
 __device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t lo, int32_t hi, int lane) {
   const int32_t row_bytes = A.S * int32_t(sizeof(T));
@@ -642,9 +728,20 @@ __device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t
     const int32_t s = A.slot(lo);
     const int32_t run = min(hi - lo, A.W - s);
     const int32_t bytes = run * row_bytes;
-    for (int32_t off = lane * 16; off < bytes; off += 1024) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(base + s * row_bytes + off);
-      __builtin_amdgcn_raw_buffer_store_b128(v, mem, uint32_t(lo * row_bytes + off), 0, kSc1);
+    const unsigned char *src = base + s * row_bytes;
+    const uint32_t dst = uint32_t(lo * row_bytes);
+    for (int32_t off0 = 0; off0 < bytes; off0 += kDrainChunks * 1024) {
+      u32x4 v[kDrainChunks];
+      int32_t off[kDrainChunks];
+#pragma unroll
+      for (int u = 0; u < kDrainChunks; ++u) {
+        off[u] = min(off0 + u * 1024 + lane * 16, bytes - 16);
+        v[u] = *reinterpret_cast<const u32x4 *>(src + off[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kDrainChunks; ++u)
+        if (off0 + u * 1024 < bytes)  // wave-uniform: chunks of this round that hold any of the run
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], mem, dst + uint32_t(off[u]), 0, kSc1);
     }
     lo += run;
   }

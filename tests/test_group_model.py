@@ -51,38 +51,60 @@ def house(x):
     return beta, (beta - alpha) / beta, 1.0 / (alpha - beta)
 
 
-def do_half(rows, n, b, t, R, q):
-    """One half-cycle on a dict row -> dense row (modified in place)."""
+def prep_half(rows, n, b, t, R, q, write_pivot=False):
+    """First part of half q: the entries that form its reflector (row r at
+    columns c..ch, or column c at rows c..ch) and the reflector; with
+    write_pivot, also the pivot's final values (beta, then zeros)."""
+    h, r, c, ch, jend = half_geom(n, b, t, R, q)
+    x = rows[r][c:ch + 1].copy() if h == 0 else np.array([rows[i][c] for i in range(c, ch + 1)])
+    hh = house(x)
+    if write_pivot:
+        write_pivot_of(rows, n, b, t, R, q, hh)
+    return x, hh, write_pivot
+
+
+def write_pivot_of(rows, n, b, t, R, q, hh):
     h, r, c, ch, jend = half_geom(n, b, t, R, q)
     if h == 0:
-        x = rows[r][c:ch + 1].copy()
-        hh = house(x)
         if hh is not None:
-            beta, tau, inv = hh
-            v = x * inv
+            rows[r][c] = hh[0]
+        rows[r][c + 1:ch + 1] = 0.0
+    else:
+        if hh is not None:
+            rows[c][c] = hh[0]
+        for i in range(c + 1, ch + 1):
+            rows[i][c] = 0.0
+
+
+def apply_half(rows, n, b, t, R, q, prep):
+    """Second part of half q: the reflector applied to the other rows
+    (row half) or columns (column half), then the pivot unless prep wrote it."""
+    h, r, c, ch, jend = half_geom(n, b, t, R, q)
+    x, hh, pivot_done = prep
+    if hh is not None:
+        beta, tau, inv = hh
+        v = x * inv
+        if h == 0:
             for i in range(r + 1, ch + 1):
                 a = rows[i][c:ch + 1]
                 w = a[0] + float(np.dot(a[1:], x[1:])) * inv
                 a[0] -= tau * w
                 a[1:] -= tau * w * v[1:]
-            rows[r][c] = beta
-        rows[r][c + 1:ch + 1] = 0.0
-    else:
-        y = np.array([rows[i][c] for i in range(c, ch + 1)])
-        hh = house(y)
-        if hh is not None:
-            beta, tau, inv = hh
-            v = y * inv
+        else:
             for col in range(c + 1, jend + 1):
                 a = np.array([rows[i][col] for i in range(c, ch + 1)])
-                w = a[0] + float(np.dot(a[1:], y[1:])) * inv
+                w = a[0] + float(np.dot(a[1:], x[1:])) * inv
                 a[0] -= tau * w
                 a[1:] -= tau * w * v[1:]
                 for ii, i in enumerate(range(c, ch + 1)):
                     rows[i][col] = a[ii]
-            rows[c][c] = beta
-        for i in range(c + 1, ch + 1):
-            rows[i][c] = 0.0
+    if not pivot_done:
+        write_pivot_of(rows, n, b, t, R, q, hh)
+
+
+def do_half(rows, n, b, t, R, q):
+    """One half-cycle on a dict row -> dense row (modified in place)."""
+    apply_half(rows, n, b, t, R, q, prep_half(rows, n, b, t, R, q))
 
 
 def sequential(A, b, t):
@@ -130,17 +152,38 @@ class Group:
         self.Gg = min(G, ns - self.R0)
         self.K = [cycles_of_sweep(n, b, t, self.R0 + j) for j in range(self.Gg)]
         self.Kp = [cycles_of_sweep(n, b, t, self.R0 + j - 1) if j > 0 else 0 for j in range(self.Gg)]
-        self.prog = [0] * self.Gg          # published half-cycles
+        self.prog = [0] * self.Gg          # published steps (two per half)
         self.done = [0] * self.Gg          # executed half-cycles
         self.floor = [self.R0 + j for j in range(self.Gg)]
         self.loaded = self.written = self.R0
         self.X = 0
         self.lds = {}
+        self.prep = [None] * self.Gg       # reflector formed ahead of the wait (early modes)
 
 
-def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True):
-    n = A.shape[0]
+def lag_steps(b, t, marks):
+    """Progress a sweep's half q waits for, in steps of its predecessor (two
+    per half done, one more once the next half's first part is done): with
+    first-part marks, 2(q+d-1)+1 for b' <= 2 (the second part of the
+    predecessor's half q+d-1 touches nothing half q needs); else 2(q+d)."""
     d = lag(b, t)
+    return 2 * d - 1 if marks and b - t <= 2 else 2 * d
+
+
+def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True, early=0, first=1, steps=None,
+            all_marks=False):
+    """early: 0, every half formed and applied after its waits; 1, a sweep
+    forms the reflector of its next half (q >= 1) as soon as it has
+    published the previous one, before waiting for its predecessor; 2, as 1
+    and also writes that half's pivot (beta, zeros) then, and publishes that
+    first part as a step when b' <= 2 (the kernel's schedule).  first: the
+    first half formed early (1; 0 plants a mistake: half 0's row comes from
+    the predecessor, so it must wait).  steps: the wait of half q in
+    predecessor steps is 2q + steps (default lag_steps; a smaller value
+    plants a mistake).  all_marks: publish first-part steps for b' >= 3 too."""
+    n = A.shape[0]
+    ls = lag_steps(b, t, early == 2) if steps is None else steps
+    mark = early == 2 and (b - t <= 2 or all_marks)
     ns = max(n - (b - t) - 1, 0)
     mem = {i: A[i].copy() for i in range(n)}
     groups = [Group(g, G, ns, n, b, t) for g in range((ns + G - 1) // G)]
@@ -164,14 +207,17 @@ def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True):
         for gr in live:
             for j in range(gr.Gg):
                 q = gr.done[j]
-                if q == gr.prog[j] and q < 2 * gr.K[j]:   # ready to run half q
+                published = gr.prog[j] >= 2 * q      # half q-1 published (prog counts steps)
+                if early and published and first <= q < 2 * gr.K[j] and gr.prep[j] is None:
+                    actions.append(("prep", gr, j))       # no wait: the sweep's own rows
+                if published and q < 2 * gr.K[j] and (not early or q < first or gr.prep[j] is not None):
                     lo, hi = half_rows(n, b, t, gr.R0 + j, q)
-                    pred_ok = j == 0 or gr.prog[j - 1] >= min(q + d, 2 * gr.Kp[j])
+                    pred_ok = j == 0 or gr.prog[j - 1] >= min(2 * q + ls, 4 * gr.Kp[j])
                     if pred_ok and gr.loaded > hi:
                         actions.append(("half", gr, j))
-                elif gr.done[j] == gr.prog[j] + 1:         # executed, not yet published
+                elif not published:                       # executed, not yet published
                     final = gr.done[j] == 2 * gr.K[j]
-                    if not final or j == 0 or gr.prog[j - 1] >= 2 * gr.Kp[j]:
+                    if not final or j == 0 or gr.prog[j - 1] >= 4 * gr.Kp[j]:
                         actions.append(("publish", gr, j))
             dead = min(gr.floor) if gr.Gg else n
             if min(dead, gr.loaded) > gr.written:
@@ -189,12 +235,22 @@ def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True):
             lo, hi = half_rows(n, b, t, R, q)
             assert all(i in gr.lds for i in range(lo, hi + 1))
             assert lo >= gr.written   # never touches a row already handed on
-            do_half(gr.lds, n, b, t, R, q)
+            pr = gr.prep[j] if gr.prep[j] is not None else prep_half(gr.lds, n, b, t, R, q)
+            apply_half(gr.lds, n, b, t, R, q, pr)
+            gr.prep[j] = None
             gr.done[j] += 1
+        elif kind == "prep":
+            R, q = gr.R0 + j, gr.done[j]
+            h, r, c, ch, _ = half_geom(n, b, t, R, q)
+            lo, hi = (r, r) if h == 0 else (c, ch)    # the entries that form the reflector
+            assert all(i in gr.lds for i in range(lo, hi + 1)) and lo >= gr.written
+            gr.prep[j] = prep_half(gr.lds, n, b, t, R, q, write_pivot=(early == 2))
+            if mark:
+                gr.prog[j] = 2 * q + 1
         elif kind == "publish":
             q = gr.done[j]
             gr.floor[j] = half_geom(n, b, t, gr.R0 + j, q - 1)[2] if q < 2 * gr.K[j] else n
-            gr.prog[j] = q
+            gr.prog[j] = 2 * q
         elif kind == "writeback":
             wb = min(min(gr.floor), gr.loaded)
             for i in range(gr.written, wb):
@@ -215,15 +271,19 @@ SHAPES = [(40, 8, 3, 2), (40, 8, 3, 4), (48, 16, 15, 3), (50, 12, 4, 3), (45, 6,
           (60, 10, 2, 3), (30, 4, 2, 5), (33, 7, 6, 8), (24, 16, 5, 2)]
 
 
+@pytest.mark.parametrize("early", [0, 2])
 @pytest.mark.parametrize("n,bw,tw,G", SHAPES)
-def test_group_protocol_matches_sequential(n, bw, tw, G):
+def test_group_protocol_matches_sequential(n, bw, tw, G, early):
+    # early = 2 is the kernel's schedule: the next half's reflector and pivot
+    # are formed right after the sweep publishes, before it waits
     rng = np.random.default_rng(n * 100 + bw)
     A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
     for (b, t) in pass_list(bw, tw):
         ref = sequential(A, b, t)
         W = group_ring_rows(n, b, t, G)
         for trial in range(3):
-            out = emulate(A, b, t, G, W, np.random.default_rng(trial), max_live=(None if trial == 0 else 2))
+            out = emulate(A, b, t, G, W, np.random.default_rng(trial), max_live=(None if trial == 0 else 2),
+                          early=early)
             assert np.array_equal(out, ref), (b, t, trial)
         A = ref
 
@@ -245,4 +305,45 @@ def test_emulation_detects_a_broken_rule():
     W = group_ring_rows(n, b, t, G)
     bad = sum(not np.array_equal(emulate(A, b, t, G, W, np.random.default_rng(trial), wait_for_prev=False), ref)
               for trial in range(5))
+    assert bad > 0
+
+
+def test_emulation_detects_an_early_first_reflector():
+    # forming half 0's reflector before the wait (its row is the
+    # predecessor's output) gives wrong results
+    n, b, t, G = 40, 8, 3, 3
+    rng = np.random.default_rng(2)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), b))
+    ref = sequential(A, b, t)
+    W = group_ring_rows(n, b, t, G)
+    bad = 0
+    for trial in range(5):
+        try:
+            out = emulate(A, b, t, G, W, np.random.default_rng(trial), early=2, first=0)
+        except (RuntimeError, AssertionError):
+            bad += 1
+            continue
+        bad += not np.array_equal(out, ref)
+    assert bad > 0
+
+
+@pytest.mark.parametrize("n,bw,tw,G", [(48, 16, 15, 3), (40, 16, 14, 3), (40, 8, 3, 3), (50, 12, 4, 3)])
+def test_emulation_detects_a_short_wait(n, bw, tw, G):
+    # one step less than the kernel waits for (for b' <= 2: the predecessor's
+    # first part of half q+d-1 not yet done; for b' >= 3: its second part of
+    # half q+d-1 not yet done) gives wrong results
+    rng = np.random.default_rng(4)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    b, t = pass_list(bw, tw)[0]
+    ref = sequential(A, b, t)
+    W = group_ring_rows(n, b, t, G) + 8
+    bad = 0
+    for trial in range(6):
+        try:
+            out = emulate(A, b, t, G, W, np.random.default_rng(trial), early=2, all_marks=True,
+                          steps=lag_steps(b, t, True) - 1)
+        except (RuntimeError, AssertionError):
+            bad += 1
+            continue
+        bad += not np.array_equal(out, ref)
     assert bad > 0
