@@ -22,8 +22,10 @@
 //   * inside the group, sweep j starts half-cycle q once sweep j-1 has done
 //     min(q + d, all of its) half-cycles, and publishes its final count only
 //     after sweep j-1 has published its own (the rule of the persistent
-//     scheduler; d = 2, 3, 4 for b' >= 3, 2, 1).  Sweep 0 has no in-group
-//     predecessor: its inputs are whole rows, complete when loaded.
+//     scheduler; d = 2, 3, 4 for b' >= 3, 2, 1); for b' <= 2 a general sweep
+//     needs only the first part of the predecessor's half q+d-1 (see
+//     group_sweep).  Sweep 0 has no in-group predecessor: its inputs are
+//     whole rows, complete when loaded.
 //   * each compute wave publishes the lowest row it will still touch; rows
 //     below the minimum over the group are dead: the writer writes them back
 //     and publishes X_g = rows written (never above X_{g-1}: only loaded rows
@@ -52,7 +54,9 @@ struct GroupCtl {
   int32_t written;                   // rows [R0, written) written back; their slots are free
   int32_t abort_;                    // a wait expired: drain
   // per sweep j, published together by one 8-byte release store:
-  //   word 0: half-cycles completed; word 1: lowest row the sweep will still touch
+  //   word 0: progress (general sweeps: steps, two per half-cycle completed
+  //   plus one for a first part done ahead; symmetric sweeps: half-cycles
+  //   completed); word 1: lowest row the sweep will still touch
   uint64_t sweep[kGroupMaxSweeps];
 };
 
@@ -555,13 +559,13 @@ __device__ __forceinline__ void ring_seg_apply(T (&a)[MAXM], const T (&v)[MAXM],
     if (j < m) a[j] = fma_(-w, v[j], a[j]);
 }
 
+// Half A, first part: the reflector from pivot row p at columns c..ch (v in
+// registers, myv = v_lane for the block), and row p becomes (beta, 0, ..., 0).
 template <typename T, int MAXM>
-__device__ void ring_sym_half_a(const Ring<T> &A, int32_t c, int m, int32_t p, int lane, Refl<T> &h,
+__device__ void ring_sym_prep_a(const Ring<T> &A, int32_t c, int m, int32_t p, int lane, Refl<T> &h,
                                 T (&v)[MAXM], T &myv) {
   const int32_t S = A.S;
-  T *L = A.L;
-  const int32_t sp = A.slot(p);
-  T *px = L + sp * S + (c - p);
+  T *px = A.L + A.slot(p) * S + (c - p);
   T x[MAXM];
 #pragma unroll
   for (int j = 0; j < MAXM; ++j) x[j] = j < m ? px[j] : T(0);
@@ -575,25 +579,30 @@ __device__ void ring_sym_half_a(const Ring<T> &A, int32_t c, int m, int32_t p, i
     v[0] = T(1);
 #pragma unroll
     for (int j = 1; j < MAXM; ++j) v[j] = x[j] * h.inv;
-    if (lane < m) myv = lane == 0 ? T(1) : px[lane] * h.inv;  // v_lane
-    const int32_t nr = c - p - 1;  // rows p+1..c-1 at columns c..ch
-    for (int32_t q = lane; q < nr; q += 64) {
-      T *pr = L + A.next(sp, 1 + q) * S + (c - (p + 1 + q));
-      T a[MAXM];
-#pragma unroll
-      for (int j = 0; j < MAXM; ++j) a[j] = j < m ? pr[j] : T(0);
-      ring_seg_apply<T, MAXM>(a, v, h.tau, m);
-#pragma unroll
-      for (int j = 0; j < MAXM; ++j)
-        if (j < m) pr[j] = a[j];
-    }
+    if (lane < m) myv = lane == 0 ? T(1) : px[lane] * h.inv;  // v_lane (read before the pivot write below)
   }
-  if (lane < m) {
-    if (lane == 0) {
-      if (h.nz) px[0] = h.beta;
-    } else {
-      px[lane] = T(0);
-    }
+  if (lane < m) px[lane] = lane > 0 ? T(0) : h.beta;  // beta = alpha for a zero tail
+}
+
+// Half A, second part: the reflector applied to the row segments of rows
+// p+1..c-1 at columns c..ch, one lane each, in rounds of 64.
+template <typename T, int MAXM>
+__device__ void ring_sym_apply_a(const Ring<T> &A, int32_t c, int m, int32_t p, int lane, const Refl<T> &h,
+                                 const T (&v)[MAXM]) {
+  if (!h.nz) return;
+  const int32_t S = A.S;
+  T *L = A.L;
+  const int32_t sp = A.slot(p);
+  const int32_t nr = c - p - 1;  // rows p+1..c-1 at columns c..ch
+  for (int32_t q = lane; q < nr; q += 64) {
+    T *pr = L + A.next(sp, 1 + q) * S + (c - (p + 1 + q));
+    T a[MAXM];
+#pragma unroll
+    for (int j = 0; j < MAXM; ++j) a[j] = j < m ? pr[j] : T(0);
+    ring_seg_apply<T, MAXM>(a, v, h.tau, m);
+#pragma unroll
+    for (int j = 0; j < MAXM; ++j)
+      if (j < m) pr[j] = a[j];
   }
 }
 
@@ -659,7 +668,10 @@ __device__ void ring_sym_half_b(const Ring<T> &A, T *ys, int32_t n, int b, int32
 // previous sweep of the group has done min(q + d, all) halves and until its
 // rows are loaded; the final count waits for the predecessor's final count.
 // Floors: after half A the sweep still touches rows from c, after half B
-// from the next pivot row (c again).
+// from the next pivot row (c again).  Half A's first part (reflector and
+// pivot) runs before its wait for every cycle but the first: its pivot row
+// c - b was last written by the sweep's own half B of the previous cycle, and
+// no other sweep touches it until this half A is done.
 template <typename T, int MAXM>
 __device__ void sym_group_sweep(const Ring<T> &A, GroupCtl &ctl, T *ys, int32_t n, int b, int t, int d, int32_t R,
                                 int j, int lane, int64_t spin_limit, uint32_t *status) {
@@ -673,9 +685,11 @@ __device__ void sym_group_sweep(const Ring<T> &A, GroupCtl &ctl, T *ys, int32_t 
     const int32_t p = k == 0 ? R : c - b;
     Refl<T> h;
     T v[MAXM], myv;
+    if (k > 0) ring_sym_prep_a<T, MAXM>(A, c, m, p, lane, h, v, myv);
     if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * k + d, 2 * Kp), ctl, spin_limit, status)) return;
     if (!rows_wait(&ctl.loaded_hi, known_rows, c, ctl, spin_limit, status)) return;
-    ring_sym_half_a<T, MAXM>(A, c, m, p, lane, h, v, myv);
+    if (k == 0) ring_sym_prep_a<T, MAXM>(A, c, m, p, lane, h, v, myv);
+    ring_sym_apply_a<T, MAXM>(A, c, m, p, lane, h, v);
     if (lane == 0)
       __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * k + 1, c), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * k + 1 + d, 2 * Kp), ctl, spin_limit, status))

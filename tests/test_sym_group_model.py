@@ -52,30 +52,42 @@ def half_floor(n, b, t, R, q, K):
     return p if q % 2 == 0 else c
 
 
-def do_half(rows, refl, n, b, t, R, q):
+def prep_a(rows, n, b, t, R, q):
+    """First part of half A (q even): the reflector from pivot row p at
+    columns c..ch, and the pivot's final values (beta, then zeros)."""
+    c, ch, p = cyc_geom(n, b, t, R, q // 2)
+    x = rows[p][c:ch + 1].copy()
+    s = float(np.dot(x[1:], x[1:]))
+    refl = None
+    if s != 0.0:
+        alpha = x[0]
+        nrm = np.sqrt(alpha * alpha + s)
+        beta = -nrm if alpha >= 0 else nrm
+        tau = (beta - alpha) / beta
+        v = x / (alpha - beta)
+        v[0] = 1.0
+        refl = (tau, v)
+        rows[p][c] = beta
+    rows[p][c + 1:ch + 1] = 0.0
+    return refl
+
+
+def do_half(rows, refl, n, b, t, R, q, pre=False):
     """Half q of sweep R on dense upper rows; refl carries v and tau from
-    half 2k to half 2k+1 (as the wave's registers do)."""
+    half 2k to half 2k+1 (as the wave's registers do).  pre: half A's first
+    part (prep_a) has already run and refl[R] holds its result."""
     c, ch, p = cyc_geom(n, b, t, R, q // 2)
     m = ch - c + 1
     if q % 2 == 0:
-        x = rows[p][c:ch + 1].copy()
-        s = float(np.dot(x[1:], x[1:]))
-        refl[R] = None
-        if s != 0.0:
-            alpha = x[0]
-            nrm = np.sqrt(alpha * alpha + s)
-            beta = -nrm if alpha >= 0 else nrm
-            tau = (beta - alpha) / beta
-            v = x / (alpha - beta)
-            v[0] = 1.0
-            refl[R] = (tau, v)
+        if not pre:
+            refl[R] = prep_a(rows, n, b, t, R, q)
+        if refl[R] is not None:
+            tau, v = refl[R]
             for i in range(p + 1, c):
                 a = rows[i][c:ch + 1]
                 w = tau * (a[0] + float(np.dot(a[1:], v[1:])))
                 a[0] -= w
                 a[1:] -= w * v[1:]
-            rows[p][c] = beta
-        rows[p][c + 1:ch + 1] = 0.0
         return
     if refl[R] is None:
         return
@@ -144,9 +156,14 @@ class Group:
         self.loaded = self.written = self.R0
         self.X = 0
         self.lds = {}
+        self.pre = [False] * self.Gg
 
 
-def emulate(A, b, t, G, W, rng, max_live=None, d=None):
+def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2):
+    """early: a sweep runs half A's first part (reflector and pivot) as soon
+    as it has published the half before it, ahead of its waits (the kernel's
+    schedule), for every half A from half `first` on (2; 0 plants a mistake:
+    half 0's pivot row comes from the predecessor)."""
     n = A.shape[0]
     L = lag(b, t) if d is None else d   # half-cycles
     ns = max(n - (b - t) - 1, 0)
@@ -165,7 +182,9 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None):
             xprev = n if gr.g == 0 else groups[gr.g - 1].X
             for j in range(gr.Gg):
                 q = gr.done[j]
-                if q == gr.prog[j] and q < gr.K[j]:
+                if early and q == gr.prog[j] and q % 2 == 0 and first <= q < gr.K[j] and not gr.pre[j]:
+                    acts.append(("prep", gr, j))
+                if q == gr.prog[j] and q < gr.K[j] and (not early or q % 2 or q < first or gr.pre[j]):
                     lo, hi = half_rows(n, b, t, gr.R0 + j, q)
                     pred_ok = j == 0 or gr.prog[j - 1] >= min(q + L, gr.Kp[j])
                     if pred_ok and gr.loaded > hi:
@@ -189,8 +208,15 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None):
             R, q = gr.R0 + j, gr.done[j]
             lo, hi = half_rows(n, b, t, R, q)
             assert all(i in gr.lds for i in range(lo, hi + 1)) and lo >= gr.written
-            do_half(gr.lds, gr.refl, n, b, t, R, q)
+            do_half(gr.lds, gr.refl, n, b, t, R, q, pre=gr.pre[j])
+            gr.pre[j] = False
             gr.done[j] += 1
+        elif kind == "prep":
+            R, q = gr.R0 + j, gr.done[j]
+            c, ch, p = cyc_geom(n, b, t, R, q // 2)
+            assert p in gr.lds and p >= gr.written
+            gr.refl[R] = prep_a(gr.lds, n, b, t, R, q)
+            gr.pre[j] = True
         elif kind == "publish":
             q = gr.done[j]
             gr.floor[j] = half_floor(n, b, t, gr.R0 + j, q, gr.K[j] // 2)
@@ -214,15 +240,17 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None):
 SHAPES = [(40, 8, 3, 2), (40, 8, 3, 3), (36, 6, 5, 3), (45, 6, 2, 4), (30, 4, 1, 3), (33, 7, 6, 5), (50, 10, 4, 2)]
 
 
+@pytest.mark.parametrize("early", [False, True])
 @pytest.mark.parametrize("n,bw,tw,G", SHAPES)
-def test_sym_group_protocol_matches_sequential(n, bw, tw, G):
+def test_sym_group_protocol_matches_sequential(n, bw, tw, G, early):
     rng = np.random.default_rng(n * 10 + bw)
     A = np.triu(np.tril(rng.standard_normal((n, n)), bw))   # upper rows of a symmetric band
     for (b, t) in pass_list(bw, tw):
         ref = sequential(A, b, t)
         W = sym_group_ring_rows(n, b, t, G)
         for trial in range(3):
-            out = emulate(A, b, t, G, W, np.random.default_rng(trial), max_live=(None if trial == 0 else 2))
+            out = emulate(A, b, t, G, W, np.random.default_rng(trial), max_live=(None if trial == 0 else 2),
+                          early=early)
             assert np.array_equal(out, ref), (b, t, trial)
         A = ref
     T = A
@@ -259,6 +287,26 @@ def test_emulation_detects_a_broken_rule():
     for trial in range(6):
         try:
             out = emulate(A, b, t, G, W + 8, np.random.default_rng(trial), d=lag(b, t) - 1)
+        except (RuntimeError, AssertionError):
+            bad += 1
+            continue
+        bad += not np.array_equal(out, ref)
+    assert bad > 0
+
+
+def test_emulation_detects_an_early_first_pivot():
+    # forming half 0's reflector before the wait (its pivot row R is still
+    # updated by the predecessor) gives wrong results
+    n, bw, tw, G = 40, 8, 3, 3
+    rng = np.random.default_rng(7)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    b, t = pass_list(bw, tw)[0]
+    ref = sequential(A, b, t)
+    W = sym_group_ring_rows(n, b, t, G)
+    bad = 0
+    for trial in range(6):
+        try:
+            out = emulate(A, b, t, G, W, np.random.default_rng(trial), early=True, first=0)
         except (RuntimeError, AssertionError):
             bad += 1
             continue
