@@ -54,9 +54,8 @@ struct GroupCtl {
   int32_t written;                   // rows [R0, written) written back; their slots are free
   int32_t abort_;                    // a wait expired: drain
   // per sweep j, published together by one 8-byte release store:
-  //   word 0: progress (general sweeps: steps, two per half-cycle completed
-  //   plus one for a first part done ahead; symmetric sweeps: half-cycles
-  //   completed); word 1: lowest row the sweep will still touch
+  //   word 0: progress in steps, two per half-cycle completed plus one for a
+  //   first part done ahead; word 1: lowest row the sweep will still touch
   uint64_t sweep[kGroupMaxSweeps];
 };
 
@@ -664,19 +663,25 @@ __device__ void ring_sym_half_b(const Ring<T> &A, T *ys, int32_t n, int b, int32
   }
 }
 
-// One symmetric sweep of the group, run by one wave: half q waits until the
-// previous sweep of the group has done min(q + d, all) halves and until its
-// rows are loaded; the final count waits for the predecessor's final count.
+// One symmetric sweep of the group, run by one wave.  Progress is published
+// in steps as for the general sweeps: two per half done, plus one once half
+// A's first part (reflector and pivot) is done ahead of its wait, which for
+// b' <= 2 is all the next sweep's half q needs of the predecessor's half
+// q+d-1 when that is a half A; so half q waits for min(2(q+d)-1, all) steps
+// of the predecessor when b' <= 2, else min(2(q+d), all), and until its rows
+// are loaded; the final count waits for the predecessor's final count.
 // Floors: after half A the sweep still touches rows from c, after half B
-// from the next pivot row (c again).  Half A's first part (reflector and
-// pivot) runs before its wait for every cycle but the first: its pivot row
-// c - b was last written by the sweep's own half B of the previous cycle, and
-// no other sweep touches it until this half A is done.
+// from the next pivot row (c again).  Half A's first part runs before its
+// wait for every cycle but the first: its pivot row c - b was last written
+// by the sweep's own half B of the previous cycle, and no other sweep
+// touches it until this half A is done.
 template <typename T, int MAXM>
 __device__ void sym_group_sweep(const Ring<T> &A, GroupCtl &ctl, T *ys, int32_t n, int b, int t, int d, int32_t R,
                                 int j, int lane, int64_t spin_limit, uint32_t *status) {
   const int32_t K = int32_t(cycles_of_dev(n, b, t, R));
   const int32_t Kp = j > 0 ? int32_t(cycles_of_dev(n, b, t, R - 1)) : 0;
+  const bool mark = b - t <= 2;
+  const int32_t lag_steps = mark ? 2 * d - 1 : 2 * d;
   int32_t known_pred = 0, known_rows = 0;
   for (int32_t k = 0; k < K; ++k) {
     const int32_t c = R + (b - t) + k * b;
@@ -685,20 +690,26 @@ __device__ void sym_group_sweep(const Ring<T> &A, GroupCtl &ctl, T *ys, int32_t 
     const int32_t p = k == 0 ? R : c - b;
     Refl<T> h;
     T v[MAXM], myv;
-    if (k > 0) ring_sym_prep_a<T, MAXM>(A, c, m, p, lane, h, v, myv);
-    if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * k + d, 2 * Kp), ctl, spin_limit, status)) return;
+    if (k > 0) {
+      ring_sym_prep_a<T, MAXM>(A, c, m, p, lane, h, v, myv);
+      if (mark && lane == 0)  // release: the pivot's LDS writes are complete
+        __hip_atomic_store(&ctl.sweep[j], sweep_word(4 * k + 1, p), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(4 * k + lag_steps, 4 * Kp), ctl, spin_limit, status))
+      return;
     if (!rows_wait(&ctl.loaded_hi, known_rows, c, ctl, spin_limit, status)) return;
     if (k == 0) ring_sym_prep_a<T, MAXM>(A, c, m, p, lane, h, v, myv);
     ring_sym_apply_a<T, MAXM>(A, c, m, p, lane, h, v);
     if (lane == 0)
-      __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * k + 1, c), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * k + 1 + d, 2 * Kp), ctl, spin_limit, status))
+      __hip_atomic_store(&ctl.sweep[j], sweep_word(4 * k + 2, c), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (j > 0 &&
+        !prog_wait(&ctl.sweep[j - 1], known_pred, min(4 * k + 2 + lag_steps, 4 * Kp), ctl, spin_limit, status))
       return;
     if (!rows_wait(&ctl.loaded_hi, known_rows, ch + 1, ctl, spin_limit, status)) return;
     ring_sym_half_b<T, MAXM>(A, ys, n, b, c, m, lane, h, v, myv);
-    if (k + 1 == K && j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, 2 * Kp, ctl, spin_limit, status)) return;
+    if (k + 1 == K && j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, 4 * Kp, ctl, spin_limit, status)) return;
     if (lane == 0)
-      __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * k + 2, k + 1 < K ? c : n), __ATOMIC_RELEASE,
+      __hip_atomic_store(&ctl.sweep[j], sweep_word(4 * k + 4, k + 1 < K ? c : n), __ATOMIC_RELEASE,
                          __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }

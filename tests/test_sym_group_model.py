@@ -157,15 +157,22 @@ class Group:
         self.X = 0
         self.lds = {}
         self.pre = [False] * self.Gg
+        self.st = [0] * self.Gg          # published steps
 
 
-def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2):
+def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2, all_marks=False, steps=None):
     """early: a sweep runs half A's first part (reflector and pivot) as soon
     as it has published the half before it, ahead of its waits (the kernel's
     schedule), for every half A from half `first` on (2; 0 plants a mistake:
-    half 0's pivot row comes from the predecessor)."""
+    half 0's pivot row comes from the predecessor), and for b' <= 2 (or every
+    b' with all_marks) publishes that first part as a step.  Progress counts
+    steps, two per half; half q waits for min(2q + steps, all) steps of the
+    predecessor, steps = 2d - 1 with first-part steps, else 2d (d: the lag
+    in halves, default lag(b, t))."""
     n = A.shape[0]
     L = lag(b, t) if d is None else d   # half-cycles
+    mark = early and (b - t <= 2 or all_marks)
+    LS = (2 * L - 1 if mark else 2 * L) if steps is None else steps
     ns = max(n - (b - t) - 1, 0)
     mem = {i: A[i].copy() for i in range(n)}
     groups = [Group(g, G, ns, n, b, t) for g in range((ns + G - 1) // G)]
@@ -186,12 +193,12 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2):
                     acts.append(("prep", gr, j))
                 if q == gr.prog[j] and q < gr.K[j] and (not early or q % 2 or q < first or gr.pre[j]):
                     lo, hi = half_rows(n, b, t, gr.R0 + j, q)
-                    pred_ok = j == 0 or gr.prog[j - 1] >= min(q + L, gr.Kp[j])
+                    pred_ok = j == 0 or gr.st[j - 1] >= min(2 * q + LS, 2 * gr.Kp[j])
                     if pred_ok and gr.loaded > hi:
                         acts.append(("cycle", gr, j))
                 elif gr.done[j] == gr.prog[j] + 1:
                     final = gr.done[j] == gr.K[j]
-                    if not final or j == 0 or gr.prog[j - 1] >= gr.Kp[j]:
+                    if not final or j == 0 or gr.st[j - 1] >= 2 * gr.Kp[j]:
                         acts.append(("publish", gr, j))
             dead = min(gr.floor) if gr.Gg else n
             if min(dead, gr.loaded) > gr.written:
@@ -217,10 +224,13 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2):
             assert p in gr.lds and p >= gr.written
             gr.refl[R] = prep_a(gr.lds, n, b, t, R, q)
             gr.pre[j] = True
+            if mark:
+                gr.st[j] = 2 * q + 1
         elif kind == "publish":
             q = gr.done[j]
             gr.floor[j] = half_floor(n, b, t, gr.R0 + j, q, gr.K[j] // 2)
             gr.prog[j] = q
+            gr.st[j] = 2 * q
         elif kind == "writeback":
             wb = min(min(gr.floor), gr.loaded)
             for i in range(gr.written, wb):
@@ -307,6 +317,27 @@ def test_emulation_detects_an_early_first_pivot():
     for trial in range(6):
         try:
             out = emulate(A, b, t, G, W, np.random.default_rng(trial), early=True, first=0)
+        except (RuntimeError, AssertionError):
+            bad += 1
+            continue
+        bad += not np.array_equal(out, ref)
+    assert bad > 0
+
+
+@pytest.mark.parametrize("n,bw,tw,G", [(40, 16, 15, 3), (48, 16, 14, 3), (40, 8, 3, 3), (50, 10, 4, 2)])
+def test_emulation_detects_a_short_wait(n, bw, tw, G):
+    # one step less than the kernel waits for gives wrong results (first-part
+    # steps published for every b', to show that b' >= 3 must not use them)
+    rng = np.random.default_rng(9)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    b, t = pass_list(bw, tw)[0]
+    ref = sequential(A, b, t)
+    W = sym_group_ring_rows(n, b, t, G) + 8
+    ls = 2 * lag(b, t) - 1 if b - t <= 2 else 2 * lag(b, t)
+    bad = 0
+    for trial in range(6):
+        try:
+            out = emulate(A, b, t, G, W, np.random.default_rng(trial), early=True, all_marks=True, steps=ls - 1)
         except (RuntimeError, AssertionError):
             bad += 1
             continue
