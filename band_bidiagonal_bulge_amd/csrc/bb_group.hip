@@ -22,10 +22,10 @@
 //   * inside the group, sweep j starts half-cycle q once sweep j-1 has done
 //     min(q + d, all of its) half-cycles, and publishes its final count only
 //     after sweep j-1 has published its own (the rule of the persistent
-//     scheduler; d = 2, 3, 4 for b' >= 3, 2, 1); for b' <= 2 a general sweep
-//     needs only the first part of the predecessor's half q+d-1 (see
-//     group_sweep).  Sweep 0 has no in-group predecessor: its inputs are
-//     whole rows, complete when loaded.
+//     scheduler; d = 2, 3, 4 for b' >= 3, 2, 1); for b' <= 2 a sweep needs
+//     only the first part of the predecessor's half q+d-1 (see group_sweep
+//     and sym_group_sweep).  Sweep 0 has no in-group predecessor: its inputs
+//     are whole rows, complete when loaded.
 //   * each compute wave publishes the lowest row it will still touch; rows
 //     below the minimum over the group are dead: the writer writes them back
 //     and publishes X_g = rows written (never above X_{g-1}: only loaded rows
@@ -920,12 +920,14 @@ hipError_t group_t(void *wband, const Geometry &g, int b, int t, int d, int64_t 
 }
 
 // Row strides with a compile-time specialisation (the working-band strides
-// of BW 64 / TW 16 and BW 32 / TW 16 in fp32, BW 16 / TW 8 in fp64); any
-// other stride runs the generic ring code.
+// of BW 64 / TW 16 and BW 32 / TW 16 in fp32, BW 16 / TW 8 in fp64, BW 64 /
+// TW 16 in fp16); any other stride runs the generic ring code.
 template <typename T, int MAXM>
 hipError_t group_stride(void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
                         uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
-  if constexpr (sizeof(T) == 2) {  // half precision: the generic ring code only
+  if constexpr (sizeof(T) == 2) {  // half precision: the headline band's stride, else the generic ring code
+    if (g.stride == 104)
+      return group_t<T, MAXM, 104>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
     return group_t<T, MAXM, 0>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
   } else {
   if (sizeof(T) == 4 && g.stride == 100)
