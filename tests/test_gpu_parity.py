@@ -23,7 +23,8 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 # (n, bw, tw, dtype, dist): several tiles, ragged tails, every register tile
-# size (t+1 = 9, 17, 33, 65), single-cycle sweeps, TW >= BW, one pass.
+# size (t+1 = 9, 17, 33, 65), single-cycle sweeps, TW >= BW, one pass, and
+# passes with b' = 1, 2 and >= 3 (each a different wait between sweeps).
 SMALL = [
     (512, 16, 8, "f64", "normal"),
     (1000, 32, 16, "f32", "normal"),
@@ -37,6 +38,8 @@ SMALL = [
     (40, 39, 13, "f64", "normal"),
     (17, 16, 5, "f32", "normal"),
     (500, 256, 32, "f32", "uniform_zero_rows"),
+    (500, 18, 16, "f32", "normal"),   # a b' = 2 pass (18 -> 2), then 2 -> 1
+    (400, 12, 10, "f64", "normal"),   # the same in fp64 (12 -> 2 -> 1)
 ]
 
 

@@ -57,6 +57,8 @@ SMALL = [
     (64, 2, 1, "f64", "normal"),
     (3, 2, 1, "f32", "normal"),
     (1, 0, 1, "f64", "normal"),
+    (500, 18, 16, "f32", "normal"),   # a b' = 2 pass (18 -> 2), then 2 -> 1
+    (400, 12, 10, "f64", "normal"),   # the same in fp64 (12 -> 2 -> 1)
 ]
 
 
