@@ -792,12 +792,21 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
   int64_t idle = 0;
   BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g); int it_no = 0;)
   for (;;) {
-    if (lds_load(&ctl.abort_)) return;
+    // One LDS access per word, all in flight together (lane j reads sweep j's
+    // word), then one acquire: the rows below every floor are then visible.
+    const int32_t ab = __hip_atomic_load(&ctl.abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int32_t lh = __hip_atomic_load(&ctl.loaded_hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t w = lane < Gg ? __hip_atomic_load(&ctl.sweep[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                 : sweep_word(0, n);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (ab) return;
+    const int32_t fl = sweep_floor(w);
     int32_t dead = n;
-    for (int j = 0; j < Gg; ++j) dead = min(dead, sweep_floor(lds_load64(&ctl.sweep[j])));
+#pragma unroll
+    for (int j = 0; j < kGroupMaxSweeps; ++j) dead = min(dead, __builtin_amdgcn_readlane(fl, j));
     // write back in batches, publishing after each: the next group's first
     // sweep needs the lowest released rows first
-    const int32_t wb = min(min(dead, lds_load(&ctl.loaded_hi)), written + kDrainBatchRows);
+    const int32_t wb = min(min(dead, lh), written + kDrainBatchRows);
     if (wb > written) {
       BB_P(const uint32_t t_a = uint32_t(wall_clock64());)
       ring_drain(A, mem, written, wb, lane);
@@ -831,9 +840,13 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
   int64_t idle = 0;
   BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g); int it_no = 0;)
   for (;;) {
-    if (lds_load(&ctl.abort_)) return;
+    // the three words are read together, then one acquire
     if (xprev < n) xprev = int32_t(__hip_atomic_load(xprev_line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    const int32_t lim = min(min(xprev, lds_load(&ctl.written) + A.W), min(n, loaded + kLoadBatchRows));
+    const int32_t ab = __hip_atomic_load(&ctl.abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int32_t wr = __hip_atomic_load(&ctl.written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (ab) return;
+    const int32_t lim = min(min(xprev, wr + A.W), min(n, loaded + kLoadBatchRows));
     if (lim > loaded) {
       ring_fill(A, mem, loaded, lim, lane);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in LDS
