@@ -440,7 +440,7 @@ __device__ __forceinline__ bool col_common(const Ring<T> &A, int32_t sc, int32_t
 // b' >= 3 the two second parts overlap and half q waits for 2(q+d) steps.
 // Either way it waits for all 4 Kp steps once the predecessor has no half
 // q+d-1 left.
-template <typename T, int MAXM, int SC>
+template <typename T, int MAXM, int SC, int TWO>
 __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, int t, int d, int32_t R, int j,
                             int lane, int64_t spin_limit, uint32_t *status, uint32_t *sync) {
   const int32_t S = SC ? SC : A.S;
@@ -497,7 +497,7 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
     if (!wait_half(2 * k, ch)) return;
     if (row_fast) {
       if (k == 0) ring_row_prep<T, MAXM, true, SC>(A, sr, colr, MAXM, lane, Pr);
-      if (nr > 64)
+      if (TWO == 1 || (TWO == 2 && nr > 64))
         ring_row_apply<T, MAXM, true, true, SC>(A, sr, colr, MAXM, nr, lane, Pr);
       else
         ring_row_apply<T, MAXM, true, false, SC>(A, sr, colr, MAXM, nr, lane, Pr);
@@ -516,7 +516,7 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
     }
     if (!wait_half(2 * k + 1, ch)) return;
     if (col_fast) {
-      if (nc > 64)
+      if (TWO == 1 || (TWO == 2 && nc > 64))
         ring_col_apply<T, MAXM, true, true, SC, false>(A, base, 0, MAXM, nc, lane, Pc);
       else
         ring_col_apply<T, MAXM, true, false, SC, false>(A, base, 0, MAXM, nc, lane, Pc);
@@ -907,7 +907,16 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         sym_group_sweep<T, MAXM>(A, ctl, sym_ys + wave * MAXM, n, b, t, d, R0 + wave, wave, lane, spin_limit,
                                  status);
       } else {
-        group_sweep<T, MAXM, SC>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
+        // TWO: 1, a pass with rows or columns beyond 64 per half (b + t > 64)
+        // runs the two-rows-per-lane code throughout (its masks cover shorter
+        // halves); 0, one row per lane; 2 (fp64, whose two-row code needs
+        // twice the registers), the choice per half
+        if constexpr (sizeof(T) == 8)
+          group_sweep<T, MAXM, SC, 2>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
+        else if (b + t > 64)
+          group_sweep<T, MAXM, SC, 1>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
+        else
+          group_sweep<T, MAXM, SC, 0>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
       }
     } else if (wave == G) {
       group_writer<T>(A, ctl, mem, n, R0, Gg, prog + int64_t(g) * kLine, lane, spin_limit, status, sync);
