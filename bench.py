@@ -10,6 +10,11 @@ Prints one JSON line:
   roofline        the dominant kernel's algorithmic bytes per launch over its
                   average launch duration (HIP events on the stream the
                   kernels run on), against the published HBM3E peak
+                  and (cache_ceiling) against a measured streaming ceiling of
+                  the Infinity Cache that holds the working band
+  ms_per_reduction_events  median and min of the per-step event times
+  schedulers_ms   the same path under the step scheduler (the page's one
+                  launch per step) and the persistent scheduler
   cpu_baseline    the CPU oracle (one thread) timed on a bounded prefix of the
                   same reduction, in the same unit
   svals           the step after the path: singular values of the workload's
@@ -100,7 +105,8 @@ def cpu_baseline(band, w, seconds):
     nbytes = alg_bytes_prefix(w.n, w.bw, w.tw, esize, done)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of the reduction's cycles in sequential order "
-                      f"({nbytes / 1e9:.2f} GB algorithmic, {dt:.1f} s, one thread)"}
+                      f"({nbytes / 1e9:.2f} GB algorithmic, {dt:.1f} s, one thread)",
+            "host": f"{host_model()}, {os.cpu_count()} logical CPUs"}
 
 
 # Pivots of one Sturm count step, VALU instructions in the issued code without
@@ -287,6 +293,18 @@ def accuracy_study(n, bw, tw, instances, out_md):
                                          "summary": summary}}), flush=True)
 
 
+def host_model() -> str:
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def host_cores() -> int:
     """Host threads for the threaded CPU chaser: the cores this process may
     run on, at most 16 (the host share that goes with one GPU).  The chaser
@@ -354,6 +372,55 @@ def stored_traffic(workload: str):
     return t
 
 
+def cache_ceiling(torch, dev, stream, mib=128, reps=10, inner=10):
+    """A measured ceiling for the level that holds the working band: an
+    elementwise streaming update y += x over two fp32 buffers of mib/2 MiB
+    each (together above the 8 x 4 MiB of L2, inside the 256 MiB Infinity
+    Cache), repeated so the buffers stay resident; bytes = 3 per element
+    (read x, read y, write y), `inner` back-to-back launches between two
+    events (so launch gaps weigh little), best of `reps`."""
+    n = (mib << 20) // 8
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.zeros(n, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        y.add_(x)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(inner):
+            y.add_(x)
+        b.record(stream)
+        b.synchronize()
+        best = min(best, a.elapsed_time(b) / inner)
+    return {"probe": f"y += x over two fp32 buffers of {mib // 2} MiB each (torch elementwise kernel), "
+                     f"{inner} launches per timing, best of {reps}", "GBps": round(3 * 4 * n / (best * 1e-3) / 1e9, 1)}
+
+
+def scheduler_times(bbm, torch, tb, w, dt, work, stream, reps=2):
+    """Median ms per reduction of the whole path under the step scheduler
+    (one launch per step, the page's design) and the persistent scheduler,
+    for comparison with the default."""
+    out = {}
+    for name, code in (("step", bbm.BB_SCHED_STEP), ("persistent", bbm.BB_SCHED_PERSISTENT)):
+        tun = bbm.tuning(scheduler=code)
+        bbm.reduce(tb, w.bw, w.tw, tun, work)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            bbm.reduce(tb, w.bw, w.tw, tun, work)
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        out[name] = round(statistics.median(ms), 3)
+    return out
+
+
 def pass_tables(w):
     """Per pass: (b, t, algorithmic bytes) of the workload."""
     esize = 8 if w.dtype == "f64" else 4
@@ -384,6 +451,8 @@ def main():
     ap.add_argument("--no-svals", action="store_true")
     ap.add_argument("--no-sym", action="store_true")
     ap.add_argument("--no-f16", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured cache ceiling probe")
+    ap.add_argument("--no-schedulers", action="store_true", help="skip the step / persistent scheduler times")
     ap.add_argument("--accuracy-study", action="store_true",
                     help="run the known-spectrum accuracy study instead of the bench (writes --study-out)")
     ap.add_argument("--study-n", type=int, default=512)
@@ -428,9 +497,12 @@ def main():
     sp = stream.cuda_stream
     wp, wn = work.data_ptr(), work.numel()
 
-    def one(evs=None):
+    def one(evs=None, sev=None):
         # pack, every pass, extract: the same launches bb_reduce makes; events
-        # (on the stream the kernels run on) bracket each pass's launches
+        # (on the stream the kernels run on) bracket each pass's launches and
+        # the whole step
+        if sev is not None:
+            sev[0].record(stream)
         bbm.bb_pack(tb.data_ptr(), tb.stride(0), w.n, w.bw, w.tw, dt, wp, wn, sp)
         for p in range(info.passes):
             if evs is not None:
@@ -439,6 +511,8 @@ def main():
             if evs is not None:
                 evs[p][1].record(stream)
         bbm.bb_extract(wp, wn, w.n, w.bw, w.tw, dt, d.data_ptr(), e.data_ptr(), sp)
+        if sev is not None:
+            sev[1].record(stream)
 
     if args.copy_probe_mib:
         nb = args.copy_probe_mib << 20
@@ -453,14 +527,16 @@ def main():
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(info.passes)]
           for _ in range(args.steps)]
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        one(ev[s])
+        one(ev[s], sev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     status = bbm.bb_device_status(wp, w.n, w.bw, w.tw, dt, sp)
     pass_ms = [[ev[s][p][0].elapsed_time(ev[s][p][1]) for s in range(args.steps)] for p in range(info.passes)]
+    step_ms = [a.elapsed_time(b) for (a, b) in sev]
     ms_per_step = wall * 1e3 / args.steps
     value = info.alg_bytes / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: the cycle kernel, one launch per pass; algorithmic
@@ -496,10 +572,18 @@ def main():
                                "one launch per pass",
                      "launches": launches, "avg_launch_ms": round(avg_launch_ms, 4),
                      "alg_bytes_per_launch": bytes_per_launch},
+        "ms_per_reduction_events": {"median": round(statistics.median(step_ms), 4), "min": round(min(step_ms), 4)},
         "passes": [{"b": b, "t": t, "alg_bytes": ab, "median_ms": round(statistics.median(pass_ms[i]), 4),
                     "GBps": round(ab / (statistics.median(pass_ms[i]) * 1e-3) / 1e9, 2)}
                    for i, (b, t, ab) in enumerate(passes)],
     }
+    if not args.no_ceiling:
+        ceil = cache_ceiling(torch, dev, stream)
+        ceil["frac"] = round(achieved / ceil["GBps"], 5)
+        out["roofline"]["cache_ceiling"] = ceil
+    if not args.no_schedulers:
+        out["schedulers_ms"] = scheduler_times(bbm, torch, tb, w, dt, work, stream)
+        out["schedulers_ms"]["default"] = round(statistics.median(step_ms), 3)
     if not args.no_svals:
         out["svals"] = measure_svals(bbm, torch, d, e, w, args.steps, stream, args.cpu_seconds / 3, not args.no_cpu)
     if not args.no_f16:
