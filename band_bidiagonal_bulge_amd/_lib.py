@@ -17,7 +17,8 @@ BB_OK, BB_ERR_ARG, BB_ERR_WORKSPACE, BB_ERR_HIP, BB_ERR_UNSUPPORTED, BB_ERR_TIME
 BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT, BB_SCHED_GROUP = 0, 1, 2, 3
 
 # Every symbol include/bb.h declares.
-EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract", "bb_export_band",
+EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_run_passes", "bb_extract",
+           "bb_launch_plan", "bb_export_band",
            "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce", "bb_sym_export_band",
            "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split", "bb_status_str")
 
@@ -48,6 +49,13 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build()")
+        # torch's HIP runtime must be loaded before this library's: loaded the
+        # other way round, torch binds to the system runtime and the library's
+        # first launch fails with hipErrorNoDevice
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
         L.bb_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(bb_plan_info)]
@@ -55,6 +63,9 @@ def lib():
         L.bb_reduce.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, sz, ctypes.POINTER(bb_tuning), vp]
         L.bb_pack.argtypes = [vp, i64, i64, i32, i32, i32, vp, sz, vp]
         L.bb_run_pass.argtypes = [i64, i32, i32, i32, i32, vp, sz, ctypes.POINTER(bb_tuning), vp]
+        L.bb_run_passes.argtypes = [i64, i32, i32, i32, i32, i32, vp, sz, ctypes.POINTER(bb_tuning), vp]
+        L.bb_launch_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(bb_tuning), ctypes.POINTER(i32), i32,
+                                     ctypes.POINTER(i32)]
         L.bb_extract.argtypes = [vp, sz, i64, i32, i32, i32, vp, vp, vp]
         L.bb_export_band.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         L.bb_device_status.argtypes = [vp, i64, i32, i32, i32, vp]
@@ -67,7 +78,8 @@ def lib():
         L.bb_svals_split.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.bb_status_str.argtypes = [i32]
         L.bb_status_str.restype = ctypes.c_char_p
-        for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_extract",
+        for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_run_passes",
+                  "bb_launch_plan", "bb_extract",
                   "bb_export_band", "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce",
                   "bb_sym_export_band", "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split"):
             getattr(L, f).restype = i32
@@ -116,6 +128,26 @@ def bb_run_pass(n: int, bw: int, tw: int, dtype: int, pass_index: int, work_ptr:
                            ctypes.byref(tuning) if tuning is not None else None, stream or None)
     if rc != BB_OK:
         raise BBError(rc, "bb_run_pass")
+
+
+def bb_run_passes(n: int, bw: int, tw: int, dtype: int, first: int, count: int, work_ptr: int, work_bytes: int,
+                  tuning: bb_tuning | None, stream: int) -> None:
+    rc = lib().bb_run_passes(n, bw, tw, dtype, first, count, work_ptr, work_bytes,
+                             ctypes.byref(tuning) if tuning is not None else None, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_run_passes")
+
+
+def bb_launch_plan(n: int, bw: int, tw: int, dtype: int, tuning: bb_tuning | None) -> list[int]:
+    """Index of the cycle-kernel launch that runs each pass (-1: no sweeps)."""
+    passes = bb_plan(n, bw, tw, dtype).passes
+    out = (ctypes.c_int32 * max(passes, 1))()
+    count = ctypes.c_int32(0)
+    rc = lib().bb_launch_plan(n, bw, tw, dtype, ctypes.byref(tuning) if tuning is not None else None, out,
+                              passes, ctypes.byref(count))
+    if rc != BB_OK:
+        raise BBError(rc, "bb_launch_plan")
+    return [int(out[i]) for i in range(passes)]
 
 
 def bb_extract(work_ptr: int, work_bytes: int, n: int, bw: int, tw: int, dtype: int, d_ptr: int, e_ptr: int,

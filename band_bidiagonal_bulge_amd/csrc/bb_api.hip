@@ -157,21 +157,72 @@ GroupPlan group_plan(const bb::Geometry &g, const bb::Pass &p, int requested_g) 
   return gp;
 }
 
-bb_status run_group_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
-                         const GroupPlan &gp, uint32_t *sync, hipStream_t st) {
-  const int64_t ns = bb::sweeps_of(g.n, p);
-  if (ns == 0) return BB_OK;
-  const int64_t ngroups = (ns + gp.G - 1) / gp.G;
+// The launches of passes [first, first + count): a group launch runs a run of
+// consecutive passes whose rings fit, with register tiles of one family (8/9
+// or 16/17 entries); under BB_SCHED_GROUP every run is one pass.  A run also
+// ends at kMaxRunPasses passes and where its groups would exceed the
+// workspace's progress lines (n + 1).  Passes without sweeps are skipped.
+struct LaunchItem {
+  bool group = false;
+  int first = 0, count = 0;  // passes [first, first + count)
+  bb::GroupRun run{};
+  int W = 0;
+};
+
+int tile_family(int maxm) { return maxm <= 9 ? 9 : 17; }
+
+std::vector<LaunchItem> plan_launches(const bb::Geometry &g, const std::vector<bb::Pass> &passes, int first, int count,
+                                      const bb_tuning &tu) {
+  std::vector<LaunchItem> out;
+  const bool may_group = tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP;
+  const bool fuse = tu.scheduler == BB_SCHED_DEFAULT;
+  const int64_t lines = g.n + 1;
+  for (int i = first; i < first + count; ++i) {
+    const bb::Pass &p = passes[size_t(i)];
+    const int64_t ns = bb::sweeps_of(g.n, p);
+    if (ns == 0) continue;
+    const GroupPlan gp = may_group ? group_plan(g, p, tu.group_sweeps) : GroupPlan{};
+    if (gp.G == 0) {
+      LaunchItem it;
+      it.first = i;
+      it.count = 1;
+      out.push_back(it);
+      continue;
+    }
+    const int maxm = pick_maxm(p.t);
+    const int64_t ngroups = (ns + gp.G - 1) / gp.G;
+    LaunchItem *cur = out.empty() ? nullptr : &out.back();
+    const bool join = fuse && cur && cur->group && cur->first + cur->count == i &&
+                      cur->run.npass < bb::kMaxRunPasses && cur->run.maxm == tile_family(maxm) && cur->W == gp.W &&
+                      cur->run.total + ngroups <= lines;
+    if (!join) {
+      out.emplace_back();
+      cur = &out.back();
+      cur->group = true;
+      cur->first = i;
+      cur->W = gp.W;
+      cur->run.maxm = tile_family(maxm);
+    }
+    const int variant = (maxm != cur->run.maxm ? 1 : 0) | (g.esize != 8 && p.b + p.t > 64 ? 2 : 0);
+    cur->run.pass[cur->run.npass] = bb::group_pass_word(p.b, p.t, gp.G, variant);
+    cur->run.base[cur->run.npass] = cur->run.total;
+    ++cur->run.npass;
+    cur->run.total += int32_t(ngroups);
+    cur->run.gmax = std::max(cur->run.gmax, gp.G);
+    cur->count = i - cur->first + 1;
+  }
+  return out;
+}
+
+bb_status run_group_launch(void *wband, const bb::Geometry &g, const LaunchItem &it, const bb_tuning &tu,
+                           uint32_t *sync, hipStream_t st) {
   if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
-      bb::launch_fill_u32(sync + bb::kSyncHeader, ngroups * bb::kLine, 0u, st) != hipSuccess)
+      bb::launch_fill_u32(sync + bb::kSyncHeader, int64_t(it.run.total) * bb::kLine, 0u, st) != hipSuccess)
     return BB_ERR_HIP;
   int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
-  grid = std::min<int64_t>(grid, ngroups);
+  grid = std::min<int64_t>(grid, it.run.total);
   const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
-  if (bb::launch_group(pick_maxm(p.t), wband, g, p.b, p.t, bb::lag_of(p), ns, gp.G, gp.W, sync, int(grid), spin,
-                       st) != hipSuccess)
-    return BB_ERR_HIP;
-  return BB_OK;
+  return hip_status(bb::launch_group(it.run, wband, g, it.W, sync, int(grid), spin, st));
 }
 
 // Shared validation of the workspace-level entry points.
@@ -198,17 +249,25 @@ bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
   return BB_OK;
 }
 
-// Scheduler of a pass: STEP and PERSISTENT as asked; GROUP when the pass fits
-// in LDS (else PERSISTENT); DEFAULT = GROUP where it fits.
-bb_status run_pass(void *work, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu, hipStream_t st) {
+// Passes [first, first + count) in order: STEP and PERSISTENT as asked;
+// GROUP and DEFAULT run the group kernel where a pass's ring fits (else
+// PERSISTENT), DEFAULT with runs of such passes in one launch.
+bb_status run_passes(void *work, const bb::Geometry &g, const std::vector<bb::Pass> &passes, int first, int count,
+                     const bb_tuning &tu, hipStream_t st) {
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
   if (g.dtype == BB_F16 && tu.scheduler == BB_SCHED_STEP) return BB_ERR_UNSUPPORTED;  // no fp16 step kernel
-  if (tu.scheduler == BB_SCHED_STEP) return run_step_pass(work, g, p, tu, st);
-  if (tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP) {
-    const GroupPlan gp = group_plan(g, p, tu.group_sweeps);
-    if (gp.G > 0) return run_group_pass(work, g, p, tu, gp, sync, st);
+  bb_status rc = BB_OK;
+  for (const LaunchItem &it : plan_launches(g, passes, first, count, tu)) {
+    const bb::Pass &p = passes[size_t(it.first)];
+    if (it.group)
+      rc = run_group_launch(work, g, it, tu, sync, st);
+    else if (tu.scheduler == BB_SCHED_STEP)
+      rc = run_step_pass(work, g, p, tu, st);
+    else
+      rc = run_persistent_pass(work, g, p, tu, sync, st);
+    if (rc != BB_OK) return rc;
   }
-  return run_persistent_pass(work, g, p, tu, sync, st);
+  return BB_OK;
 }
 
 // Symmetric band -> tridiagonal: validation and the passes.
@@ -290,8 +349,13 @@ bb_status run_sym_pass(void *work, const bb::SymGeometry &g, const bb::Pass &p, 
       int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
       grid = std::min<int64_t>(grid, ngroups);
       const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
-      return hip_status(bb::launch_sym_group(sym_maxm(p.t), work, g, p.b, p.t, bb::lag_of(p), ns, gp.G, gp.W,
-                                             sync, int(grid), spin, st));
+      bb::GroupRun run{};
+      run.npass = 1;
+      run.total = int32_t(ngroups);
+      run.gmax = gp.G;
+      run.maxm = sym_maxm(p.t);
+      run.pass[0] = bb::group_pass_word(p.b, p.t, gp.G, 0);
+      return hip_status(bb::launch_sym_group(run, work, g, gp.W, sync, int(grid), spin, st));
     }
   }
   if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
@@ -501,7 +565,40 @@ bb_status bb_run_pass(int64_t n, int32_t bw, int32_t tw, int32_t dtype, int32_t 
   if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
   const std::vector<bb::Pass> passes = bb::pass_list(bw, tw);
   if (pass < 0 || pass >= int32_t(passes.size())) return BB_ERR_ARG;
-  return run_pass(work, g, passes[size_t(pass)], tu, static_cast<hipStream_t>(stream));
+  return run_passes(work, g, passes, pass, 1, tu, static_cast<hipStream_t>(stream));
+}
+
+bb_status bb_run_passes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, int32_t first, int32_t count, void *work,
+                        size_t work_bytes, const bb_tuning *tuning, void *stream) {
+  bb::Geometry g;
+  bb_status rc = check_work(n, bw, tw, dtype, work, work_bytes, &g);
+  if (rc != BB_OK) return rc;
+  bb_tuning tu;
+  if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
+  const std::vector<bb::Pass> passes = bb::pass_list(bw, tw);
+  if (first < 0 || count < 0 || int64_t(first) + count > int64_t(passes.size())) return BB_ERR_ARG;
+  return run_passes(work, g, passes, first, count, tu, static_cast<hipStream_t>(stream));
+}
+
+bb_status bb_launch_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const bb_tuning *tuning,
+                         int32_t *launch_of_pass, int32_t capacity, int32_t *launches) {
+  if (!valid_shape(n, bw, tw, dtype) || !launches || capacity < 0 || (capacity > 0 && !launch_of_pass))
+    return BB_ERR_ARG;
+  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
+  if (!supported(g)) return BB_ERR_UNSUPPORTED;
+  bb_tuning tu;
+  bb_status rc = check_tuning(tuning, &tu);
+  if (rc != BB_OK) return rc;
+  const std::vector<bb::Pass> passes = bb::pass_list(bw, tw);
+  if (capacity > 0 && capacity < int32_t(passes.size())) return BB_ERR_ARG;
+  const std::vector<LaunchItem> items = plan_launches(g, passes, 0, int(passes.size()), tu);
+  if (capacity > 0) {
+    for (size_t i = 0; i < passes.size(); ++i) launch_of_pass[i] = -1;  // no sweeps: nothing to launch
+    for (size_t k = 0; k < items.size(); ++k)
+      for (int i = items[k].first; i < items[k].first + items[k].count; ++i) launch_of_pass[i] = int32_t(k);
+  }
+  *launches = int32_t(items.size());
+  return BB_OK;
 }
 
 bb_status bb_extract(const void *work, size_t work_bytes, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
@@ -525,9 +622,9 @@ bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, in
   bb_tuning tu;
   if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
   if ((rc = bb_pack(band, ld_band, n, bw, tw, dtype, work, work_bytes, stream)) != BB_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  for (const bb::Pass &p : bb::pass_list(bw, tw))
-    if ((rc = run_pass(work, g, p, tu, st)) != BB_OK) return rc;
+  const std::vector<bb::Pass> passes = bb::pass_list(bw, tw);
+  if ((rc = run_passes(work, g, passes, 0, int(passes.size()), tu, static_cast<hipStream_t>(stream))) != BB_OK)
+    return rc;
   return bb_extract(work, work_bytes, n, bw, tw, dtype, d, e, stream);
 }
 

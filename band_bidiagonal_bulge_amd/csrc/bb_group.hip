@@ -49,7 +49,9 @@ constexpr int32_t kLoadBatchRows = 64;   // rows per loader batch: early rows ar
 constexpr int32_t kDrainBatchRows = 32;  // rows per writer batch, published one batch at a time
 
 struct GroupCtl {
-  int32_t g;                         // group being run
+  int32_t g;                         // group being run (numbered over the launch's run of passes)
+  uint32_t pass_word, prev_word;     // its pass and the pass before it (group_pass_word)
+  int32_t base, prev_base;           // their first groups (prev_base -1: the run's first pass)
   int32_t loaded_hi;                 // rows [R0, loaded_hi) resident in the ring
   int32_t written;                   // rows [R0, written) written back; their slots are free
   int32_t abort_;                    // a wait expired: drain
@@ -829,24 +831,42 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
   }
 }
 
-// The loader: polls the previous group's released rows and loads them into
-// free ring slots, in batches, signalling each batch.
+// Where a group's loader learns which rows are final: the previous group's
+// release counter X_{g-1} (G = 0), or, for the first group of a pass that
+// follows another in the same launch, the counters of that pass's groups
+// (G sweeps each, ngroups of them, the first at `line`): its group
+// q = min(i / G, ngroups - 1) is the last one to touch row i, and since
+// X_q <= X_{q'} for q' < q, X_q > i means that every group of that pass is
+// done with row i.  line = nullptr: every row is final (the launch's first
+// pass).
+struct PrevRows {
+  const uint32_t *line;
+  int32_t G, ngroups;
+};
+
+// The loader: polls the released rows and loads them into free ring slots,
+// in batches, signalling each batch.
 template <typename T>
 __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
-                             const uint32_t *xprev_line, int lane, int64_t spin_limit, uint32_t *status,
-                             uint32_t *sync) {
+                             const PrevRows src, int lane, int64_t spin_limit, uint32_t *status, uint32_t *sync) {
   int32_t loaded = R0;
-  int32_t xprev = xprev_line ? 0 : n;
+  int32_t xprev = src.line ? 0 : n;
   int64_t idle = 0;
   BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g); int it_no = 0;)
   for (;;) {
     // the three words are read together, then one acquire
-    if (xprev < n) xprev = int32_t(__hip_atomic_load(xprev_line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const int32_t want = min(n, loaded + kLoadBatchRows);
+    if (src.G > 0) {  // the owner of the batch's last row, in the previous pass
+      const int32_t q = min((want - 1) / src.G, src.ngroups - 1);
+      xprev = int32_t(__hip_atomic_load(src.line + int64_t(q) * kLine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    } else if (xprev < n) {
+      xprev = int32_t(__hip_atomic_load(src.line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
     const int32_t ab = __hip_atomic_load(&ctl.abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const int32_t wr = __hip_atomic_load(&ctl.written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (ab) return;
-    const int32_t lim = min(min(xprev, wr + A.W), min(n, loaded + kLoadBatchRows));
+    const int32_t lim = min(min(xprev, wr + A.W), want);
     if (lim > loaded) {
       ring_fill(A, mem, loaded, lim, lane);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in LDS
@@ -866,13 +886,14 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
   }
 }
 
-// Persistent group kernel: workgroups claim groups in increasing order.
-// blockDim = 64 (G + 2); dynamic LDS = W * S * sizeof(T).  SYM: the sweeps
-// are the symmetric reduction's (by half-cycles, with the same lag d).
+// Persistent group kernel: workgroups claim the groups of a run of passes
+// in increasing order.  blockDim = 64 (gmax + 2); dynamic LDS = W * S *
+// sizeof(T).  MAXM: the run's register tile; a pass of the run may use
+// MAXM - 1 instead (variant bit 0).  SYM: the sweeps are the symmetric
+// reduction's (by half-cycles, with the same lag d), every pass at MAXM.
 template <typename T, int MAXM, int SC, bool SYM = false>
-__global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, int32_t sub, int32_t n, int b,
-                                                                 int t, int d, int32_t nsweeps, int G, int W,
-                                                                 uint32_t *sync, int64_t spin_limit) {
+__global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, int32_t sub, int32_t n, GroupRun run,
+                                                                 int W, uint32_t *sync, int64_t spin_limit) {
   extern __shared__ __align__(16) unsigned char lds_ring[];
   __shared__ GroupCtl ctl;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);  // wave-uniform
@@ -883,15 +904,53 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
   const Ring<T> A{reinterpret_cast<T *>(lds_ring), S, W, sub};
   const __amdgpu_buffer_rsrc_t mem =
       __builtin_amdgcn_make_buffer_rsrc(a, 0, int(uint32_t(int64_t(n) * S * int64_t(sizeof(T)))), kRsrcWord3);
-  if (threadIdx.x == 0) ctl.abort_ = 0;
+  // the run's table goes to LDS once, so that no SGPRs hold it while the
+  // sweeps run
+  __shared__ uint32_t tab_pass[kMaxRunPasses];
+  __shared__ int32_t tab_base[kMaxRunPasses];
+  if (threadIdx.x == 0) {
+    ctl.abort_ = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxRunPasses; ++j) {
+      tab_pass[j] = run.pass[j];
+      tab_base[j] = j < run.npass ? run.base[j] : run.total;
+    }
+  }
   for (;;) {
-    if (threadIdx.x == 0) ctl.g = int32_t(atomicAdd(claim, 1u));
+    // thread 0 claims a group and looks up its pass (the last whose first
+    // group is <= gi) and the pass before it in the run; the other waves
+    // read them from LDS
+    if (threadIdx.x == 0) {
+      const int32_t gi = int32_t(atomicAdd(claim, 1u));
+      uint32_t pw = tab_pass[0], qw = 0;
+      int32_t base = 0, qbase = -1;
+#pragma unroll
+      for (int j = 1; j < kMaxRunPasses; ++j) {
+        if (gi >= tab_base[j] && tab_base[j] < run.total) {
+          qw = pw;
+          qbase = base;
+          pw = tab_pass[j];
+          base = tab_base[j];
+        }
+      }
+      ctl.g = gi;
+      ctl.pass_word = pw;
+      ctl.prev_word = qw;
+      ctl.base = base;
+      ctl.prev_base = qbase;
+    }
     __syncthreads();
-    const int32_t g = ctl.g;
-    const int64_t R0l = int64_t(g) * G;
-    if (R0l >= nsweeps || ctl.abort_) break;
-    const int32_t R0 = int32_t(R0l);
-    const int32_t Gg = min(G, nsweeps - R0);
+    const int32_t gi = __builtin_amdgcn_readfirstlane(ctl.g);  // over the run
+    if (gi >= run.total || ctl.abort_) break;
+    const uint32_t pw = __builtin_amdgcn_readfirstlane(ctl.pass_word);
+    const int32_t base = __builtin_amdgcn_readfirstlane(ctl.base);
+    const int pb = int(pw & 0x1fffu), pt = int((pw >> 13) & 0x1fffu), pG = int((pw >> 26) & 7u);
+    const int variant = int(pw >> 29);
+    const int pd = pb - pt >= 3 ? 2 : (pb - pt == 2 ? 3 : 4);
+    const int32_t nsweeps = max(n - (pb - pt) - 1, 0);
+    const int32_t g = gi - base;
+    const int32_t R0 = g * pG;
+    const int32_t Gg = min(pG, nsweeps - R0);
     __syncthreads();  // every wave has read ctl.g before it is reset below
     if (threadIdx.x == 0) {
       ctl.loaded_hi = R0;
@@ -904,40 +963,61 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
     if (wave < Gg) {
       if constexpr (SYM) {
         __shared__ T sym_ys[kGroupMaxSweeps * MAXM];
-        sym_group_sweep<T, MAXM>(A, ctl, sym_ys + wave * MAXM, n, b, t, d, R0 + wave, wave, lane, spin_limit,
+        sym_group_sweep<T, MAXM>(A, ctl, sym_ys + wave * MAXM, n, pb, pt, pd, R0 + wave, wave, lane, spin_limit,
                                  status);
       } else {
-        // TWO: 1, a pass with rows or columns beyond 64 per half (b + t > 64)
-        // runs the two-rows-per-lane code throughout (its masks cover shorter
+        // the pass's tile (MAXM or MAXM - 1) and rows per lane: 1, a pass
+        // with rows or columns beyond 64 per half (b + t > 64) runs the
+        // two-rows-per-lane code throughout (its masks cover shorter
         // halves); 0, one row per lane; 2 (fp64, whose two-row code needs
         // twice the registers), the choice per half
-        if constexpr (sizeof(T) == 8)
-          group_sweep<T, MAXM, SC, 2>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
-        else if (b + t > 64)
-          group_sweep<T, MAXM, SC, 1>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
-        else
-          group_sweep<T, MAXM, SC, 0>(A, ctl, n, b, t, d, R0 + wave, wave, lane, spin_limit, status, sync);
+        const bool lo = (variant & 1) != 0;
+        const bool two = (variant & 2) != 0;
+        const int32_t R = R0 + wave;
+        if constexpr (sizeof(T) == 8) {
+          if (lo)
+            group_sweep<T, MAXM - 1, SC, 2>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+          else
+            group_sweep<T, MAXM, SC, 2>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+        } else if (lo) {
+          if (two)
+            group_sweep<T, MAXM - 1, SC, 1>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+          else
+            group_sweep<T, MAXM - 1, SC, 0>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+        } else {
+          if (two)
+            group_sweep<T, MAXM, SC, 1>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+          else
+            group_sweep<T, MAXM, SC, 0>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+        }
       }
-    } else if (wave == G) {
-      group_writer<T>(A, ctl, mem, n, R0, Gg, prog + int64_t(g) * kLine, lane, spin_limit, status, sync);
-    } else if (wave == G + 1) {
-      group_loader<T>(A, ctl, mem, n, R0, g > 0 ? prog + int64_t(g - 1) * kLine : nullptr, lane, spin_limit,
-                      status, sync);
+    } else if (wave == run.gmax) {
+      group_writer<T>(A, ctl, mem, n, R0, Gg, prog + int64_t(gi) * kLine, lane, spin_limit, status, sync);
+    } else if (wave == run.gmax + 1) {
+      PrevRows src{nullptr, 0, 0};
+      if (g > 0)
+        src.line = prog + int64_t(gi - 1) * kLine;
+      else if (ctl.prev_base >= 0) {  // the first group of a pass after the run's first
+        const uint32_t qw = ctl.prev_word;
+        const int qb = int(qw & 0x1fffu), qt = int((qw >> 13) & 0x1fffu), qG = int((qw >> 26) & 7u);
+        const int32_t qsweeps = max(n - (qb - qt) - 1, 0);
+        src = PrevRows{prog + int64_t(ctl.prev_base) * kLine, qG, (qsweeps + qG - 1) / qG};
+      }
+      group_loader<T>(A, ctl, mem, n, R0, src, lane, spin_limit, status, sync);
     }
     __syncthreads();
   }
 }
 
 template <typename T, int MAXM, int SC>
-hipError_t group_t(void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
-                   uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+hipError_t group_t(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
+                   int64_t spin_limit, hipStream_t st) {
   const size_t lds = size_t(W) * size_t(g.stride) * sizeof(T);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, SC>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_group<T, MAXM, SC>), dim3(unsigned(grid)), dim3(unsigned(64 * (G + 2))), lds, st,
-                     static_cast<T *>(wband), g.stride, g.sub, int32_t(g.n), b, t, d, int32_t(nsweeps), G, W, sync,
-                     spin_limit);
+  hipLaunchKernelGGL((k_group<T, MAXM, SC>), dim3(unsigned(grid)), dim3(unsigned(64 * (run.gmax + 2))), lds, st,
+                     static_cast<T *>(wband), g.stride, g.sub, int32_t(g.n), run, W, sync, spin_limit);
   return hipGetLastError();
 }
 
@@ -945,70 +1025,62 @@ hipError_t group_t(void *wband, const Geometry &g, int b, int t, int d, int64_t 
 // of BW 64 / TW 16 and BW 32 / TW 16 in fp32, BW 16 / TW 8 in fp64, BW 64 /
 // TW 16 in fp16); any other stride runs the generic ring code.
 template <typename T, int MAXM>
-hipError_t group_stride(void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
-                        uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+hipError_t group_stride(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
+                        int64_t spin_limit, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {  // half precision: the headline band's stride, else the generic ring code
-    if (g.stride == 104)
-      return group_t<T, MAXM, 104>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-    return group_t<T, MAXM, 0>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    if (g.stride == 104) return group_t<T, MAXM, 104>(run, wband, g, W, sync, grid, spin_limit, st);
+    return group_t<T, MAXM, 0>(run, wband, g, W, sync, grid, spin_limit, st);
   } else {
-  if (sizeof(T) == 4 && g.stride == 100)
-    return group_t<T, MAXM, 100>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-  if (sizeof(T) == 4 && g.stride == 68)
-    return group_t<T, MAXM, 68>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-  if (sizeof(T) == 8 && g.stride == 34)
-    return group_t<T, MAXM, 34>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-  return group_t<T, MAXM, 0>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    if (sizeof(T) == 4 && g.stride == 100) return group_t<T, MAXM, 100>(run, wband, g, W, sync, grid, spin_limit, st);
+    if (sizeof(T) == 4 && g.stride == 68) return group_t<T, MAXM, 68>(run, wband, g, W, sync, grid, spin_limit, st);
+    if (sizeof(T) == 8 && g.stride == 34) return group_t<T, MAXM, 34>(run, wband, g, W, sync, grid, spin_limit, st);
+    return group_t<T, MAXM, 0>(run, wband, g, W, sync, grid, spin_limit, st);
   }
 }
 
 template <typename T>
-hipError_t group_dispatch(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
-                          int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
-  switch (maxm) {
-    case 8: return group_stride<T, 8>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-    case 9: return group_stride<T, 9>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-    case 16: return group_stride<T, 16>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-    case 17: return group_stride<T, 17>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+hipError_t group_dispatch(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
+                          int64_t spin_limit, hipStream_t st) {
+  switch (run.maxm) {
+    case 9: return group_stride<T, 9>(run, wband, g, W, sync, grid, spin_limit, st);
+    case 17: return group_stride<T, 17>(run, wband, g, W, sync, grid, spin_limit, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, int MAXM>
-hipError_t sym_group_t(void *wband, const SymGeometry &g, int b, int t, int d, int64_t nsweeps, int G, int W,
-                       uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+hipError_t sym_group_t(const GroupRun &run, void *wband, const SymGeometry &g, int W, uint32_t *sync, int grid,
+                       int64_t spin_limit, hipStream_t st) {
   const size_t lds = size_t(W) * size_t(g.stride) * sizeof(T);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, 0, true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_group<T, MAXM, 0, true>), dim3(unsigned(grid)), dim3(unsigned(64 * (G + 2))), lds, st,
-                     static_cast<T *>(wband), g.stride, 0, int32_t(g.n), b, t, d, int32_t(nsweeps), G, W, sync,
-                     spin_limit);
+  hipLaunchKernelGGL((k_group<T, MAXM, 0, true>), dim3(unsigned(grid)), dim3(unsigned(64 * (run.gmax + 2))), lds, st,
+                     static_cast<T *>(wband), g.stride, 0, int32_t(g.n), run, W, sync, spin_limit);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_sym_group(int maxm, void *wband, const SymGeometry &g, int b, int t, int d, int64_t nsweeps, int G,
-                            int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
+hipError_t launch_sym_group(const GroupRun &run, void *wband, const SymGeometry &g, int W, uint32_t *sync, int grid,
+                            int64_t spin_limit, hipStream_t st) {
   if (g.dtype == 1) {
-    if (maxm == 9) return sym_group_t<double, 9>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-    if (maxm == 17) return sym_group_t<double, 17>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+    if (run.maxm == 9) return sym_group_t<double, 9>(run, wband, g, W, sync, grid, spin_limit, st);
+    if (run.maxm == 17) return sym_group_t<double, 17>(run, wband, g, W, sync, grid, spin_limit, st);
     return hipErrorInvalidValue;
   }
   if (g.dtype != 0) return hipErrorInvalidValue;
-  if (maxm == 9) return sym_group_t<float, 9>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-  if (maxm == 17) return sym_group_t<float, 17>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-  if (maxm == 33) return sym_group_t<float, 33>(wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+  if (run.maxm == 9) return sym_group_t<float, 9>(run, wband, g, W, sync, grid, spin_limit, st);
+  if (run.maxm == 17) return sym_group_t<float, 17>(run, wband, g, W, sync, grid, spin_limit, st);
+  if (run.maxm == 33) return sym_group_t<float, 33>(run, wband, g, W, sync, grid, spin_limit, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
-                        int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st) {
-  if (g.dtype == 1) return group_dispatch<double>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-  if (g.dtype == 2)
-    return group_dispatch<_Float16>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
-  return group_dispatch<float>(maxm, wband, g, b, t, d, nsweeps, G, W, sync, grid, spin_limit, st);
+hipError_t launch_group(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
+                        int64_t spin_limit, hipStream_t st) {
+  if (g.dtype == 1) return group_dispatch<double>(run, wband, g, W, sync, grid, spin_limit, st);
+  if (g.dtype == 2) return group_dispatch<_Float16>(run, wband, g, W, sync, grid, spin_limit, st);
+  return group_dispatch<float>(run, wband, g, W, sync, grid, spin_limit, st);
 }
 
 }  // namespace bb

@@ -24,12 +24,31 @@ hipError_t launch_step(int maxm, void *wband, const Geometry &g, int b, int t, i
 hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
                           int grid, int nt, int64_t spin_limit, hipStream_t st);
 
-// Sweep groups resident in LDS for one pass: `grid` workgroups of 64 (G+2)
-// threads claim groups of G consecutive sweeps; each keeps a ring of W band
-// rows in LDS; d is the in-group lag in half-cycles.
+// Sweep groups resident in LDS: `grid` workgroups of 64 (gmax+2) threads
+// claim groups of G consecutive sweeps; each keeps a ring of W band rows in
+// LDS; d is the in-group lag in half-cycles.  One launch runs a run of
+// consecutive passes: the run's groups are numbered pass by pass (pass j's
+// groups are base .. base+ngroups-1, its progress lines at the same indices)
+// and claimed in that order, so a group only ever waits for groups claimed
+// before it.  The first group of a pass loads a row once the previous pass's
+// group that owns the row has released it.
 constexpr int kGroupMaxWaves = 8;  // G <= 6 sweeps plus a loader and a writer wave (2 waves per SIMD: 256 VGPRs)
-hipError_t launch_group(int maxm, void *wband, const Geometry &g, int b, int t, int d, int64_t nsweeps, int G,
-                        int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st);
+constexpr int kMaxRunPasses = 4;
+// A pass of a run in one word (the kernel derives the rest: the lag d from
+// b' = b - t, n - b' - 1 sweeps, groups of G): b | t << 13 | G << 26 |
+// variant << 29; variant bit 0: register tile maxm - 1 (else maxm), bit 1:
+// two rows per lane (b + t > 64).
+inline uint32_t group_pass_word(int b, int t, int G, int variant) {
+  return uint32_t(b) | (uint32_t(t) << 13) | (uint32_t(G) << 26) | (uint32_t(variant) << 29);
+}
+struct GroupRun {
+  int32_t npass, total;  // passes in the run (1..kMaxRunPasses), groups over the run
+  int32_t gmax, maxm;    // largest G (block = 64 (gmax+2) threads); the run's register tile family
+  uint32_t pass[kMaxRunPasses];
+  int32_t base[kMaxRunPasses];  // the pass's first group in the run
+};
+hipError_t launch_group(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
+                        int64_t spin_limit, hipStream_t st);
 
 // LDS bytes one workgroup stages per cycle for a pass (b, t) with register
 // tile maxm.
@@ -44,9 +63,10 @@ hipError_t launch_sym_persist(int maxm, void *wband, const SymGeometry &g, int b
                               uint32_t *sync, int grid, int nt, int64_t spin_limit, hipStream_t st);
 hipError_t launch_sym_extract(const void *wband, const SymGeometry &g, void *d, void *e, hipStream_t st);
 // The symmetric sweeps in LDS-resident groups (the k_group kernel with the
-// symmetric half-cycles): maxm 9 or 17 (fp32 also 33), d = the lag in halves.
-hipError_t launch_sym_group(int maxm, void *wband, const SymGeometry &g, int b, int t, int d, int64_t nsweeps, int G,
-                            int W, uint32_t *sync, int grid, int64_t spin_limit, hipStream_t st);
+// symmetric half-cycles): run.maxm 9 or 17 (fp32 also 33) for every pass of
+// the run, d = the lag in halves.
+hipError_t launch_sym_group(const GroupRun &run, void *wband, const SymGeometry &g, int W, uint32_t *sync, int grid,
+                            int64_t spin_limit, hipStream_t st);
 
 // Singular values of the bidiagonal by bisection (bb_svals.hip).  The
 // workspace holds a header {lo, hi, pivmin} in its first kSvalsHeaderBytes,

@@ -14,7 +14,12 @@ Prints one JSON line:
                   the Infinity Cache that holds the working band
   ms_per_reduction_events  median and min of the per-step event times
   schedulers_ms   the same path under the step scheduler (the page's one
-                  launch per step) and the persistent scheduler
+                  launch per step) and the persistent scheduler, and the sum
+                  of the per-pass times below (the group kernel, one launch
+                  per pass)
+  passes          each pass in a launch of its own (bb_run_pass), timed after
+                  the steps; launch_of_pass: which cycle-kernel launch runs
+                  each pass in a step
   cpu_baseline    the CPU oracle (one thread) timed on a bounded prefix of the
                   same reduction, in the same unit
   svals           the step after the path: singular values of the workload's
@@ -453,6 +458,8 @@ def main():
     ap.add_argument("--no-f16", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured cache ceiling probe")
     ap.add_argument("--no-schedulers", action="store_true", help="skip the step / persistent scheduler times")
+    ap.add_argument("--no-per-pass", action="store_true",
+                    help="skip the per-pass breakdown (each pass in a launch of its own, after the steps)")
     ap.add_argument("--accuracy-study", action="store_true",
                     help="run the known-spectrum accuracy study instead of the bench (writes --study-out)")
     ap.add_argument("--study-n", type=int, default=512)
@@ -497,22 +504,42 @@ def main():
     sp = stream.cuda_stream
     wp, wn = work.data_ptr(), work.numel()
 
-    def one(evs=None, sev=None):
-        # pack, every pass, extract: the same launches bb_reduce makes; events
-        # (on the stream the kernels run on) bracket each pass's launches and
-        # the whole step
+    # the cycle-kernel launches of one reduction: under the default scheduler
+    # consecutive passes on the group kernel share one launch
+    launch_of = bbm.bb_launch_plan(w.n, w.bw, w.tw, dt, tun)
+    nlaunch = len(set(x for x in launch_of if x >= 0))
+
+    def one(rev=None, sev=None):
+        # pack, every pass (one bb_run_passes call, as bb_reduce makes it),
+        # extract; events on the stream the kernels run on bracket the passes
+        # and the whole step
         if sev is not None:
             sev[0].record(stream)
         bbm.bb_pack(tb.data_ptr(), tb.stride(0), w.n, w.bw, w.tw, dt, wp, wn, sp)
-        for p in range(info.passes):
-            if evs is not None:
-                evs[p][0].record(stream)
-            bbm.bb_run_pass(w.n, w.bw, w.tw, dt, p, wp, wn, tun, sp)
-            if evs is not None:
-                evs[p][1].record(stream)
+        if rev is not None:
+            rev[0].record(stream)
+        bbm.bb_run_passes(w.n, w.bw, w.tw, dt, 0, info.passes, wp, wn, tun, sp)
+        if rev is not None:
+            rev[1].record(stream)
         bbm.bb_extract(wp, wn, w.n, w.bw, w.tw, dt, d.data_ptr(), e.data_ptr(), sp)
         if sev is not None:
             sev[1].record(stream)
+
+    def per_pass(reps=3):
+        """Each pass in a launch of its own (bb_run_pass): median ms per pass."""
+        ms = [[] for _ in range(info.passes)]
+        for _ in range(reps):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(info.passes)]
+            bbm.bb_pack(tb.data_ptr(), tb.stride(0), w.n, w.bw, w.tw, dt, wp, wn, sp)
+            for p in range(info.passes):
+                evs[p][0].record(stream)
+                bbm.bb_run_pass(w.n, w.bw, w.tw, dt, p, wp, wn, tun, sp)
+                evs[p][1].record(stream)
+            torch.cuda.synchronize()
+            for p in range(info.passes):
+                ms[p].append(evs[p][0].elapsed_time(evs[p][1]))
+        return [statistics.median(x) for x in ms]
 
     if args.copy_probe_mib:
         nb = args.copy_probe_mib << 20
@@ -525,26 +552,26 @@ def main():
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(info.passes)]
-          for _ in range(args.steps)]
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        one(ev[s], sev[s])
+        one(rev[s], sev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     status = bbm.bb_device_status(wp, w.n, w.bw, w.tw, dt, sp)
-    pass_ms = [[ev[s][p][0].elapsed_time(ev[s][p][1]) for s in range(args.steps)] for p in range(info.passes)]
+    run_ms = [a.elapsed_time(b) for (a, b) in rev]
     step_ms = [a.elapsed_time(b) for (a, b) in sev]
     ms_per_step = wall * 1e3 / args.steps
     value = info.alg_bytes / (ms_per_step * 1e-3) / 1e9
-    # dominant kernel: the cycle kernel, one launch per pass; algorithmic
-    # bytes per launch over the average launch duration
-    launches = info.passes * args.steps
-    avg_launch_ms = sum(sum(x) for x in pass_ms) / launches
-    bytes_per_launch = sum(p[2] for p in passes) / info.passes
+    # dominant kernel: the cycle kernel; algorithmic bytes per launch over the
+    # average launch duration (the passes' event time over the launches)
+    launches = nlaunch * args.steps
+    avg_launch_ms = sum(run_ms) / launches
+    bytes_per_launch = sum(p[2] for p in passes) / nlaunch
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    pass_ms = None if args.no_per_pass else per_pass()
     traffic = stored_traffic(w.name)
 
     out = {
@@ -568,13 +595,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 5),
                      "traffic": None if traffic is None else round(traffic["hbm_bytes_per_launch"], 1),
-                     "kernel": "cycle kernel (k_group where the pass's LDS ring fits, else k_persist), "
-                               "one launch per pass",
+                     "kernel": "cycle kernel (k_group where the pass's LDS ring fits, consecutive such passes "
+                               "in one launch; else k_persist, one launch per pass)",
                      "launches": launches, "avg_launch_ms": round(avg_launch_ms, 4),
                      "alg_bytes_per_launch": bytes_per_launch},
         "ms_per_reduction_events": {"median": round(statistics.median(step_ms), 4), "min": round(min(step_ms), 4)},
-        "passes": [{"b": b, "t": t, "alg_bytes": ab, "median_ms": round(statistics.median(pass_ms[i]), 4),
-                    "GBps": round(ab / (statistics.median(pass_ms[i]) * 1e-3) / 1e9, 2)}
+        "launch_of_pass": launch_of,
+        # each pass in a launch of its own, timed after the steps
+        "passes": [{"b": b, "t": t, "alg_bytes": ab} if pass_ms is None else
+                   {"b": b, "t": t, "alg_bytes": ab, "median_ms": round(pass_ms[i], 4),
+                    "GBps": round(ab / (pass_ms[i] * 1e-3) / 1e9, 2)}
                    for i, (b, t, ab) in enumerate(passes)],
     }
     if not args.no_ceiling:
@@ -584,6 +614,8 @@ def main():
     if not args.no_schedulers:
         out["schedulers_ms"] = scheduler_times(bbm, torch, tb, w, dt, work, stream)
         out["schedulers_ms"]["default"] = round(statistics.median(step_ms), 3)
+        if pass_ms is not None:
+            out["schedulers_ms"]["group_per_pass"] = round(sum(pass_ms), 3)
     if not args.no_svals:
         out["svals"] = measure_svals(bbm, torch, d, e, w, args.steps, stream, args.cpu_seconds / 3, not args.no_cpu)
     if not args.no_f16:

@@ -67,7 +67,9 @@ typedef enum {
   BB_SCHED_PERSISTENT = 2, /* resident workgroups; per-sweep progress counters */
   BB_SCHED_GROUP = 3       /* resident workgroups each running a group of
                               consecutive sweeps on a ring of band rows in LDS;
-                              passes whose ring does not fit run PERSISTENT */
+                              passes whose ring does not fit run PERSISTENT;
+                              one launch per pass (DEFAULT also lets
+                              consecutive group passes share a launch) */
 } bb_scheduler;
 
 /* Optional tuning; pass NULL for the gfx950 defaults.  Zero fields take the
@@ -128,8 +130,10 @@ bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, in
 
 /*
  * The three stages bb_reduce runs, for callers that time or interleave them:
- * bb_pack, then bb_run_pass for pass = 0 .. passes-1 in order, then
- * bb_extract, all on one stream, equal bb_reduce with the same arguments.
+ * bb_pack, then bb_run_passes over passes 0 .. passes-1 (in one call, or
+ * split into consecutive ranges, or bb_run_pass for each pass in order), then
+ * bb_extract, all on one stream, equal bb_reduce with the same arguments
+ * (bit for bit, however the passes are split).
  *
  * bb_pack: resets the counters in `work` and copies the caller's band (same
  *   layout and requirements as bb_reduce's `band`, `ld_band`) into the
@@ -139,6 +143,14 @@ bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, in
  *   Bidiagonalization of Banded Matrices through Memory-Aware Bulge-Chasing
  *   on GPUs", tile-width passage) on the working band in `work`; every
  *   earlier pass must have run on it.  tuning as for bb_reduce.
+ * bb_run_passes: runs passes first .. first+count-1 (count >= 0) in order,
+ *   as bb_run_pass would one by one.  Under BB_SCHED_DEFAULT, consecutive
+ *   passes that run on the LDS group kernel with register tiles of one
+ *   family (8/9 or 16/17 entries) share one launch, at most 8 passes each:
+ *   the first sweep group of a pass starts on rows the previous pass is done
+ *   with while that pass still runs (each row's owner in the previous pass
+ *   publishes when it is done with the row).  bb_run_pass never shares a
+ *   launch.
  * bb_extract: writes d and e (as for bb_reduce) from the working band.
  * Errors: BB_ERR_ARG (also for pass out of range), BB_ERR_WORKSPACE,
  * BB_ERR_UNSUPPORTED, BB_ERR_HIP.
@@ -147,8 +159,19 @@ bb_status bb_pack(const void *band, int64_t ld_band, int64_t n, int32_t bw, int3
                   size_t work_bytes, void *stream);
 bb_status bb_run_pass(int64_t n, int32_t bw, int32_t tw, int32_t dtype, int32_t pass, void *work, size_t work_bytes,
                       const bb_tuning *tuning, void *stream);
+bb_status bb_run_passes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, int32_t first, int32_t count, void *work,
+                        size_t work_bytes, const bb_tuning *tuning, void *stream);
 bb_status bb_extract(const void *work, size_t work_bytes, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *d,
                      void *e, void *stream);
+
+/* The cycle-kernel launches bb_run_passes makes for all passes with this
+ * tuning (host only, no device work): *launches = their number; when
+ * capacity > 0 (it must then be >= the number of passes), launch_of_pass[p] =
+ * the index of the launch that runs pass p, -1 for a pass without sweeps.
+ * launch_of_pass, launches: host pointers.  Errors: BB_ERR_ARG,
+ * BB_ERR_UNSUPPORTED. */
+bb_status bb_launch_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const bb_tuning *tuning,
+                         int32_t *launch_of_pass, int32_t capacity, int32_t *launches);
 
 /* Copies the working band left in `work` by the last bb_reduce with the same
  * (n, bw, tw, dtype) to dst (device, n * ld elements of dtype; element (i,j)

@@ -104,7 +104,24 @@ def test_scheduler_variants_bitwise(tun, n, bw, tw, dt):
     _check_bitwise(band, bw, tw, bbm.tuning(**tun))
 
 
-@pytest.mark.parametrize("sched", [PERSIST, GROUP])
+# Runs of passes in one launch (the default scheduler): every pass's first
+# group starts on rows the previous pass has released while that pass still
+# runs.  Shapes: four passes in one launch, runs split at four passes (BW 64 /
+# TW 4: 16 passes), mixed tiles (t+1 = 9 then 8, 17 then 16), two rows per
+# lane then one, fp16; few resident workgroups, where a pass's first group
+# waits longest for the previous pass.
+@pytest.mark.parametrize("tun", [dict(), dict(max_blocks=1), dict(max_blocks=3), dict(group_sweeps=2, max_blocks=5)])
+@pytest.mark.parametrize("n,bw,tw,dt", [(900, 64, 16, "f32"), (700, 24, 7, "f64"), (600, 64, 4, "f32"),
+                                        (300, 64, 8, "f32"), (800, 64, 16, "f16"), (640, 40, 13, "f64")])
+def test_fused_passes_bitwise(tun, n, bw, tw, dt):
+    log(f"fused {tun} n={n} bw={bw} tw={tw} {dt}")
+    launches = bbm.bb_launch_plan(n, bw, tw, {"f32": 0, "f64": 1, "f16": 2}[dt], bbm.tuning(**tun))
+    assert len(set(launches)) < len(launches)  # some passes do share a launch
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=n + bw)
+    _check_bitwise(band, bw, tw, bbm.tuning(**tun))
+
+
+@pytest.mark.parametrize("sched", [PERSIST, GROUP, bbm.BB_SCHED_DEFAULT])
 def test_forced_timeout_reports_status(sched):
     # A spin limit of one poll makes the first wait on a predecessor expire;
     # every workgroup then stops and the launch ends normally.
@@ -214,5 +231,15 @@ def test_staged_calls_equal_reduce(n, bw, tw, dt, sched):
     bbm.bb_extract(work.data_ptr(), work.numel(), n, bw, tw, code, d.data_ptr(), e.data_ptr(), st)
     torch.cuda.synchronize()
     rd, re = gpu_reduce(band, bw, tw, tun)
+    np.testing.assert_array_equal(d.cpu().numpy(), rd)
+    np.testing.assert_array_equal(e.cpu().numpy(), re)
+    # the passes in ranges (the default scheduler shares a launch within each)
+    bbm.bb_pack(tb.data_ptr(), tb.stride(0), n, bw, tw, code, work.data_ptr(), work.numel(), st)
+    half = info.passes // 2
+    bbm.bb_run_passes(n, bw, tw, code, 0, half, work.data_ptr(), work.numel(), None, st)
+    bbm.bb_run_passes(n, bw, tw, code, half, 0, work.data_ptr(), work.numel(), None, st)
+    bbm.bb_run_passes(n, bw, tw, code, half, info.passes - half, work.data_ptr(), work.numel(), None, st)
+    bbm.bb_extract(work.data_ptr(), work.numel(), n, bw, tw, code, d.data_ptr(), e.data_ptr(), st)
+    torch.cuda.synchronize()
     np.testing.assert_array_equal(d.cpu().numpy(), rd)
     np.testing.assert_array_equal(e.cpu().numpy(), re)

@@ -147,8 +147,8 @@ def group_ring_rows(n, b, t, G):
 
 
 class Group:
-    def __init__(self, g, G, ns, n, b, t):
-        self.g, self.R0 = g, g * G
+    def __init__(self, g, G, ns, n, b, t, p=0):
+        self.g, self.R0, self.b, self.t, self.p = g, g * G, b, t, p
         self.Gg = min(G, ns - self.R0)
         self.K = [cycles_of_sweep(n, b, t, self.R0 + j) for j in range(self.Gg)]
         self.Kp = [cycles_of_sweep(n, b, t, self.R0 + j - 1) if j > 0 else 0 for j in range(self.Gg)]
@@ -172,7 +172,20 @@ def lag_steps(b, t, marks):
 
 def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True, early=0, first=1, steps=None,
             all_marks=False):
-    """early: 0, every half formed and applied after its waits; 1, a sweep
+    """One pass (b, t): see emulate_run."""
+    return emulate_run(A, [(b, t)], G, W, rng, max_live=max_live, wait_for_prev=wait_for_prev, early=early,
+                       first=first, steps=steps, all_marks=all_marks)
+
+
+def emulate_run(A, passes, G, W, rng, max_live=None, wait_for_prev=True, early=0, first=1, steps=None,
+                all_marks=False, cross=True, batch=None):
+    """A run of passes in one launch: the groups of every pass in one claim
+    order (pass by pass; max_live of them resident at a time; G, sweeps per
+    group, one for all passes or one per pass).  The first
+    group of a pass after the first loads rows [loaded, want), want =
+    loaded + batch, only below X of the previous pass's group that owns row
+    want - 1 (cross = False plants a mistake: it loads without waiting).
+    early: 0, every half formed and applied after its waits; 1, a sweep
     forms the reflector of its next half (q >= 1) as soon as it has
     published the previous one, before waiting for its predecessor; 2, as 1
     and also writes that half's pivot (beta, zeros) then, and publishes that
@@ -182,15 +195,32 @@ def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True, early=0, firs
     predecessor steps is 2q + steps (default lag_steps; a smaller value
     plants a mistake).  all_marks: publish first-part steps for b' >= 3 too."""
     n = A.shape[0]
-    ls = lag_steps(b, t, early == 2) if steps is None else steps
-    mark = early == 2 and (b - t <= 2 or all_marks)
-    ns = max(n - (b - t) - 1, 0)
+    batch = batch or n
+    Gs = G if isinstance(G, (list, tuple)) else [G] * len(passes)   # sweeps per group, per pass
     mem = {i: A[i].copy() for i in range(n)}
-    groups = [Group(g, G, ns, n, b, t) for g in range((ns + G - 1) // G)]
+    groups, first_of = [], []
+    for p, (b, t) in enumerate(passes):
+        ns = max(n - (b - t) - 1, 0)
+        first_of.append(len(groups))
+        groups += [Group(g, Gs[p], ns, n, b, t, p) for g in range((ns + Gs[p] - 1) // Gs[p])]
+    first_of.append(len(groups))
     started = 0 if max_live else len(groups)
 
-    def xprev(gr):
-        return n if gr.g == 0 or not wait_for_prev else groups[gr.g - 1].X
+    def index(gr):
+        return first_of[gr.p] + gr.g
+
+    def xprev(gr, want):
+        if not wait_for_prev or (gr.p == 0 and gr.g == 0):
+            return n
+        if gr.g > 0:
+            return groups[index(gr) - 1].X
+        if not cross:
+            return n
+        lo, hi = first_of[gr.p - 1], first_of[gr.p]      # the previous pass's groups
+        if lo == hi:
+            return n
+        q = min((want - 1) // Gs[gr.p - 1], hi - lo - 1)
+        return groups[lo + q].X
 
     def finished(gr):
         return gr.X >= n
@@ -205,6 +235,8 @@ def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True, early=0, firs
             break
         actions = []
         for gr in live:
+            b, t = gr.b, gr.t
+            ls = lag_steps(b, t, early == 2) if steps is None else steps
             for j in range(gr.Gg):
                 q = gr.done[j]
                 published = gr.prog[j] >= 2 * q      # half q-1 published (prog counts steps)
@@ -222,14 +254,16 @@ def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True, early=0, firs
             dead = min(gr.floor) if gr.Gg else n
             if min(dead, gr.loaded) > gr.written:
                 actions.append(("writeback", gr, None))
-            lim = min(xprev(gr), gr.written + W, n)
+            want = min(n, gr.loaded + batch)
+            lim = min(xprev(gr, want), gr.written + W, want)
             if lim > gr.loaded:
                 actions.append(("load", gr, None))
-            if min(gr.written, xprev(gr)) > gr.X:
+            if gr.written > max(gr.X, gr.R0):               # X moves only past rows written back
                 actions.append(("announce", gr, None))
         if not actions:
             raise RuntimeError("deadlock")
         kind, gr, j = actions[rng.integers(len(actions))]
+        b, t = gr.b, gr.t
         if kind == "half":
             R, q = gr.R0 + j, gr.done[j]
             lo, hi = half_rows(n, b, t, R, q)
@@ -245,7 +279,7 @@ def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True, early=0, firs
             lo, hi = (r, r) if h == 0 else (c, ch)    # the entries that form the reflector
             assert all(i in gr.lds for i in range(lo, hi + 1)) and lo >= gr.written
             gr.prep[j] = prep_half(gr.lds, n, b, t, R, q, write_pivot=(early == 2))
-            if mark:
+            if early == 2 and (b - t <= 2 or all_marks):
                 gr.prog[j] = 2 * q + 1
         elif kind == "publish":
             q = gr.done[j]
@@ -257,13 +291,14 @@ def emulate(A, b, t, G, W, rng, max_live=None, wait_for_prev=True, early=0, firs
                 mem[i] = gr.lds.pop(i).copy()
             gr.written = wb
         elif kind == "load":
-            lim = min(xprev(gr), gr.written + W, n)
+            want = min(n, gr.loaded + batch)
+            lim = min(xprev(gr, want), gr.written + W, want)
             for i in range(gr.loaded, lim):
                 gr.lds[i] = mem[i].copy()
             gr.loaded = lim
             assert len(gr.lds) <= W
         else:
-            gr.X = min(gr.written, xprev(gr))
+            gr.X = gr.written
     return np.array([mem[i] for i in range(n)])
 
 
@@ -342,6 +377,53 @@ def test_emulation_detects_a_short_wait(n, bw, tw, G):
         try:
             out = emulate(A, b, t, G, W, np.random.default_rng(trial), early=2, all_marks=True,
                           steps=lag_steps(b, t, True) - 1)
+        except (RuntimeError, AssertionError):
+            bad += 1
+            continue
+        bad += not np.array_equal(out, ref)
+    assert bad > 0
+
+
+RUNS = [(40, 8, 3, [2, 3, 2]), (48, 16, 5, [3, 2, 4, 3]), (45, 12, 4, 3), (36, 9, 8, [2, 4]), (50, 10, 2, 2),
+        (30, 16, 15, [3, 2])]
+
+
+@pytest.mark.parametrize("n,bw,tw,G", RUNS)
+def test_run_of_passes_matches_sequential(n, bw, tw, G):
+    # every pass of the band in one launch: a pass's first group starts on
+    # the rows the previous pass has released while that pass still runs
+    # (small load batches, so that a batch's owner in the previous pass
+    # changes often; few resident groups, so that claims wait)
+    rng = np.random.default_rng(n * 7 + bw)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    passes = pass_list(bw, tw)
+    Gs = G if isinstance(G, list) else [G] * len(passes)
+    Gs = (Gs * len(passes))[:len(passes)]
+    ref = A
+    for (b, t) in passes:
+        ref = sequential(ref, b, t)
+    W = max(group_ring_rows(n, b, t, g) for (b, t), g in zip(passes, Gs)) + 2
+    for trial in range(3):
+        out = emulate_run(A, passes, Gs, W, np.random.default_rng(trial), early=2, batch=[3, 5, 64][trial],
+                          max_live=[None, 2, 3][trial])
+        assert np.array_equal(out, ref), trial
+
+
+def test_run_detects_a_missing_cross_pass_wait():
+    # the first group of a pass loading rows before the previous pass has
+    # released them gives wrong results
+    n, bw, tw = 40, 8, 3
+    rng = np.random.default_rng(5)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    passes = pass_list(bw, tw)
+    ref = A
+    for (b, t) in passes:
+        ref = sequential(ref, b, t)
+    W = max(group_ring_rows(n, b, t, 2) for (b, t) in passes) + 2
+    bad = 0
+    for trial in range(5):
+        try:
+            out = emulate_run(A, passes, 2, W, np.random.default_rng(trial), early=2, batch=4, cross=False)
         except (RuntimeError, AssertionError):
             bad += 1
             continue
