@@ -248,8 +248,9 @@ def measure_f16(bbm, torch, w, steps, stream):
     status = bbm.bb_device_status(work.data_ptr(), w.n, w.bw, w.tw, bbm.BB_F16, stream.cuda_stream)
     gbps = info.alg_bytes / (ms * 1e-3) / 1e9
     return {"workload": f"n{w.n}-bw{w.bw}-tw{w.tw}-f16-{w.dist}", "ms": round(ms, 3), "GBps": round(gbps, 2),
-            "alg_bytes": info.alg_bytes, "kernel": "k_group<_Float16> where the pass's LDS ring fits, "
-                                                 "else k_persist<_Float16>; one launch per pass",
+            "alg_bytes": info.alg_bytes, "kernel": "k_group<_Float16> where the pass's LDS ring fits "
+                                                 "(consecutive such passes in one launch), else "
+                                                 "k_persist<_Float16>",
             "device_status": bbm.bb_status_str(status),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 5),
