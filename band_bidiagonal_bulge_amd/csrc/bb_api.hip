@@ -334,30 +334,9 @@ GroupPlan sym_group_plan(const bb::SymGeometry &g, const bb::Pass &p, int reques
   return gp;
 }
 
-bb_status run_sym_pass(void *work, const bb::SymGeometry &g, const bb::Pass &p, const bb_tuning &tu,
-                       hipStream_t st) {
-  uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
+bb_status run_sym_persistent_pass(void *work, const bb::SymGeometry &g, const bb::Pass &p, const bb_tuning &tu,
+                                  uint32_t *sync, hipStream_t st) {
   const int64_t ns = bb::sweeps_of(g.n, p);
-  if (ns == 0) return BB_OK;
-  if (tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP) {
-    const GroupPlan gp = sym_group_plan(g, p, tu.group_sweeps);
-    if (gp.G > 0) {
-      const int64_t ngroups = (ns + gp.G - 1) / gp.G;
-      if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
-          bb::launch_fill_u32(sync + bb::kSyncHeader, ngroups * bb::kLine, 0u, st) != hipSuccess)
-        return BB_ERR_HIP;
-      int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
-      grid = std::min<int64_t>(grid, ngroups);
-      const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
-      bb::GroupRun run{};
-      run.npass = 1;
-      run.total = int32_t(ngroups);
-      run.gmax = gp.G;
-      run.maxm = sym_maxm(p.t);
-      run.pass[0] = bb::group_pass_word(p.b, p.t, gp.G, 0);
-      return hip_status(bb::launch_sym_group(run, work, g, gp.W, sync, int(grid), spin, st));
-    }
-  }
   if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
       bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
     return BB_ERR_HIP;
@@ -366,6 +345,66 @@ bb_status run_sym_pass(void *work, const bb::SymGeometry &g, const bb::Pass &p, 
   grid = std::min<int64_t>(grid, ns);
   const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
   return hip_status(bb::launch_sym_persist(sym_maxm(p.t), work, g, p.b, p.t, ns, sync, int(grid), nt, spin, st));
+}
+
+// The symmetric passes in order: the group kernel where a pass's ring fits
+// (else the persistent kernel), under the default scheduler with runs of
+// consecutive such passes of one register tile in one launch, as for the
+// general band (plan_launches).
+bb_status run_sym_passes(void *work, const bb::SymGeometry &g, const std::vector<bb::Pass> &passes,
+                         const bb_tuning &tu, hipStream_t st) {
+  uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
+  const bool may_group = tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP;
+  const bool fuse = tu.scheduler == BB_SCHED_DEFAULT;
+  std::vector<LaunchItem> items;
+  for (int i = 0; i < int(passes.size()); ++i) {
+    const bb::Pass &p = passes[size_t(i)];
+    const int64_t ns = bb::sweeps_of(g.n, p);
+    if (ns == 0) continue;
+    const GroupPlan gp = may_group ? sym_group_plan(g, p, tu.group_sweeps) : GroupPlan{};
+    if (gp.G == 0) {
+      LaunchItem it;
+      it.first = i;
+      it.count = 1;
+      items.push_back(it);
+      continue;
+    }
+    const int64_t ngroups = (ns + gp.G - 1) / gp.G;
+    LaunchItem *cur = items.empty() ? nullptr : &items.back();
+    const bool join = fuse && cur && cur->group && cur->first + cur->count == i &&
+                      cur->run.npass < bb::kMaxRunPasses && cur->run.maxm == sym_maxm(p.t) && cur->W == gp.W &&
+                      cur->run.total + ngroups <= g.n + 1;
+    if (!join) {
+      items.emplace_back();
+      cur = &items.back();
+      cur->group = true;
+      cur->first = i;
+      cur->W = gp.W;
+      cur->run.maxm = sym_maxm(p.t);
+    }
+    cur->run.pass[cur->run.npass] = bb::group_pass_word(p.b, p.t, gp.G, 0);
+    cur->run.base[cur->run.npass] = cur->run.total;
+    ++cur->run.npass;
+    cur->run.total += int32_t(ngroups);
+    cur->run.gmax = std::max(cur->run.gmax, gp.G);
+    cur->count = i - cur->first + 1;
+  }
+  for (const LaunchItem &it : items) {
+    bb_status rc = BB_OK;
+    if (it.group) {
+      if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
+          bb::launch_fill_u32(sync + bb::kSyncHeader, int64_t(it.run.total) * bb::kLine, 0u, st) != hipSuccess)
+        return BB_ERR_HIP;
+      int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
+      grid = std::min<int64_t>(grid, it.run.total);
+      const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+      rc = hip_status(bb::launch_sym_group(it.run, work, g, it.W, sync, int(grid), spin, st));
+    } else {
+      rc = run_sym_persistent_pass(work, g, passes[size_t(it.first)], tu, sync, st);
+    }
+    if (rc != BB_OK) return rc;
+  }
+  return BB_OK;
 }
 
 // Bisection of the Golub-Kahan tridiagonal: sizes, and how it is split.
@@ -447,8 +486,7 @@ bb_status bb_sym_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw
   if (bb::launch_sym_pack(band, ld_band, work, g, st) != hipSuccess ||
       bb::launch_fill_u32(sync, int64_t(g.sync_words), 0u, st) != hipSuccess)
     return BB_ERR_HIP;
-  for (const bb::Pass &p : bb::pass_list(bw, tw))
-    if ((rc = run_sym_pass(work, g, p, tu, st)) != BB_OK) return rc;
+  if ((rc = run_sym_passes(work, g, bb::pass_list(bw, tw), tu, st)) != BB_OK) return rc;
   return hip_status(bb::launch_sym_extract(work, g, d, n > 1 ? e : nullptr, st));
 }
 

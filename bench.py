@@ -216,7 +216,7 @@ def measure_sym(bbm, torch, steps, stream, with_cpu):
         entry = {"workload": f"sym-n{n}-bw{bw}-tw{tw}-{dt}-normal", "ms": round(ms, 3), "GBps": round(gbps, 2),
                  "alg_bytes": total, "passes": len(passes), "device_status": bbm.bb_status_str(status),
                  "kernel": "symmetric cycle kernel (k_group with the symmetric half-cycles where the pass's LDS "
-                           "ring fits, else k_sym_persist), one launch per pass",
+                           "ring fits, consecutive such passes in one launch; else k_sym_persist)",
                  "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(gbps / HBM_PEAK_GBPS, 5),
                               "note": "whole reduction over its wall time (the launches are back to back)"}}

@@ -103,13 +103,29 @@ def test_group_and_persistent_agree_to_the_bit(n, bw, tw, dt):
     np.testing.assert_array_equal(eg, oe)
 
 
+@pytest.mark.parametrize("n,bw,tw,dt", [(700, 64, 16, "f32"), (500, 64, 8, "f32"), (400, 24, 8, "f64"),
+                                        (300, 12, 2, "f32")])
+@pytest.mark.parametrize("blocks", [0, 2])
+def test_passes_in_one_launch_to_the_bit(n, bw, tw, dt, blocks):
+    # the default scheduler runs consecutive group passes in one launch (at
+    # most four); the result equals the oracle's and one launch per pass
+    log(f"sym fused n={n} bw={bw} tw={tw} {dt} blocks={blocks}")
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=3 * n + bw)
+    df, ef, Wf = gpu_sym(band, bw, tw, bbm.tuning(max_blocks=blocks), return_band=True)
+    dg, eg, Wg = gpu_sym(band, bw, tw, bbm.tuning(scheduler=bbm.BB_SCHED_GROUP), return_band=True)
+    np.testing.assert_array_equal(Wf, Wg)
+    od, oe = oracle.sym_reduce(band, bw, tw)
+    np.testing.assert_array_equal(df, od)
+    np.testing.assert_array_equal(ef, oe)
+
+
 def test_forced_timeout_is_reported():
     import torch
     n, bw, tw = 400, 16, 8
     log("sym forced timeout")
     band = torch.from_numpy(bb_inputs.make_band(n, bw, "f32", "normal", seed=1)).to("cuda:0")
     work = bbm.sym_workspace(n, bw, tw, band.dtype, band.device)
-    for sched in (bbm.BB_SCHED_PERSISTENT, bbm.BB_SCHED_GROUP):
+    for sched in (bbm.BB_SCHED_PERSISTENT, bbm.BB_SCHED_GROUP, bbm.BB_SCHED_DEFAULT):
         bbm.sym_reduce(band, bw, tw, bbm.tuning(scheduler=sched, spin_limit=1), work)
         st = bbm.bb_sym_device_status(work.data_ptr(), n, bw, tw, bbm.BB_F32,
                                       torch.cuda.current_stream().cuda_stream)

@@ -144,8 +144,8 @@ def sym_group_ring_rows(n, b, t, G):
 
 
 class Group:
-    def __init__(self, g, G, ns, n, b, t):
-        self.g, self.R0 = g, g * G
+    def __init__(self, g, G, ns, n, b, t, p=0):
+        self.g, self.R0, self.b, self.t, self.p = g, g * G, b, t, p
         self.Gg = min(G, ns - self.R0)
         self.K = [2 * cycles_of(n, b, t, self.R0 + j) for j in range(self.Gg)]
         self.Kp = [2 * cycles_of(n, b, t, self.R0 + j - 1) if j > 0 else 0 for j in range(self.Gg)]
@@ -161,7 +161,20 @@ class Group:
 
 
 def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2, all_marks=False, steps=None):
-    """early: a sweep runs half A's first part (reflector and pivot) as soon
+    """One pass (b, t): see emulate_run."""
+    return emulate_run(A, [(b, t)], G, W, rng, max_live=max_live, d=d, early=early, first=first,
+                       all_marks=all_marks, steps=steps)
+
+
+def emulate_run(A, passes, G, W, rng, max_live=None, d=None, early=False, first=2, all_marks=False, steps=None,
+                cross=True, batch=None):
+    """A run of passes in one launch: the groups of every pass in one claim
+    order, pass by pass (max_live of them resident at a time; G, sweeps per
+    group, one for all passes or one per pass).  The first group of a pass
+    after the first loads rows [loaded, want), want = loaded + batch, only
+    below X of the previous pass's group that owns row want - 1 (cross =
+    False plants a mistake: it loads without waiting).
+    early: a sweep runs half A's first part (reflector and pivot) as soon
     as it has published the half before it, ahead of its waits (the kernel's
     schedule), for every half A from half `first` on (2; 0 plants a mistake:
     half 0's pivot row comes from the predecessor), and for b' <= 2 (or every
@@ -170,13 +183,29 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2, all
     predecessor, steps = 2d - 1 with first-part steps, else 2d (d: the lag
     in halves, default lag(b, t))."""
     n = A.shape[0]
-    L = lag(b, t) if d is None else d   # half-cycles
-    mark = early and (b - t <= 2 or all_marks)
-    LS = (2 * L - 1 if mark else 2 * L) if steps is None else steps
-    ns = max(n - (b - t) - 1, 0)
+    batch = batch or n
+    Gs = G if isinstance(G, (list, tuple)) else [G] * len(passes)
     mem = {i: A[i].copy() for i in range(n)}
-    groups = [Group(g, G, ns, n, b, t) for g in range((ns + G - 1) // G)]
+    groups, first_of = [], []
+    for p, (b, t) in enumerate(passes):
+        ns = max(n - (b - t) - 1, 0)
+        first_of.append(len(groups))
+        groups += [Group(g, Gs[p], ns, n, b, t, p) for g in range((ns + Gs[p] - 1) // Gs[p])]
+    first_of.append(len(groups))
     started = 0 if max_live else len(groups)
+
+    def xprev(gr, want):
+        if gr.p == 0 and gr.g == 0:
+            return n
+        if gr.g > 0:
+            return groups[first_of[gr.p] + gr.g - 1].X
+        if not cross:
+            return n
+        lo, hi = first_of[gr.p - 1], first_of[gr.p]
+        if lo == hi:
+            return n
+        return groups[lo + min((want - 1) // Gs[gr.p - 1], hi - lo - 1)].X
+
     while True:
         live = [gr for gr in groups[:started] if gr.X < n]
         if max_live and len(live) < max_live and started < len(groups):
@@ -186,7 +215,10 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2, all
             break
         acts = []
         for gr in live:
-            xprev = n if gr.g == 0 else groups[gr.g - 1].X
+            b, t = gr.b, gr.t
+            L = lag(b, t) if d is None else d   # half-cycles
+            mark = early and (b - t <= 2 or all_marks)
+            LS = (2 * L - 1 if mark else 2 * L) if steps is None else steps
             for j in range(gr.Gg):
                 q = gr.done[j]
                 if early and q == gr.prog[j] and q % 2 == 0 and first <= q < gr.K[j] and not gr.pre[j]:
@@ -203,14 +235,15 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2, all
             dead = min(gr.floor) if gr.Gg else n
             if min(dead, gr.loaded) > gr.written:
                 acts.append(("writeback", gr, None))
-            if min(xprev, gr.written + W, n) > gr.loaded:
+            want = min(n, gr.loaded + batch)
+            if min(xprev(gr, want), gr.written + W, want) > gr.loaded:
                 acts.append(("load", gr, None))
-            if min(gr.written, xprev) > gr.X:
+            if gr.written > max(gr.X, gr.R0):             # X moves only past rows written back
                 acts.append(("announce", gr, None))
         if not acts:
             raise RuntimeError("deadlock")
         kind, gr, j = acts[rng.integers(len(acts))]
-        xprev = n if gr.g == 0 else groups[gr.g - 1].X
+        b, t = gr.b, gr.t
         if kind == "cycle":
             R, q = gr.R0 + j, gr.done[j]
             lo, hi = half_rows(n, b, t, R, q)
@@ -224,7 +257,7 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2, all
             assert p in gr.lds and p >= gr.written
             gr.refl[R] = prep_a(gr.lds, n, b, t, R, q)
             gr.pre[j] = True
-            if mark:
+            if early and (b - t <= 2 or all_marks):
                 gr.st[j] = 2 * q + 1
         elif kind == "publish":
             q = gr.done[j]
@@ -237,13 +270,14 @@ def emulate(A, b, t, G, W, rng, max_live=None, d=None, early=False, first=2, all
                 mem[i] = gr.lds.pop(i).copy()
             gr.written = wb
         elif kind == "load":
-            lim = min(xprev, gr.written + W, n)
+            want = min(n, gr.loaded + batch)
+            lim = min(xprev(gr, want), gr.written + W, want)
             for i in range(gr.loaded, lim):
                 gr.lds[i] = mem[i].copy()
             gr.loaded = lim
             assert len(gr.lds) <= W
         else:
-            gr.X = min(gr.written, xprev)
+            gr.X = gr.written
     return np.array([mem[i] for i in range(n)])
 
 
@@ -338,6 +372,45 @@ def test_emulation_detects_a_short_wait(n, bw, tw, G):
     for trial in range(6):
         try:
             out = emulate(A, b, t, G, W, np.random.default_rng(trial), early=True, all_marks=True, steps=ls - 1)
+        except (RuntimeError, AssertionError):
+            bad += 1
+            continue
+        bad += not np.array_equal(out, ref)
+    assert bad > 0
+
+
+@pytest.mark.parametrize("n,bw,tw,G", [(40, 8, 3, [2, 3, 2]), (36, 6, 2, 3), (45, 12, 5, [3, 2, 4]), (30, 9, 8, 2)])
+def test_sym_run_of_passes_matches_sequential(n, bw, tw, G):
+    # every pass in one launch: a pass's first group loads each row once the
+    # previous pass's group that owns it has released it
+    rng = np.random.default_rng(n * 3 + bw)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    passes = pass_list(bw, tw)
+    Gs = G if isinstance(G, list) else [G] * len(passes)
+    Gs = (Gs * len(passes))[:len(passes)]
+    ref = A
+    for (b, t) in passes:
+        ref = sequential(ref, b, t)
+    W = max(sym_group_ring_rows(n, b, t, g) for (b, t), g in zip(passes, Gs)) + 2
+    for trial in range(3):
+        out = emulate_run(A, passes, Gs, W, np.random.default_rng(trial), early=True, batch=[3, 5, 64][trial],
+                          max_live=[None, 2, 3][trial])
+        assert np.array_equal(out, ref), trial
+
+
+def test_sym_run_detects_a_missing_cross_pass_wait():
+    n, bw, tw = 40, 8, 3
+    rng = np.random.default_rng(6)
+    A = np.triu(np.tril(rng.standard_normal((n, n)), bw))
+    passes = pass_list(bw, tw)
+    ref = A
+    for (b, t) in passes:
+        ref = sequential(ref, b, t)
+    W = max(sym_group_ring_rows(n, b, t, 2) for (b, t) in passes) + 2
+    bad = 0
+    for trial in range(5):
+        try:
+            out = emulate_run(A, passes, 2, W, np.random.default_rng(trial), early=True, batch=4, cross=False)
         except (RuntimeError, AssertionError):
             bad += 1
             continue
