@@ -627,6 +627,7 @@ bb_status bb_launch_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const
   bb_tuning tu;
   bb_status rc = check_tuning(tuning, &tu);
   if (rc != BB_OK) return rc;
+  if (dtype == BB_F16 && tu.scheduler == BB_SCHED_STEP) return BB_ERR_UNSUPPORTED;  // as bb_run_passes
   const std::vector<bb::Pass> passes = bb::pass_list(bw, tw);
   if (capacity > 0 && capacity < int32_t(passes.size())) return BB_ERR_ARG;
   const std::vector<LaunchItem> items = plan_launches(g, passes, 0, int(passes.size()), tu);

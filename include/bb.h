@@ -169,7 +169,7 @@ bb_status bb_extract(const void *work, size_t work_bytes, int64_t n, int32_t bw,
  * capacity > 0 (it must then be >= the number of passes), launch_of_pass[p] =
  * the index of the launch that runs pass p, -1 for a pass without sweeps.
  * launch_of_pass, launches: host pointers.  Errors: BB_ERR_ARG,
- * BB_ERR_UNSUPPORTED. */
+ * BB_ERR_UNSUPPORTED (also fp16 with BB_SCHED_STEP, as bb_run_passes). */
 bb_status bb_launch_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const bb_tuning *tuning,
                          int32_t *launch_of_pass, int32_t capacity, int32_t *launches);
 

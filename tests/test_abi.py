@@ -134,6 +134,12 @@ def test_staged_entry_points_validate_on_host():
     assert L.bb_run_pass(10, 4, 2, 0, 0, fake, 16, None, None) == _lib.BB_ERR_WORKSPACE
     bad = _lib.bb_tuning(9, 0, 0, 0, 0)
     assert L.bb_run_pass(10, 4, 2, 0, 0, fake, big, ctypes.byref(bad), None) == _lib.BB_ERR_ARG
+    # bb_run_passes: the range must lie within the passes; an empty range
+    # launches nothing
+    for (first, count) in ((-1, 1), (0, -1), (0, 3), (2, 1), (1, 2)):
+        assert L.bb_run_passes(10, 4, 2, 0, first, count, fake, big, None, None) == _lib.BB_ERR_ARG
+    assert L.bb_run_passes(10, 4, 2, 0, 1, 0, fake, big, None, None) == _lib.BB_OK
+    assert L.bb_run_passes(10, 4, 2, 0, 0, 2, fake, 16, None, None) == _lib.BB_ERR_WORKSPACE
     # bb_extract: null d, null e with n > 1, misaligned d
     assert L.bb_extract(fake, big, 10, 4, 2, 0, None, fake, None) == _lib.BB_ERR_ARG
     assert L.bb_extract(fake, big, 10, 4, 2, 0, fake, None, None) == _lib.BB_ERR_ARG
@@ -193,3 +199,31 @@ def test_sym_and_f16_validation_without_a_gpu():
     tun = bbm.tuning(scheduler=bbm.BB_SCHED_STEP)
     ws = bbm.bb_workspace_bytes(100, 8, 4, bbm.BB_F16)
     assert L.bb_run_pass(100, 8, 4, 2, 0, ctypes.c_void_p(1 << 20), ws, ctypes.byref(tun), None) == 4
+
+
+def test_launch_plan_groups_consecutive_passes():
+    # which cycle-kernel launch runs each pass (host only): under the default
+    # scheduler consecutive group-kernel passes with one tile family share a
+    # launch, at most four; the other schedulers launch once per pass; passes
+    # without sweeps launch nothing
+    plan = bbm.bb_launch_plan
+    sched = [bbm.tuning(scheduler=s) for s in (bbm.BB_SCHED_DEFAULT, bbm.BB_SCHED_STEP, bbm.BB_SCHED_PERSISTENT,
+                                               bbm.BB_SCHED_GROUP)]
+    assert plan(16384, 64, 16, bbm.BB_F32, sched[0]) == [0, 0, 0, 0]        # tiles 17, 17, 17, 16
+    assert plan(16384, 64, 16, bbm.BB_F16, sched[0]) == [0, 0, 0, 0]
+    assert plan(512, 16, 8, bbm.BB_F64, sched[0]) == [0, 0]                  # tiles 9, 8
+    for tun in sched[1:]:
+        assert plan(16384, 64, 16, bbm.BB_F32, tun) == [0, 1, 2, 3]
+    assert plan(600, 64, 4, bbm.BB_F32, sched[0]) == sum(([k] * 4 for k in range(4)), [])  # 16 passes
+    assert plan(4096, 64, 15, bbm.BB_F32, sched[0]) == [0, 0, 0, 0, 1]     # tiles 16 x 4, then 9 (t = 3)
+    assert plan(32768, 128, 32, bbm.BB_F64, sched[0]) == [0, 1, 2, 3]      # t + 1 = 33: persistent
+    assert plan(5, 8, 2, bbm.BB_F32, sched[0]) == [-1, -1, 0, 0]           # b' >= n - 1: no sweeps
+    L = _lib.lib()
+    count = ctypes.c_int32(-1)
+    assert L.bb_launch_plan(16384, 64, 16, 0, None, None, 0, ctypes.byref(count)) == _lib.BB_OK
+    assert count.value == 1
+    out = (ctypes.c_int32 * 4)()
+    assert L.bb_launch_plan(16384, 64, 16, 0, None, out, 3, ctypes.byref(count)) == _lib.BB_ERR_ARG
+    assert L.bb_launch_plan(16384, 64, 16, 0, None, out, 4, None) == _lib.BB_ERR_ARG
+    assert L.bb_launch_plan(16384, 64, 16, 2, ctypes.byref(sched[1]), out, 4, ctypes.byref(count)) == \
+        _lib.BB_ERR_UNSUPPORTED
