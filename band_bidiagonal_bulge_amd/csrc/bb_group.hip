@@ -834,11 +834,11 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
 // Where a group's loader learns which rows are final: the previous group's
 // release counter X_{g-1} (G = 0), or, for the first group of a pass that
 // follows another in the same launch, the counters of that pass's groups
-// (G sweeps each, ngroups of them, the first at `line`): its group
-// q = min(i / G, ngroups - 1) is the last one to touch row i, and since
-// X_q <= X_{q'} for q' < q, X_q > i means that every group of that pass is
-// done with row i.  line = nullptr: every row is final (the launch's first
-// pass).
+// (G sweeps each, ngroups of them, the first at `line`).  Row i is touched
+// by that pass's groups 0 .. q, q = min(i / G, ngroups - 1), only (a group
+// touches no row below its first sweep), and X_q <= X_{q'} for q' < q, so
+// X_q > i means that all of them are done with row i.  line = nullptr:
+// every row is final (the launch's first pass).
 struct PrevRows {
   const uint32_t *line;
   int32_t G, ngroups;
@@ -951,7 +951,7 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
     const int32_t g = gi - base;
     const int32_t R0 = g * pG;
     const int32_t Gg = min(pG, nsweeps - R0);
-    __syncthreads();  // every wave has read ctl.g before it is reset below
+    __syncthreads();  // every wave has read the claim before thread 0 resets the control words
     if (threadIdx.x == 0) {
       ctl.loaded_hi = R0;
       ctl.written = R0;
