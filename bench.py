@@ -36,6 +36,10 @@ Prints one JSON line:
                   cores (at most 16), on the whole reduction when it fits the
                   time bound, else on its first pass
 
+--pass-ranges prints the ms of each pass alone, of each consecutive pair of
+passes in one launch and of all passes (what sharing a launch gains at each
+pass boundary) instead of the bench line.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -427,6 +431,32 @@ def scheduler_times(bbm, torch, tb, w, dt, work, stream, reps=2):
     return out
 
 
+def pass_ranges(bbm, torch, tb, w, dt, info, wp, wn, stream, reps=3):
+    """Median ms of ranges of passes run by one bb_run_passes call under the
+    default scheduler (consecutive group-kernel passes share a launch): each
+    pass alone, each pair of consecutive passes, and all of them.  The
+    passes before a range run untimed first, so each range starts from the
+    working band it would see in a reduction."""
+    sp = stream.cuda_stream
+    one_each = bbm.tuning(scheduler=bbm.BB_SCHED_GROUP)
+    ranges = [(p, 1) for p in range(info.passes)] + [(p, 2) for p in range(info.passes - 1)] + [(0, info.passes)]
+    out = []
+    for (first, count) in ranges:
+        ms = []
+        for _ in range(reps):
+            bbm.bb_pack(tb.data_ptr(), tb.stride(0), w.n, w.bw, w.tw, dt, wp, wn, sp)
+            if first:
+                bbm.bb_run_passes(w.n, w.bw, w.tw, dt, 0, first, wp, wn, None, sp)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            bbm.bb_run_passes(w.n, w.bw, w.tw, dt, first, count, wp, wn, None if count > 1 else one_each, sp)
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        out.append({"first": first, "count": count, "ms": round(statistics.median(ms), 3)})
+    return out
+
+
 def pass_tables(w):
     """Per pass: (b, t, algorithmic bytes) of the workload."""
     esize = 8 if w.dtype == "f64" else 4
@@ -459,6 +489,8 @@ def main():
     ap.add_argument("--no-f16", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured cache ceiling probe")
     ap.add_argument("--no-schedulers", action="store_true", help="skip the step / persistent scheduler times")
+    ap.add_argument("--pass-ranges", action="store_true",
+                    help="time each pass alone, each consecutive pair in one launch and all passes, then exit")
     ap.add_argument("--no-per-pass", action="store_true",
                     help="skip the per-pass breakdown (each pass in a launch of its own, after the steps)")
     ap.add_argument("--accuracy-study", action="store_true",
@@ -541,6 +573,11 @@ def main():
             for p in range(info.passes):
                 ms[p].append(evs[p][0].elapsed_time(evs[p][1]))
         return [statistics.median(x) for x in ms]
+
+    if args.pass_ranges:
+        print(json.dumps({"workload": w.name, "pass_ranges": pass_ranges(bbm, torch, tb, w, dt, info, wp, wn, stream)}),
+              flush=True)
+        return
 
     if args.copy_probe_mib:
         nb = args.copy_probe_mib << 20
