@@ -143,6 +143,30 @@ def test_forced_timeout_reports_status(sched):
     np.testing.assert_array_equal(d.cpu().numpy(), od)
 
 
+def test_library_loaded_before_torch():
+    # a fresh process whose first call is host-only (it loads libbb.so before
+    # torch has been imported) still reduces on the GPU: the binding imports
+    # torch's HIP runtime first
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys\n"
+        "import band_bidiagonal_bulge_amd as bbm\n"
+        "assert 'torch' not in sys.modules\n"
+        "plan = bbm.bb_launch_plan(300, 24, 8, bbm.BB_F32, None)\n"
+        "import numpy as np, torch, bb_inputs\n"
+        "band = bb_inputs.make_band(300, 24, 'f32', 'normal', seed=4)\n"
+        "d, e = bbm.reduce(torch.from_numpy(band).to('cuda:0'), 24, 8)\n"
+        "torch.cuda.synchronize()\n"
+        "print('ok', plan, float(d.double().abs().sum()))\n")
+    log("fresh process: library loaded before torch")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240,
+                       env=dict(os.environ, PYTHONPATH=root))
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert r.stdout.startswith("ok")
+
+
 def test_repeated_calls_reuse_workspace():
     n, bw, tw = 600, 40, 12
     band = bb_inputs.make_band(n, bw, "f64", "normal", seed=9)
