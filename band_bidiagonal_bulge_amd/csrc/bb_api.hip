@@ -67,6 +67,11 @@ int64_t ceil_div(int64_t a, int64_t b) {  // b > 0
 
 bb_status hip_status(hipError_t e) { return e == hipSuccess ? BB_OK : BB_ERR_HIP; }
 
+// Default block of the step and persistent kernels: one thread per row of
+// a row half and per column of a column half (b + t + 1 each), in whole
+// waves, at most 256.
+int default_threads(const bb::Pass &p) { return std::min(256, std::max(64, (p.b + p.t + 1 + 63) / 64 * 64)); }
+
 bb_status run_step_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
                         hipStream_t st) {
   const int maxm = pick_maxm(p.t);
@@ -74,7 +79,7 @@ bb_status run_step_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, c
   if (ns == 0) return BB_OK;
   const int32_t s = stagger_for(p, tu.stagger);
   int nt = tu.threads_per_block;
-  if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
+  if (nt == 0) nt = default_threads(p);
   const int64_t bp = p.b - p.t;
   const int64_t steps = bb::steps_of(g.n, p, s);
   for (int64_t L = 0; L < steps; ++L) {
@@ -107,7 +112,7 @@ bb_status run_persistent_pass(void *wband, const bb::Geometry &g, const bb::Pass
       bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
     return BB_ERR_HIP;
   int nt = tu.threads_per_block;
-  if (nt == 0) nt = std::min(256, std::max(64, (p.b + p.t + 63) / 64 * 64));
+  if (nt == 0) nt = default_threads(p);
   int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(device_cus());
   grid = std::min<int64_t>(grid, ns);
   const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
