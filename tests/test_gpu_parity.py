@@ -109,12 +109,15 @@ def test_scheduler_variants_bitwise(tun, n, bw, tw, dt):
 # runs.  Shapes: four passes in one launch, runs split at four passes (BW 64 /
 # TW 4: 16 passes), mixed tiles (t+1 = 9 then 8, 17 then 16), two rows per
 # lane then one, fp16, a first pass with the smaller tile and two rows per
-# lane (TW 15 and 7); few resident workgroups, where a pass's first group
-# waits longest for the previous pass.
+# lane (TW 15 and 7), persistent passes before a run (BW 128 and 100: their
+# rings do not fit) and runs split where their groups would exceed the
+# progress lines; few resident workgroups, where a pass's first group waits
+# longest for the previous pass.
 @pytest.mark.parametrize("tun", [dict(), dict(max_blocks=1), dict(max_blocks=3), dict(group_sweeps=2, max_blocks=5)])
 @pytest.mark.parametrize("n,bw,tw,dt", [(900, 64, 16, "f32"), (700, 24, 7, "f64"), (600, 64, 4, "f32"),
                                         (300, 64, 8, "f32"), (800, 64, 16, "f16"), (640, 40, 13, "f64"),
-                                        (500, 64, 15, "f32"), (300, 64, 7, "f16")])
+                                        (500, 64, 15, "f32"), (300, 64, 7, "f16"), (1500, 128, 16, "f32"),
+                                        (900, 100, 16, "f64")])
 def test_fused_passes_bitwise(tun, n, bw, tw, dt):
     log(f"fused {tun} n={n} bw={bw} tw={tw} {dt}")
     launches = bbm.bb_launch_plan(n, bw, tw, {"f32": 0, "f64": 1, "f16": 2}[dt], bbm.tuning(**tun))
