@@ -394,9 +394,9 @@ __device__ __attribute__((noinline)) void ring_row_half_masked(const Ring<T> &A,
   ring_row_apply<T, MAXM, false, true, SC>(A, sr, colr, m, nr, lane, P);
 }
 
-// The rare column halves, both parts, out of line so that the common one
-// keeps its registers: rows that wrap around the ring (about m/W of the
-// halves) and the truncated last cycle of a sweep (m < MAXM).
+// The truncated last cycle of a sweep (m < MAXM), both parts, out of line so
+// that the common path keeps its registers; its rows may also wrap around the
+// ring.
 template <typename T, int MAXM, int SC>
 __device__ __attribute__((noinline)) void ring_col_half_rare(const Ring<T> &A, int32_t sc, int32_t m, int32_t nc,
                                                              int lane) {
@@ -416,8 +416,8 @@ __device__ __attribute__((noinline)) void ring_col_half_rare(const Ring<T> &A, i
   }
 }
 
-// Whether a half takes the common path (full register tile, no wrap for a
-// column half), whose first part may run ahead of the waits.
+// Whether a row half takes the common path (full register tile), whose
+// first part may run ahead of the waits.
 template <int MAXM>
 __device__ __forceinline__ bool row_common(int32_t m, int t) {
   // With an exact register tile (MAXM = t+1) a truncated last cycle
@@ -426,10 +426,7 @@ __device__ __forceinline__ bool row_common(int32_t m, int t) {
   // and update unchanged to the bit, and get +0 written back.
   return m == MAXM || MAXM == t + 1;
 }
-template <typename T, int MAXM>
-__device__ __forceinline__ bool col_common(const Ring<T> &A, int32_t sc, int32_t m) {
-  return m == MAXM && A.W - sc >= MAXM;
-}
+
 
 // One sweep of the group, run by one wave.  Cycle geometry and ring slots
 // advance incrementally (c by b per cycle, the slot of c likewise).
@@ -511,17 +508,33 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
     // is formed before the wait.
     HalfRefl<T, MAXM> Pc;
     T *base = A.L + __umul24(sc, S) + A.sub;
-    const bool col_fast = col_common<T, MAXM>(A, sc, m);
+    // A full column block whose rows run past the end of the ring (rows
+    // c+i, i >= iw, live at the start) takes the same path with per-row
+    // offsets: about MAXM of every W slots, and every sweep of a group meets
+    // it at nearly the same cycle, so it sits on the chain between sweeps.
+    const bool col_fast = m == MAXM;
+    const int32_t iw = A.W - sc;
+    const bool col_wrap = iw < MAXM;
     if (col_fast) {
-      ring_col_prep<T, MAXM, true, false, SC>(A, base, 0, MAXM, lane, Pc);
+      if (col_wrap)
+        ring_col_prep<T, MAXM, true, true, SC>(A, base, iw, MAXM, lane, Pc);
+      else
+        ring_col_prep<T, MAXM, true, false, SC>(A, base, 0, MAXM, lane, Pc);
       publish_first(2 * k + 1, c);
     }
     if (!wait_half(2 * k + 1, ch)) return;
     if (col_fast) {
-      if (TWO == 1 || (TWO == 2 && nc > 64))
+      const bool two = TWO == 1 || (TWO == 2 && nc > 64);
+      if (col_wrap) {
+        if (two)
+          ring_col_apply<T, MAXM, true, true, SC, true>(A, base, iw, MAXM, nc, lane, Pc);
+        else
+          ring_col_apply<T, MAXM, true, false, SC, true>(A, base, iw, MAXM, nc, lane, Pc);
+      } else if (two) {
         ring_col_apply<T, MAXM, true, true, SC, false>(A, base, 0, MAXM, nc, lane, Pc);
-      else
+      } else {
         ring_col_apply<T, MAXM, true, false, SC, false>(A, base, 0, MAXM, nc, lane, Pc);
+      }
     } else {
       ring_col_half_rare<T, MAXM, SC>(A, sc, m, nc, lane);
     }
