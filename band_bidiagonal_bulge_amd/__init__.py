@@ -7,7 +7,7 @@ for device memory and the stream only).
 """
 from __future__ import annotations
 
-from ._lib import (BB_F16, BB_F32, BB_F64, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
+from ._lib import (BB_ERR_TIMEOUT, BB_F16, BB_F32, BB_F64, BB_OK, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
                    BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
                    bb_launch_plan, bb_run_pass, bb_run_passes, bb_status_str, bb_svals, bb_svals_split, bb_svals_workspace_bytes, bb_sym_device_status,
@@ -43,12 +43,22 @@ def workspace(n: int, bw: int, tw: int, torch_dtype, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, stream=None):
-    """Reduces a device band (n, >= bw+1) float32/float64 tensor; returns (d, e).
+def _check_workspace(work, device) -> None:
+    import torch
+    if work.dtype != torch.uint8 or work.dim() != 1 or not work.is_contiguous():
+        raise ValueError("work must be a contiguous 1-D uint8 tensor (sizes are in bytes)")
+    if work.device != device:
+        raise ValueError(f"work is on {work.device}, the band on {device}")
+
+
+def reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, stream=None, check: bool = False):
+    """Reduces a device band (n, >= bw+1) float16/float32/float64 tensor; returns (d, e).
 
     Row i of ``band`` holds A(i, i..i+bw).  Runs on ``stream`` (default: the
     current torch stream) asynchronously.  ``work`` may be a preallocated
-    workspace from :func:`workspace`.
+    workspace from :func:`workspace` (a uint8 tensor on the band's device).
+    With ``check``, waits for the stream and raises :class:`BBError` when a
+    device-side wait expired (BB_ERR_TIMEOUT): d and e are then not valid.
     """
     import torch
     if not band.is_cuda or band.dim() != 2 or band.stride(1) != 1:
@@ -57,11 +67,16 @@ def reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, stre
     dt = dtype_code(band.dtype)
     if work is None:
         work = workspace(n, bw, tw, band.dtype, band.device)
+    _check_workspace(work, band.device)
     d = torch.empty(n, dtype=band.dtype, device=band.device)
     e = torch.empty(max(n - 1, 0), dtype=band.dtype, device=band.device)
     s = stream if stream is not None else torch.cuda.current_stream(band.device)
     bb_reduce(band.data_ptr(), band.stride(0), n, bw, tw, dt, d.data_ptr(), e.data_ptr() if n > 1 else 0,
               work.data_ptr(), work.numel(), tun, s.cuda_stream)
+    if check:
+        st = bb_device_status(work.data_ptr(), n, bw, tw, dt, s.cuda_stream)
+        if st != BB_OK:
+            raise BBError(st, "bb_reduce")
     return d, e
 
 
@@ -105,9 +120,12 @@ def sym_workspace(n: int, bw: int, tw: int, torch_dtype, device="cuda"):
     return torch.empty(bb_sym_workspace_bytes(n, bw, tw, dtype_code(torch_dtype)), dtype=torch.uint8, device=device)
 
 
-def sym_reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, stream=None):
-    """Symmetric band -> tridiagonal of a device band (n, >= bw+1), row i
-    holding A(i, i..i+bw); returns (d, e) device tensors."""
+def sym_reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, stream=None,
+               check: bool = False):
+    """Symmetric band -> tridiagonal of a device band (n, >= bw+1) float32 or
+    float64 tensor, row i holding A(i, i..i+bw); returns (d, e) device
+    tensors.  ``work``: a uint8 tensor on the band's device; ``check`` as for
+    :func:`reduce`."""
     import torch
     if not band.is_cuda or band.dim() != 2 or band.stride(1) != 1:
         raise ValueError("band must be a 2-D device tensor with unit column stride")
@@ -115,9 +133,14 @@ def sym_reduce(band, bw: int, tw: int, tun: bb_tuning | None = None, work=None, 
     dt = dtype_code(band.dtype)
     if work is None:
         work = sym_workspace(n, bw, tw, band.dtype, band.device)
+    _check_workspace(work, band.device)
     d = torch.empty(n, dtype=band.dtype, device=band.device)
     e = torch.empty(max(n - 1, 0), dtype=band.dtype, device=band.device)
     s = stream if stream is not None else torch.cuda.current_stream(band.device)
     bb_sym_reduce(band.data_ptr(), band.stride(0), n, bw, tw, dt, d.data_ptr(), e.data_ptr() if n > 1 else 0,
                   work.data_ptr(), work.numel(), tun, s.cuda_stream)
+    if check:
+        st = bb_sym_device_status(work.data_ptr(), n, bw, tw, dt, s.cuda_stream)
+        if st != BB_OK:
+            raise BBError(st, "bb_sym_reduce")
     return d, e

@@ -44,6 +44,30 @@ class BBError(RuntimeError):
 _lib = None
 
 
+def hip_runtimes(maps_text: str) -> list[str]:
+    """Distinct HIP runtime files (libamdhip64) mapped, from /proc/self/maps text."""
+    out = set()
+    for line in maps_text.splitlines():
+        parts = line.split()
+        if len(parts) >= 6 and "libamdhip64" in os.path.basename(parts[-1]) and parts[-1].startswith("/"):
+            out.add(os.path.realpath(parts[-1]))
+    return sorted(out)
+
+
+def check_one_runtime() -> None:
+    """Raises when more than one HIP runtime is mapped into this process:
+    launches would then go to a runtime that sees no device."""
+    try:
+        with open("/proc/self/maps") as fh:
+            rts = hip_runtimes(fh.read())
+    except OSError:
+        return
+    if len(rts) > 1:
+        raise RuntimeError("more than one HIP runtime is loaded in this process (" + ", ".join(rts) + "); "
+                           "import torch before loading any other HIP library, so that libbb.so binds to "
+                           "torch's runtime")
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -57,6 +81,7 @@ def lib():
         except ImportError:
             pass
         L = ctypes.CDLL(LIB_PATH)
+        check_one_runtime()
         i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
         L.bb_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(bb_plan_info)]
         L.bb_workspace_bytes.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]

@@ -100,7 +100,14 @@ int device_cus() {
   return cus;
 }
 
-constexpr int64_t kDefaultSpin = int64_t(1) << 24;  // polls (~0.5 us each) before giving up
+// Bound of every device-side wait: tuning.spin_limit microseconds (default
+// two seconds, at most twenty), passed to the kernels in ticks of the 100 MHz
+// constant clock.
+constexpr int64_t kDefaultWaitUs = 2000000;
+constexpr int64_t kMaxWaitUs = 20000000;
+uint32_t wait_ticks(const bb_tuning &tu) {
+  return uint32_t((tu.spin_limit > 0 ? tu.spin_limit : kDefaultWaitUs) * 100);
+}
 
 bb_status run_persistent_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
                               uint32_t *sync, hipStream_t st) {
@@ -115,7 +122,7 @@ bb_status run_persistent_pass(void *wband, const bb::Geometry &g, const bb::Pass
   if (nt == 0) nt = default_threads(p);
   int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(device_cus());
   grid = std::min<int64_t>(grid, ns);
-  const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+  const uint32_t spin = wait_ticks(tu);
   if (bb::launch_persist(maxm, wband, g, p.b, p.t, ns, sync, int(grid), nt, spin, st) != hipSuccess)
     return BB_ERR_HIP;
   return BB_OK;
@@ -180,7 +187,11 @@ std::vector<LaunchItem> plan_launches(const bb::Geometry &g, const std::vector<b
                                       const bb_tuning &tu) {
   std::vector<LaunchItem> out;
   const bool may_group = tu.scheduler == BB_SCHED_DEFAULT || tu.scheduler == BB_SCHED_GROUP;
+#ifdef BB_PROFILE
+  const bool fuse = false;  // instrumented builds run every pass in a launch of its own
+#else
   const bool fuse = tu.scheduler == BB_SCHED_DEFAULT;
+#endif
   const int64_t lines = g.n + 1;
   for (int i = first; i < first + count; ++i) {
     const bb::Pass &p = passes[size_t(i)];
@@ -226,7 +237,7 @@ bb_status run_group_launch(void *wband, const bb::Geometry &g, const LaunchItem 
     return BB_ERR_HIP;
   int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
   grid = std::min<int64_t>(grid, it.run.total);
-  const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+  const uint32_t spin = wait_ticks(tu);
   return hip_status(bb::launch_group(it.run, wband, g, it.W, sync, int(grid), spin, st));
 }
 
@@ -249,7 +260,7 @@ bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
   if (tu->threads_per_block != 0 && (tu->threads_per_block < 64 || tu->threads_per_block > 256 ||
                                      tu->threads_per_block % 64 != 0))
     return BB_ERR_ARG;
-  if (tu->max_blocks < 0 || tu->spin_limit < 0) return BB_ERR_ARG;
+  if (tu->max_blocks < 0 || tu->spin_limit < 0 || tu->spin_limit > kMaxWaitUs) return BB_ERR_ARG;
   if (tu->group_sweeps < 0 || tu->group_sweeps > kGroupMaxSweeps || tu->reserved != 0) return BB_ERR_ARG;
   return BB_OK;
 }
@@ -348,7 +359,7 @@ bb_status run_sym_persistent_pass(void *work, const bb::SymGeometry &g, const bb
   const int nt = tu.threads_per_block ? tu.threads_per_block : 256;
   int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(device_cus());
   grid = std::min<int64_t>(grid, ns);
-  const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+  const uint32_t spin = wait_ticks(tu);
   return hip_status(bb::launch_sym_persist(sym_maxm(p.t), work, g, p.b, p.t, ns, sync, int(grid), nt, spin, st));
 }
 
@@ -402,7 +413,7 @@ bb_status run_sym_passes(void *work, const bb::SymGeometry &g, const std::vector
         return BB_ERR_HIP;
       int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : int64_t(device_cus());
       grid = std::min<int64_t>(grid, it.run.total);
-      const int64_t spin = tu.spin_limit > 0 ? tu.spin_limit : kDefaultSpin;
+      const uint32_t spin = wait_ticks(tu);
       rc = hip_status(bb::launch_sym_group(it.run, work, g, it.W, sync, int(grid), spin, st));
     } else {
       rc = run_sym_persistent_pass(work, g, passes[size_t(it.first)], tu, sync, st);

@@ -46,6 +46,44 @@ __device__ __forceinline__ _Float16 div_(_Float16 a, _Float16 b) {
   return _Float16(q);
 }
 
+// Bounded waits.  Every poll loop calls WaitClock::tick once per poll;
+// once per `every` polls (a power of two) it reads the 100 MHz constant
+// clock (wall_clock64: 10 ns per tick) and, with `global`, the launch's
+// status word.  The wait expires `limit` ticks after its first such check,
+// or, with `global`, as soon as any other wait of the launch has expired
+// (the status word is nonzero); on expiry it sets the status word.  Waits
+// that poll memory and the idle loops of the group kernel's auxiliary waves
+// read the status word (a memory round trip, off their critical path); the
+// sweeps' LDS waits check only the clock and their group's abort flag, which
+// the auxiliary waves raise.  Workgroups also read the status word when they
+// claim work, so after a first expiry the whole launch drains within about
+// one limit: a chain of waits cannot outlast it.
+// The clock is read in its low 32 bits (42.9 s before it wraps), so a bound
+// stays below 2^31 ticks (21.4 s).
+struct WaitClock {
+  uint32_t polls = 0;
+  uint32_t t0 = 0;
+  // false: expired (the status word is set)
+  template <uint32_t every = 16, bool global = true>
+  __device__ __forceinline__ bool tick(uint32_t limit, uint32_t *status) {
+    static_assert((every & (every - 1)) == 0, "power of two");
+    if ((++polls & (every - 1)) != 0) return true;
+    const uint32_t now = uint32_t(wall_clock64());
+    if (polls == every) {
+      t0 = now;
+      return true;
+    }
+    if (now - t0 <= limit && (!global || __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0))
+      return true;
+    __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+};
+
+__device__ __forceinline__ bool launch_failed(const uint32_t *status) {
+  return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+
 template <typename T>
 struct Refl {
   T beta, tau, inv;

@@ -76,30 +76,35 @@ __device__ __forceinline__ uint64_t lds_load64(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Bounded LDS poll until the progress of a sweep reaches `need` (whole
-// wave); `known` caches the last value seen, so a satisfied wait costs no
-// LDS access.  False on expiry or abort.
-__device__ __forceinline__ bool prog_wait(const uint64_t *w, int32_t &known, int32_t need, GroupCtl &ctl,
-                                          int64_t spin_limit, uint32_t *status);
+// One poll of a sweep's LDS wait: false once the group has aborted (checked
+// every 64 polls).  The sweeps' waits need no clock of their own: whenever
+// the group makes no progress, its writer idles, and the writer's idle wait
+// is bounded (aux_idle); the loader raises the abort flag when any other
+// wait of the launch has expired.
+__device__ __forceinline__ bool keep_waiting(uint32_t &polls, GroupCtl &ctl) {
+  __builtin_amdgcn_s_sleep(1);
+  return (++polls & 63u) != 0 || !lds_load(&ctl.abort_);
+}
 
-// Bounded LDS poll until *p >= need (whole wave).  False on expiry or abort.
-__device__ __forceinline__ bool lds_wait(const int32_t *p, int32_t need, GroupCtl &ctl, int64_t spin_limit,
+// LDS poll until the progress of a sweep reaches `need` (whole wave);
+// `known` caches the last value seen, so a satisfied wait costs no LDS
+// access.  False on abort.
+__device__ __forceinline__ bool prog_wait(const uint64_t *w, int32_t &known, int32_t need, GroupCtl &ctl,
+                                          uint32_t limit, uint32_t *status);
+
+// LDS poll until *p >= need (whole wave).  False on abort.
+__device__ __forceinline__ bool lds_wait(const int32_t *p, int32_t need, GroupCtl &ctl, uint32_t limit,
                                          uint32_t *status) {
-  int64_t polls = 0;
-  while (lds_load(p) < need) {
-    if ((polls & 15) == 15 && lds_load(&ctl.abort_)) return false;
-    __builtin_amdgcn_s_sleep(1);
-    if (++polls > spin_limit) {
-      lds_store(&ctl.abort_, 1);
-      __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
-  }
+  uint32_t polls = 0;
+  while (lds_load(p) < need)
+    if (!keep_waiting(polls, ctl)) return false;
   return true;
 }
 
 // Instrumented builds (-DBB_PROFILE) accumulate wall-clock ticks (100 MHz)
-// per phase into 64-bit counters of the workspace's profiling area.
+// per phase in registers and add them, once per sweep, with atomics to the
+// 64-bit counters of the workspace's profiling line (a line of its own that
+// nothing polls).  Such builds run every pass in a launch of its own.
 #ifdef BB_PROFILE
 struct Prof {
   uint64_t v[16] = {};
@@ -119,40 +124,24 @@ struct Prof {
   }
 };
 #define BB_P(stmt) stmt
-// Event trace of groups [kTraceG0, kTraceG0 + kTraceGroups) in the space
-// past the counter area (instrumented builds allocate it): per group,
-// kTraceHalves (start, end) stamps per sweep, then kTraceIters aux records
-// (stamp, xprev, loaded, written).
-constexpr int kTraceG0 = 100, kTraceGroups = 8, kTraceHalves = 1200, kTraceIters = 6000;
-constexpr int kTraceGroupWords = 8 * kTraceHalves * 2 + kTraceIters * 4;
-__device__ __forceinline__ uint32_t *trace_base(uint32_t *sync, int32_t n, int g) {
-  if (g < kTraceG0 || g >= kTraceG0 + kTraceGroups) return nullptr;
-  return sync + kSyncHeader + (int64_t(n) + 1) * kLine + int64_t(g - kTraceG0) * kTraceGroupWords;
-}
 #else
 #define BB_P(stmt)
 #endif
 
 __device__ __forceinline__ bool prog_wait(const uint64_t *w, int32_t &known, int32_t need, GroupCtl &ctl,
-                                          int64_t spin_limit, uint32_t *status) {
+                                          uint32_t limit, uint32_t *status) {
   if (known >= need) return true;
-  int64_t polls = 0;
+  uint32_t polls = 0;
   for (;;) {
     known = sweep_prog(lds_load64(w));
     if (known >= need) return true;
-    if ((polls & 15) == 15 && lds_load(&ctl.abort_)) return false;
-    __builtin_amdgcn_s_sleep(1);
-    if (++polls > spin_limit) {
-      lds_store(&ctl.abort_, 1);
-      __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
+    if (!keep_waiting(polls, ctl)) return false;
   }
 }
 
 // The same for the loaded-rows bound of the ring.
 __device__ __forceinline__ bool rows_wait(const int32_t *p, int32_t &known, int32_t need, GroupCtl &ctl,
-                                          int64_t spin_limit, uint32_t *status) {
+                                          uint32_t spin_limit, uint32_t *status) {
   if (known >= need) return true;
   if (!lds_wait(p, need, ctl, spin_limit, status)) return false;
   known = lds_load(p);
@@ -441,7 +430,7 @@ __device__ __forceinline__ bool row_common(int32_t m, int t) {
 // q+d-1 left.
 template <typename T, int MAXM, int SC, int TWO>
 __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, int t, int d, int32_t R, int j,
-                            int lane, int64_t spin_limit, uint32_t *status, uint32_t *sync) {
+                            int lane, uint32_t spin_limit, uint32_t *status, uint32_t *sync) {
   const int32_t S = SC ? SC : A.S;
   const int32_t K = int32_t(cycles_of_dev(n, b, t, R));
   const int32_t Kp = j > 0 ? int32_t(cycles_of_dev(n, b, t, R - 1)) : 0;
@@ -450,14 +439,14 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
   int32_t known_pred = 0, known_rows = 0;
   const bool mark = b - t <= 2;                   // publish the first-part step
   const int32_t lag_steps = mark ? 2 * d - 1 : 2 * d;
-  BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g);)
+  BB_P(Prof pr; pr.start();)
   // Waits before half q (rows up to `hi` resident); false: abort.
   auto wait_half = [&](int32_t q, int32_t hi) -> bool {
     if (j > 0 && !prog_wait(&ctl.sweep[j - 1], known_pred, min(2 * q + lag_steps, 4 * Kp), ctl, spin_limit, status))
       return false;
     BB_P(pr.tick(0);)
     if (!rows_wait(&ctl.loaded_hi, known_rows, hi + 1, ctl, spin_limit, status)) return false;
-    BB_P(pr.tick(1); if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2] = uint32_t(pr.mark);)
+    BB_P(pr.tick(1);)
     return true;
   };
   // Publishes half q done; the sweep's lowest row from then on is `fl`.
@@ -468,8 +457,7 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
       return false;
     if (lane == 0)  // one release: the half's LDS writes are complete before either word moves
       __hip_atomic_store(&ctl.sweep[j], sweep_word(2 * (q + 1), fl), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    BB_P(pr.tick(4); pr.add(5, 1);
-         if (tr && lane == 0 && q < kTraceHalves) tr[(j * kTraceHalves + q) * 2 + 1] = uint32_t(pr.mark);)
+    BB_P(pr.tick(4); pr.add(5, 1);)
     return true;
   };
   // Publishes that the first part of half q (q halves done) is done.
@@ -692,7 +680,7 @@ __device__ void ring_sym_half_b(const Ring<T> &A, T *ys, int32_t n, int b, int32
 // touches it until this half A is done.
 template <typename T, int MAXM>
 __device__ void sym_group_sweep(const Ring<T> &A, GroupCtl &ctl, T *ys, int32_t n, int b, int t, int d, int32_t R,
-                                int j, int lane, int64_t spin_limit, uint32_t *status) {
+                                int j, int lane, uint32_t spin_limit, uint32_t *status) {
   const int32_t K = int32_t(cycles_of_dev(n, b, t, R));
   const int32_t Kp = j > 0 ? int32_t(cycles_of_dev(n, b, t, R - 1)) : 0;
   const bool mark = b - t <= 2;
@@ -787,13 +775,14 @@ __device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t
   }
 }
 
-// Idle accounting of the auxiliary waves: a bounded number of empty polls
-// in a row, then abort.
-__device__ __forceinline__ bool aux_idle(int64_t &idle, int64_t spin_limit, GroupCtl &ctl, uint32_t *status) {
+// Idle accounting of the auxiliary waves: a run of empty polls is one
+// bounded wait (WaitClock, restarted whenever rows move); on expiry the
+// status word is set and the group aborts.  The loop that calls it reads
+// the abort flag itself.
+__device__ __forceinline__ bool aux_idle(WaitClock &idle, uint32_t limit, GroupCtl &ctl, uint32_t *status) {
   __builtin_amdgcn_s_sleep(1);
-  if (++idle <= spin_limit) return true;
+  if (idle.tick<256, false>(limit, status)) return true;
   lds_store(&ctl.abort_, 1);
-  __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;
 }
 
@@ -801,11 +790,10 @@ __device__ __forceinline__ bool aux_idle(int64_t &idle, int64_t spin_limit, Grou
 // X_g = rows written.
 template <typename T>
 __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
-                             int32_t Gg, uint32_t *xself_line, int lane, int64_t spin_limit, uint32_t *status,
+                             int32_t Gg, uint32_t *xself_line, int lane, uint32_t spin_limit, uint32_t *status,
                              uint32_t *sync) {
   int32_t written = R0;
-  int64_t idle = 0;
-  BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g); int it_no = 0;)
+  WaitClock idle;
   for (;;) {
     // One LDS access per word, all in flight together (lane j reads sweep j's
     // word), then one acquire: the rows below every floor are then visible.
@@ -823,20 +811,12 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
     // sweep needs the lowest released rows first
     const int32_t wb = min(min(dead, lh), written + kDrainBatchRows);
     if (wb > written) {
-      BB_P(const uint32_t t_a = uint32_t(wall_clock64());)
       ring_drain(A, mem, written, wb, lane);
-      BB_P(const uint32_t t_b = uint32_t(wall_clock64());)
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in memory
       written = wb;
       lds_store(&ctl.written, written);  // their slots may be refilled
       if (lane == 0) __hip_atomic_store(xself_line, uint32_t(written), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      idle = 0;
-      BB_P(pr.tick(6); pr.add(14, 1);
-           if (tr && lane == 0 && it_no < kTraceIters / 2) {
-             uint32_t *e = tr + 8 * kTraceHalves * 2 + it_no * 4;
-             e[0] = uint32_t(pr.mark); e[1] = t_a; e[2] = uint32_t(wb); e[3] = t_b;
-             ++it_no;
-           })
+      idle = WaitClock();
       if (written >= n) return;
     } else if (!aux_idle(idle, spin_limit, ctl, status)) {
       return;
@@ -861,11 +841,10 @@ struct PrevRows {
 // in batches, signalling each batch.
 template <typename T>
 __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
-                             const PrevRows src, int lane, int64_t spin_limit, uint32_t *status, uint32_t *sync) {
+                             const PrevRows src, int lane, uint32_t spin_limit, uint32_t *status, uint32_t *sync) {
   int32_t loaded = R0;
   int32_t xprev = src.line ? 0 : n;
-  int64_t idle = 0;
-  BB_P(Prof pr; pr.start(); uint32_t *tr = trace_base(sync, n, ctl.g); int it_no = 0;)
+  WaitClock idle;
   for (;;) {
     // the three words are read together, then one acquire
     const int32_t want = min(n, loaded + kLoadBatchRows);
@@ -877,21 +856,20 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
     }
     const int32_t ab = __hip_atomic_load(&ctl.abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const int32_t wr = __hip_atomic_load(&ctl.written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const bool failed = launch_failed(status);  // in flight with the release counter
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (ab) return;
+    if (failed) {  // a wait elsewhere in the launch expired: the group drains
+      lds_store(&ctl.abort_, 1);
+      return;
+    }
     const int32_t lim = min(min(xprev, wr + A.W), want);
     if (lim > loaded) {
       ring_fill(A, mem, loaded, lim, lane);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in LDS
       loaded = lim;
       lds_store(&ctl.loaded_hi, loaded);
-      idle = 0;
-      BB_P(pr.tick(8); pr.add(13, 1);
-           if (tr && lane == 0 && it_no < kTraceIters / 2) {
-             uint32_t *e = tr + 8 * kTraceHalves * 2 + (kTraceIters / 2 + it_no) * 4;
-             e[0] = uint32_t(pr.mark); e[1] = uint32_t(xprev); e[2] = uint32_t(loaded); e[3] = 0;
-             ++it_no;
-           })
+      idle = WaitClock();
       if (loaded >= n) return;
     } else if (!aux_idle(idle, spin_limit, ctl, status)) {
       return;
@@ -906,7 +884,7 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
 // reduction's (by half-cycles, with the same lag d), every pass at MAXM.
 template <typename T, int MAXM, int SC, bool SYM = false>
 __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, int32_t sub, int32_t n, GroupRun run,
-                                                                 int W, uint32_t *sync, int64_t spin_limit) {
+                                                                 int W, uint32_t *sync, uint32_t spin_limit) {
   extern __shared__ __align__(16) unsigned char lds_ring[];
   __shared__ GroupCtl ctl;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);  // wave-uniform
@@ -946,6 +924,7 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
           base = tab_base[j];
         }
       }
+      if (launch_failed(status)) ctl.abort_ = 1;  // a wait elsewhere expired: drain
       ctl.g = gi;
       ctl.pass_word = pw;
       ctl.prev_word = qw;
@@ -1024,7 +1003,7 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
 
 template <typename T, int MAXM, int SC>
 hipError_t group_t(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
-                   int64_t spin_limit, hipStream_t st) {
+                   uint32_t spin_limit, hipStream_t st) {
   const size_t lds = size_t(W) * size_t(g.stride) * sizeof(T);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, SC>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -1039,7 +1018,7 @@ hipError_t group_t(const GroupRun &run, void *wband, const Geometry &g, int W, u
 // TW 16 in fp16); any other stride runs the generic ring code.
 template <typename T, int MAXM>
 hipError_t group_stride(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
-                        int64_t spin_limit, hipStream_t st) {
+                        uint32_t spin_limit, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {  // half precision: the headline band's stride, else the generic ring code
     if (g.stride == 104) return group_t<T, MAXM, 104>(run, wband, g, W, sync, grid, spin_limit, st);
     return group_t<T, MAXM, 0>(run, wband, g, W, sync, grid, spin_limit, st);
@@ -1053,7 +1032,7 @@ hipError_t group_stride(const GroupRun &run, void *wband, const Geometry &g, int
 
 template <typename T>
 hipError_t group_dispatch(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
-                          int64_t spin_limit, hipStream_t st) {
+                          uint32_t spin_limit, hipStream_t st) {
   switch (run.maxm) {
     case 9: return group_stride<T, 9>(run, wband, g, W, sync, grid, spin_limit, st);
     case 17: return group_stride<T, 17>(run, wband, g, W, sync, grid, spin_limit, st);
@@ -1063,7 +1042,7 @@ hipError_t group_dispatch(const GroupRun &run, void *wband, const Geometry &g, i
 
 template <typename T, int MAXM>
 hipError_t sym_group_t(const GroupRun &run, void *wband, const SymGeometry &g, int W, uint32_t *sync, int grid,
-                       int64_t spin_limit, hipStream_t st) {
+                       uint32_t spin_limit, hipStream_t st) {
   const size_t lds = size_t(W) * size_t(g.stride) * sizeof(T);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, 0, true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -1076,7 +1055,7 @@ hipError_t sym_group_t(const GroupRun &run, void *wband, const SymGeometry &g, i
 }  // namespace
 
 hipError_t launch_sym_group(const GroupRun &run, void *wband, const SymGeometry &g, int W, uint32_t *sync, int grid,
-                            int64_t spin_limit, hipStream_t st) {
+                            uint32_t spin_limit, hipStream_t st) {
   if (g.dtype == 1) {
     if (run.maxm == 9) return sym_group_t<double, 9>(run, wband, g, W, sync, grid, spin_limit, st);
     if (run.maxm == 17) return sym_group_t<double, 17>(run, wband, g, W, sync, grid, spin_limit, st);
@@ -1090,7 +1069,7 @@ hipError_t launch_sym_group(const GroupRun &run, void *wband, const SymGeometry 
 }
 
 hipError_t launch_group(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
-                        int64_t spin_limit, hipStream_t st) {
+                        uint32_t spin_limit, hipStream_t st) {
   if (g.dtype == 1) return group_dispatch<double>(run, wband, g, W, sync, grid, spin_limit, st);
   if (g.dtype == 2) return group_dispatch<_Float16>(run, wband, g, W, sync, grid, spin_limit, st);
   return group_dispatch<float>(run, wband, g, W, sync, grid, spin_limit, st);

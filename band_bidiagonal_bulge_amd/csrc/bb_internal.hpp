@@ -22,7 +22,7 @@ hipError_t launch_step(int maxm, void *wband, const Geometry &g, int b, int t, i
 // pass's sweeps in order; sync = the workspace's counter area (status word,
 // claim counter, per-sweep progress), claim and progress zeroed beforehand.
 hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
-                          int grid, int nt, int64_t spin_limit, hipStream_t st);
+                          int grid, int nt, uint32_t wait_ticks, hipStream_t st);
 
 // Sweep groups resident in LDS: `grid` workgroups of 64 (gmax+2) threads
 // claim groups of G consecutive sweeps; each keeps a ring of W band rows in
@@ -48,7 +48,7 @@ struct GroupRun {
   int32_t base[kMaxRunPasses];  // the pass's first group in the run
 };
 hipError_t launch_group(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
-                        int64_t spin_limit, hipStream_t st);
+                        uint32_t wait_ticks, hipStream_t st);
 
 // LDS bytes one workgroup stages per cycle for a pass (b, t) with register
 // tile maxm.
@@ -60,13 +60,13 @@ size_t stage_lds_bytes(int dtype, int maxm, int b, int t);
 // d = diagonal, e = first superdiagonal.
 hipError_t launch_sym_pack(const void *band, int64_t ld_band, void *wband, const SymGeometry &g, hipStream_t st);
 hipError_t launch_sym_persist(int maxm, void *wband, const SymGeometry &g, int b, int t, int64_t nsweeps,
-                              uint32_t *sync, int grid, int nt, int64_t spin_limit, hipStream_t st);
+                              uint32_t *sync, int grid, int nt, uint32_t wait_ticks, hipStream_t st);
 hipError_t launch_sym_extract(const void *wband, const SymGeometry &g, void *d, void *e, hipStream_t st);
 // The symmetric sweeps in LDS-resident groups (the k_group kernel with the
 // symmetric half-cycles): run.maxm 9 or 17 (fp32 also 33) for every pass of
 // the run, d = the lag in halves.
 hipError_t launch_sym_group(const GroupRun &run, void *wband, const SymGeometry &g, int W, uint32_t *sync, int grid,
-                            int64_t spin_limit, hipStream_t st);
+                            uint32_t wait_ticks, hipStream_t st);
 
 // Singular values of the bidiagonal by bisection (bb_svals.hip).  The
 // workspace holds a header {lo, hi, pivmin} in its first kSvalsHeaderBytes,

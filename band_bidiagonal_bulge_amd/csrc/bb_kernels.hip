@@ -216,18 +216,15 @@ __device__ __forceinline__ int64_t half_cycles_needed(int b, int t, int64_t k, i
   return need < all ? need : all;
 }
 
-// Bounded poll of a progress counter (one thread).  Returns false, after
-// setting the status word, when spin_limit polls pass without the counter
-// reaching `need`.
-__device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t need, int64_t spin_limit,
+// Bounded poll of a progress counter (one thread).  Returns false, with the
+// status word set, once the wait expires (WaitClock: `limit` ticks, or any
+// other wait of the launch expired).
+__device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t need, uint32_t limit,
                                               uint32_t *status) {
-  int64_t polls = 0;
+  WaitClock wc;
   while (__hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
     __builtin_amdgcn_s_sleep(1);
-    if (++polls > spin_limit) {
-      __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
+    if (!wc.tick(limit, status)) return false;
   }
   return true;
 }
@@ -237,8 +234,8 @@ __device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t nee
 // cycle it waits on its predecessor's progress counter, after it publishes
 // its own.  Claims are monotone, so every sweep waited on is held by a
 // running workgroup: no deadlock for any grid size.  Waits are bounded by
-// spin_limit polls; on expiry the workgroup sets the status word and stops,
-// and so, in turn, do its successors.
+// time (WaitClock); on expiry the workgroup sets the status word and stops,
+// and every other workgroup stops at its next wait or claim.
 //
 // AUX selects how band data crosses between workgroups (and XCDs, whose L2
 // caches are not coherent with each other): kSc1 makes every band access an
@@ -251,7 +248,7 @@ __device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t nee
 #endif
 template <typename T, int MAXM, int AUX>
 __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, int64_t n, int b, int t,
-                                                 int64_t nsweeps, uint32_t *sync, int64_t spin_limit) {
+                                                 int64_t nsweeps, uint32_t *sync, uint32_t spin_limit) {
   const Band<T, AUX> A = make_band<T, AUX>(a, ld, sub, n);
   __shared__ T xs[MAXM];
   __shared__ T ys[MAXM];
@@ -278,7 +275,10 @@ __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, 
 #endif
   if (tid == 0) sgo = 1;
   for (;;) {
-    if (tid == 0) sR = int64_t(atomicAdd(claim, 1u));
+    if (tid == 0) {
+      sR = int64_t(atomicAdd(claim, 1u));
+      if (launch_failed(status)) sgo = 0;  // a wait elsewhere expired: drain
+    }
     __syncthreads();
     const int64_t R = sR;
     if (R >= nsweeps || !sgo) break;
@@ -402,7 +402,7 @@ hipError_t step_dispatch(int maxm, void *wband, const Geometry &g, int b, int t,
 
 template <typename T, int MAXM>
 hipError_t persist_t(void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync, int grid,
-                     int nt, int64_t spin_limit, hipStream_t st) {
+                     int nt, uint32_t spin_limit, hipStream_t st) {
   hipLaunchKernelGGL((k_persist<T, MAXM, BB_PERSIST_AUX>), dim3(unsigned(grid)), dim3(nt), 0, st,
                      static_cast<T *>(wband),
                      int64_t(g.stride), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
@@ -411,7 +411,7 @@ hipError_t persist_t(void *wband, const Geometry &g, int b, int t, int64_t nswee
 
 template <typename T>
 hipError_t persist_dispatch(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
-                            int grid, int nt, int64_t spin_limit, hipStream_t st) {
+                            int grid, int nt, uint32_t spin_limit, hipStream_t st) {
   switch (maxm) {
     case 8: return persist_t<T, 8>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
     case 9: return persist_t<T, 9>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
@@ -434,7 +434,7 @@ size_t stage_lds_bytes(int dtype, int maxm, int b, int t) {
 }
 
 hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
-                          int grid, int nt, int64_t spin_limit, hipStream_t st) {
+                          int grid, int nt, uint32_t spin_limit, hipStream_t st) {
   if (g.dtype == 1) return persist_dispatch<double>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
   if (g.dtype == 2)
     return persist_dispatch<_Float16>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);

@@ -39,15 +39,11 @@
 namespace bb {
 namespace {
 
-__device__ __forceinline__ bool sym_wait(const uint32_t *line, uint32_t need, int64_t spin_limit,
-                                         uint32_t *status) {
-  int64_t polls = 0;
+__device__ __forceinline__ bool sym_wait(const uint32_t *line, uint32_t need, uint32_t limit, uint32_t *status) {
+  WaitClock wc;
   while (__hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
     __builtin_amdgcn_s_sleep(1);
-    if (++polls > spin_limit) {
-      __hip_atomic_store(status, uint32_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
+    if (!wc.tick(limit, status)) return false;
   }
   return true;
 }
@@ -97,7 +93,7 @@ __device__ __forceinline__ void tri_index(int q, int m, int &i, int &j) {
 
 template <typename T, int MAXM>
 __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64_t n, int b, int t, int64_t nsweeps,
-                                                     uint32_t *sync, int64_t spin_limit) {
+                                                     uint32_t *sync, uint32_t spin_limit) {
   const Band<T, kSc1> A = make_band<T, kSc1>(a, stride, 0, n);
   __shared__ T xs[MAXM], vs[MAXM], ys[MAXM], zs[MAXM];
   __shared__ T Bs[MAXM * MAXM];  // the symmetric block, both triangles
@@ -111,7 +107,10 @@ __global__ void __launch_bounds__(256) k_sym_persist(T *a, int64_t stride, int64
   const int d = bp >= 3 ? 2 : (bp == 2 ? 3 : 4);  // half-cycles between consecutive sweeps
   if (tid == 0) sgo = 1;
   for (;;) {
-    if (tid == 0) sR = int64_t(atomicAdd(claim, 1u));
+    if (tid == 0) {
+      sR = int64_t(atomicAdd(claim, 1u));
+      if (launch_failed(status)) sgo = 0;  // a wait elsewhere expired: drain
+    }
     __syncthreads();
     const int64_t R = sR;
     if (R >= nsweeps || !sgo) break;
@@ -258,7 +257,7 @@ __global__ void k_sym_extract(const T *__restrict__ a, int64_t stride, int64_t n
 
 template <typename T, int MAXM>
 hipError_t sym_persist_t(void *wband, const SymGeometry &g, int b, int t, int64_t nsweeps, uint32_t *sync, int grid,
-                         int nt, int64_t spin_limit, hipStream_t st) {
+                         int nt, uint32_t spin_limit, hipStream_t st) {
   hipLaunchKernelGGL((k_sym_persist<T, MAXM>), dim3(grid), dim3(nt), 0, st, static_cast<T *>(wband),
                      int64_t(g.stride), g.n, b, t, nsweeps, sync, spin_limit);
   return hipGetLastError();
@@ -266,7 +265,7 @@ hipError_t sym_persist_t(void *wband, const SymGeometry &g, int b, int t, int64_
 
 template <typename T>
 hipError_t sym_persist_d(int maxm, void *wband, const SymGeometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
-                         int grid, int nt, int64_t spin_limit, hipStream_t st) {
+                         int grid, int nt, uint32_t spin_limit, hipStream_t st) {
   switch (maxm) {
     case 9: return sym_persist_t<T, 9>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
     case 17: return sym_persist_t<T, 17>(wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
@@ -295,7 +294,7 @@ hipError_t launch_sym_pack(const void *band, int64_t ld_band, void *wband, const
 }
 
 hipError_t launch_sym_persist(int maxm, void *wband, const SymGeometry &g, int b, int t, int64_t nsweeps,
-                              uint32_t *sync, int grid, int nt, int64_t spin_limit, hipStream_t st) {
+                              uint32_t *sync, int grid, int nt, uint32_t spin_limit, hipStream_t st) {
   return g.dtype == 0 ? sym_persist_d<float>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st)
                       : sym_persist_d<double>(maxm, wband, g, b, t, nsweeps, sync, grid, nt, spin_limit, st);
 }

@@ -81,7 +81,12 @@ typedef struct {
                                 bandwidth b' > 1, else 3); 3 = always three */
   int32_t max_blocks;        /* persistent, group: resident workgroups (0 = device fill) */
   int32_t threads_per_block; /* 64..256, multiple of 64 (0 = default) */
-  int64_t spin_limit;        /* persistent, group: polls before BB_ERR_TIMEOUT (0 = default) */
+  int64_t spin_limit;        /* persistent, group: bound of every device-side
+                                wait, in microseconds (0 = 2 s, at most 20 s):
+                                a wait that outlasts it, or any wait running
+                                when another has expired, stops; every
+                                workgroup of the launch then drains, and
+                                bb_device_status reports BB_ERR_TIMEOUT */
   int32_t group_sweeps;      /* group: sweeps per workgroup, 1..6 (0 = the most that fit) */
   int32_t reserved;          /* must be 0 */
 } bb_tuning;

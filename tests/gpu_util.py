@@ -47,4 +47,20 @@ def weyl_sv_bound(d1, e1, d2, e2) -> float:
     return float(dd + de)
 
 
+def assert_bits_equal(a, b, what: str = "") -> int:
+    """Bit patterns equal, except that a zero may differ from the other zero
+    in sign (the documented sign-of-zero caveat: a full-width register tile
+    over entries known to hold +0 can turn a -0 partial sum into +0).
+    Returns how many entries differ only in the sign of a zero."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape and a.dtype == b.dtype, (what, a.shape, b.shape, a.dtype, b.dtype)
+    ut = {2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize]
+    diff = a.view(ut) != b.view(ut)
+    zero_sign = diff & (a == 0) & (b == 0)
+    bad = diff & ~zero_sign
+    assert not bad.any(), f"{what}: {int(bad.sum())} entries differ in their bits, first at {np.argwhere(bad)[:3].tolist()}"
+    return int(zero_sign.sum())
+
+
 TOL = {"f32": 2e-4, "f64": 1e-10}  # elementwise |d|,|e| and singular values, times ||A||_F

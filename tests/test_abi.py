@@ -227,3 +227,26 @@ def test_launch_plan_groups_consecutive_passes():
     assert L.bb_launch_plan(16384, 64, 16, 0, None, out, 4, None) == _lib.BB_ERR_ARG
     assert L.bb_launch_plan(16384, 64, 16, 2, ctypes.byref(sched[1]), out, 4, ctypes.byref(count)) == \
         _lib.BB_ERR_UNSUPPORTED
+
+
+def test_hip_runtime_parser_finds_duplicates():
+    # /proc/self/maps text: one runtime mapped twice (several segments) is
+    # one; two different files are two
+    from band_bidiagonal_bulge_amd._lib import hip_runtimes
+    one = ("7f00-7f10 r-xp 00000000 00:2a 11 /opt/t/lib/libamdhip64.so\n"
+           "7f10-7f20 r--p 00010000 00:2a 11 /opt/t/lib/libamdhip64.so\n"
+           "7f20-7f30 r-xp 00000000 00:2a 12 /usr/lib/libc.so.6\n")
+    assert hip_runtimes(one) == ["/opt/t/lib/libamdhip64.so"]
+    two = one + "7f40-7f50 r-xp 00000000 00:2a 13 /opt/rocm/lib/libamdhip64.so.7\n"
+    assert len(hip_runtimes(two)) == 2
+    assert hip_runtimes("7f00-7f10 rw-p 00000000 00:00 0 \n") == []
+
+
+def test_wait_bound_is_validated():
+    # the per-wait bound is in microseconds, at most twenty seconds
+    import band_bidiagonal_bulge_amd as bbm
+    assert bbm.bb_launch_plan(1000, 32, 16, bbm.BB_F32, bbm.tuning(spin_limit=20000000))
+    with pytest.raises(bbm.BBError):
+        bbm.bb_launch_plan(1000, 32, 16, bbm.BB_F32, bbm.tuning(spin_limit=20000001))
+    with pytest.raises(bbm.BBError):
+        bbm.bb_launch_plan(1000, 32, 16, bbm.BB_F32, bbm.tuning(spin_limit=-1))

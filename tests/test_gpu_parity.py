@@ -16,7 +16,7 @@ import pytest
 import band_bidiagonal_bulge_amd as bbm
 import bb_inputs
 import oracle
-from gpu_util import TOL, gpu_reduce, log, weyl_sv_bound
+from gpu_util import TOL, assert_bits_equal, gpu_reduce, log, weyl_sv_bound
 from refs import bidiag_singular_values
 
 pytestmark = pytest.mark.gpu
@@ -48,9 +48,9 @@ def _check_bitwise(band, bw, tw, tun=None):
     d, e, W, sub = gpu_reduce(band, bw, tw, tun, return_band=True)
     od, oe, OW, osub = oracle.reduce(band, bw, tw, return_band=True)
     assert sub == osub and W.shape == OW.shape
-    np.testing.assert_array_equal(d, od)
-    np.testing.assert_array_equal(e, oe)
-    np.testing.assert_array_equal(W, OW)
+    assert_bits_equal(d, od)
+    assert_bits_equal(e, oe)
+    assert_bits_equal(W, OW)
     return d, e, W, sub
 
 
@@ -143,7 +143,33 @@ def test_forced_timeout_reports_status(sched):
     st = bbm.bb_device_status(work.data_ptr(), n, bw, tw, 0, torch.cuda.current_stream().cuda_stream)
     assert st == 0
     od, oe = oracle.reduce(band.cpu().numpy(), bw, tw)
-    np.testing.assert_array_equal(d.cpu().numpy(), od)
+    assert_bits_equal(d.cpu().numpy(), od)
+
+
+def test_forced_timeout_drains_the_launch():
+    # Every wait bounded to 1 us on the headline band, all four passes in one
+    # launch: the first wait that is not satisfied at once expires, every
+    # other wait and every claim then sees the status word, and the launch
+    # drains well inside a second; the next call succeeds.
+    import time
+    import torch
+    n, bw, tw = 16384, 64, 16
+    band = torch.from_numpy(bb_inputs.make_band(n, bw, "f32", "normal", seed=0)).to("cuda:0")
+    work = bbm.workspace(n, bw, tw, band.dtype)
+    bbm.reduce(band, bw, tw, None, work)
+    torch.cuda.synchronize()
+    log("forced timeout, headline band, one launch")
+    t0 = time.perf_counter()
+    bbm.reduce(band, bw, tw, bbm.tuning(spin_limit=1), work)
+    st = bbm.bb_device_status(work.data_ptr(), n, bw, tw, 0, torch.cuda.current_stream().cuda_stream)
+    dt = time.perf_counter() - t0
+    assert st == bbm.BB_ERR_TIMEOUT, bbm.bb_status_str(st)
+    assert dt < 1.0, dt
+    with pytest.raises(bbm.BBError):
+        bbm.reduce(band, bw, tw, bbm.tuning(spin_limit=1), work, check=True)
+    d, e = bbm.reduce(band, bw, tw, None, work, check=True)
+    z = np.load(os.path.join(GOLDEN, "n16384-bw64-tw16-f32-normal.npz"))
+    assert_bits_equal(d.cpu().numpy(), z["d"], "d")
 
 
 def test_library_loaded_before_torch():
@@ -176,8 +202,8 @@ def test_repeated_calls_reuse_workspace():
     log("repeat x3")
     d, e = gpu_reduce(band, bw, tw, reps=3)
     od, oe = oracle.reduce(band, bw, tw)
-    np.testing.assert_array_equal(d, od)
-    np.testing.assert_array_equal(e, oe)
+    assert_bits_equal(d, od)
+    assert_bits_equal(e, oe)
 
 
 def _gate(w, d, e, od, oe, fro):
@@ -199,8 +225,8 @@ def test_workload_live_oracle(name):
     d, e, W, sub = gpu_reduce(band, w.bw, w.tw, return_band=True)
     od, oe = oracle.reduce(band, w.bw, w.tw)
     _gate(w, d, e, od, oe, fro)
-    np.testing.assert_array_equal(d, od)
-    np.testing.assert_array_equal(e, oe)
+    assert_bits_equal(d, od)
+    assert_bits_equal(e, oe)
     off = [o for o in range(W.shape[1]) if o - sub not in (0, 1)]
     assert np.all(W[:, off] == 0)
     sv = bidiag_singular_values(d, e)
@@ -222,8 +248,8 @@ def test_workload_stored_oracle(name):
     log(f"workload {name}")
     d, e, W, sub = gpu_reduce(band, w.bw, w.tw, return_band=True)
     _gate(w, d, e, z["d"], z["e"], fro)
-    np.testing.assert_array_equal(d, z["d"])
-    np.testing.assert_array_equal(e, z["e"])
+    assert_bits_equal(d, z["d"])
+    assert_bits_equal(e, z["e"])
     off = [o for o in range(W.shape[1]) if o - sub not in (0, 1)]
     assert np.all(W[:, off] == 0)
 
@@ -254,14 +280,14 @@ def test_staged_calls_equal_reduce(n, bw, tw, dt, sched):
     K = [(n - 2 - R - (b0 - t0)) // b0 + 1 for R in range(max(n - (b0 - t0) - 1, 0))]
     first_pass = np.array([(0, R, k) for R in range(len(K)) for k in range(K[R])], dtype=np.int64)
     OW1 = oracle.run_cycles(band, bw, tw, first_pass)
-    np.testing.assert_array_equal(W1.cpu().numpy(), OW1)
+    assert_bits_equal(W1.cpu().numpy(), OW1)
     for p in range(1, info.passes):
         bbm.bb_run_pass(n, bw, tw, code, p, work.data_ptr(), work.numel(), tun, st)
     bbm.bb_extract(work.data_ptr(), work.numel(), n, bw, tw, code, d.data_ptr(), e.data_ptr(), st)
     torch.cuda.synchronize()
     rd, re = gpu_reduce(band, bw, tw, tun)
-    np.testing.assert_array_equal(d.cpu().numpy(), rd)
-    np.testing.assert_array_equal(e.cpu().numpy(), re)
+    assert_bits_equal(d.cpu().numpy(), rd)
+    assert_bits_equal(e.cpu().numpy(), re)
     # the passes in ranges (the default scheduler shares a launch within each)
     bbm.bb_pack(tb.data_ptr(), tb.stride(0), n, bw, tw, code, work.data_ptr(), work.numel(), st)
     half = info.passes // 2
@@ -270,5 +296,5 @@ def test_staged_calls_equal_reduce(n, bw, tw, dt, sched):
     bbm.bb_run_passes(n, bw, tw, code, half, info.passes - half, work.data_ptr(), work.numel(), None, st)
     bbm.bb_extract(work.data_ptr(), work.numel(), n, bw, tw, code, d.data_ptr(), e.data_ptr(), st)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(d.cpu().numpy(), rd)
-    np.testing.assert_array_equal(e.cpu().numpy(), re)
+    assert_bits_equal(d.cpu().numpy(), rd)
+    assert_bits_equal(e.cpu().numpy(), re)

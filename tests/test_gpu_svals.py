@@ -14,7 +14,7 @@ import pytest
 import band_bidiagonal_bulge_amd as bbm
 import bb_inputs
 import oracle
-from gpu_util import TOL, gpu_reduce, log
+from gpu_util import TOL, assert_bits_equal, gpu_reduce, log
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def test_bitwise_equal_to_oracle(n, dist, dt):
     ref = oracle.svals(d, e)
     for (tree, levels) in [(0, 0), (-1, 1), (-1, 2), (-1, 3), (-1, 6), (1, 1), (5, 4), (12, 2), (16, 5)]:
         log(f"svals n={n} {dist} {dt} tree={tree} levels={levels}")
-        np.testing.assert_array_equal(gpu_svals(d, e, levels=levels, tree_levels=tree), ref)
+        assert_bits_equal(gpu_svals(d, e, levels=levels, tree_levels=tree), ref)
 
 
 @pytest.mark.parametrize("dt", ["f32", "f64"])
@@ -51,7 +51,7 @@ def test_index_ranges_and_ragged_groups(dt):
     for (i0, i1, levels, tree) in [(0, 1, 0, 0), (5, 6, 4, -1), (0, 13, 3, 7), (100, 357, 5, 0), (770, 777, 2, 16),
                                    (0, 777, 4, 3), (333, 333, 0, 0)]:
         log(f"svals range {i0}:{i1} {dt} levels={levels} tree={tree}")
-        np.testing.assert_array_equal(gpu_svals(d, e, i0, i1, levels, tree), ref[i0:i1])
+        assert_bits_equal(gpu_svals(d, e, i0, i1, levels, tree), ref[i0:i1])
 
 
 @pytest.mark.parametrize("dt", ["f32", "f64"])
@@ -64,7 +64,7 @@ def test_degenerate_bidiagonals(dt):
         d, e = d.astype(bb_inputs.np_dtype(dt)), e.astype(bb_inputs.np_dtype(dt))
         log(f"svals degenerate {name} {dt}")
         got = gpu_svals(d, e)
-        np.testing.assert_array_equal(got, oracle.svals(d, e))
+        assert_bits_equal(got, oracle.svals(d, e))
         assert np.all(got >= 0) and not np.any(np.signbit(got))
 
 
@@ -94,7 +94,7 @@ def test_band_to_singular_values_on_the_gpu(dt):
     sig = gpu_svals(d, e)
     assert np.all(np.diff(sig.astype(np.float64)) <= 0)
     for (i0, i1) in [(0, 48), (8000, 8048), (n - 48, n)]:
-        np.testing.assert_array_equal(sig[i0:i1], oracle.svals(d, e, i0, i1))
+        assert_bits_equal(sig[i0:i1], oracle.svals(d, e, i0, i1))
     if dt == "f32":
         # accuracy of the fp32 path against the fp64 path on the same band,
         # within the gate for the fp32 reduction (2e-4 ||A||_F)
