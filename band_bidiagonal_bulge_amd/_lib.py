@@ -20,7 +20,8 @@ BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT, BB_SCHED_GROUP = 0, 1, 2, 
 EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_run_passes", "bb_extract",
            "bb_launch_plan", "bb_export_band",
            "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce", "bb_sym_export_band",
-           "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split", "bb_status_str")
+           "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split", "bb_status_str",
+           "bb_probe_stream", "bb_probe_transpose_add")
 
 
 class bb_tuning(ctypes.Structure):
@@ -101,12 +102,15 @@ def lib():
         L.bb_svals_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.bb_svals.argtypes = [vp, vp, i64, i32, i64, i64, i32, i32, vp, vp, sz, vp]
         L.bb_svals_split.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.bb_probe_stream.argtypes = [vp, vp, vp, i64, i32, vp]
+        L.bb_probe_transpose_add.argtypes = [vp, vp, i32, i32, vp]
         L.bb_status_str.argtypes = [i32]
         L.bb_status_str.restype = ctypes.c_char_p
         for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_run_passes",
                   "bb_launch_plan", "bb_extract",
                   "bb_export_band", "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce",
-                  "bb_sym_export_band", "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split"):
+                  "bb_sym_export_band", "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split",
+                  "bb_probe_stream", "bb_probe_transpose_add"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -241,6 +245,18 @@ def bb_svals_split(values: int, dtype: int):
     if rc != BB_OK:
         raise BBError(rc, "bb_svals_split")
     return int(k.value), int(d.value)
+
+
+def bb_probe_stream(x_ptr: int, y_ptr: int, z_ptr: int, n: int, reps: int, stream: int) -> None:
+    rc = lib().bb_probe_stream(x_ptr, y_ptr, z_ptr, n, reps, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_probe_stream")
+
+
+def bb_probe_transpose_add(a_ptr: int, b_ptr: int, m: int, reps: int, stream: int) -> None:
+    rc = lib().bb_probe_transpose_add(a_ptr, b_ptr, m, reps, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_probe_transpose_add")
 
 
 def bb_status_str(status: int) -> str:

@@ -9,9 +9,12 @@ Prints one JSON line:
                   (ms per reduction is ms_per_step)
   roofline        the dominant kernel's algorithmic bytes per launch over its
                   average launch duration (HIP events on the stream the
-                  kernels run on), against the published HBM3E peak
-                  and (cache_ceiling) against a measured streaming ceiling of
-                  the Infinity Cache that holds the working band
+                  kernels run on), against the published HBM3E peak;
+                  working_set names the level that holds the working band
+                  (by its size) with that level's datasheet peak and the
+                  library's stream (z = x + y) and transpose-add probes over
+                  the band's footprint and over 64 MiB, each with its
+                  fraction
   ms_per_reduction_events  median and min of the per-step event times
   schedulers_ms   the same path under the step scheduler (the page's one
                   launch per step) and the persistent scheduler, and the sum
@@ -21,7 +24,7 @@ Prints one JSON line:
                   the steps; launch_of_pass: which cycle-kernel launch runs
                   each pass in a step
   cpu_baseline    the CPU oracle (one thread) timed on a bounded prefix of the
-                  same reduction, in the same unit
+                  same reduction, in the same unit: median of three samples
   svals           the step after the path: singular values of the workload's
                   bidiagonal by bisection on the GPU (bb_svals), its ALU
                   roofline in Sturm pivots per second, and the bisection
@@ -94,7 +97,10 @@ def alg_bytes_prefix(n, bw, tw, esize, ncycles):
     return total
 
 
-def cpu_baseline(band, w, seconds):
+def cpu_baseline(band, w, seconds, samples=3):
+    """The oracle (one thread) on a bounded prefix of the reduction: the
+    prefix is sized to about seconds / samples of work, run `samples` times,
+    and the median rate is the value."""
     import oracle
     oracle.build()
     esize = 8 if w.dtype == "f64" else 4
@@ -103,27 +109,41 @@ def cpu_baseline(band, w, seconds):
     _, _, done = oracle.reduce(band, w.bw, w.tw, max_cycles=100000)
     dt = time.perf_counter() - t0
     rate = alg_bytes_prefix(w.n, w.bw, w.tw, esize, done) / max(dt, 1e-9)
-    target = rate * seconds
+    target = rate * seconds / samples
     # grow the cycle count until the prefix holds about `target` bytes
-    ncyc = done
-    while alg_bytes_prefix(w.n, w.bw, w.tw, esize, ncyc * 2) < target and ncyc < 10 ** 9:
-        ncyc *= 2
-    t0 = time.perf_counter()
-    _, _, done = oracle.reduce(band, w.bw, w.tw, max_cycles=ncyc)
-    dt = time.perf_counter() - t0
-    nbytes = alg_bytes_prefix(w.n, w.bw, w.tw, esize, done)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    lo, hi = done, done
+    while alg_bytes_prefix(w.n, w.bw, w.tw, esize, hi) < target and hi < 10 ** 9:
+        lo, hi = hi, hi * 2
+    for _ in range(12):
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if alg_bytes_prefix(w.n, w.bw, w.tw, esize, mid) < target else (lo, mid)
+    ncyc = hi
+    rates, times = [], []
+    for _ in range(samples):
+        t0 = time.perf_counter()
+        _, _, done = oracle.reduce(band, w.bw, w.tw, max_cycles=ncyc)
+        dt = time.perf_counter() - t0
+        nbytes = alg_bytes_prefix(w.n, w.bw, w.tw, esize, done)
+        rates.append(nbytes / dt / 1e9)
+        times.append(dt)
+    return {"value": statistics.median(rates), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of the reduction's cycles in sequential order "
-                      f"({nbytes / 1e9:.2f} GB algorithmic, {dt:.1f} s, one thread)",
+                      f"({nbytes / 1e9:.2f} GB algorithmic), median of {samples} runs "
+                      f"({', '.join(f'{t:.1f}' for t in times)} s, one thread)",
+            "samples_GBps": [round(r, 3) for r in rates],
             "host": f"{host_model()}, {os.cpu_count()} logical CPUs"}
 
 
-# Pivots of one Sturm count step, VALU instructions in the issued code without
-# the operand broadcast: the correctly rounded division (10 fp32 / 11 fp64),
-# the shift subtraction, the pivmin guard (compare, select: 2 / 3) and the
-# count (compare, add).  Peak = the chip's vector FMA lane rate for the dtype
-# (fp32 157.3 TFLOP/s, fp64 78.6 TFLOP/s, two flops per FMA) over that count.
-PIVOT_OPS = {"f32": 15, "f64": 17}
+# The method's arithmetic per pivot of a Sturm count on the Golub-Kahan
+# tridiagonal (squares of the off-diagonal formed once per value, outside the
+# count): one division, one subtraction and one sign test.  Peak = the chip's
+# vector lane-instruction rate for the dtype (fp32 157.3 TFLOP/s, fp64 78.6
+# TFLOP/s, two flops per FMA lane-instruction) over those 3 operations, as if
+# each were one instruction.  ISSUED_OPS is what the kernel issues per pivot
+# (a correctly rounded division takes 10 fp32 / 11 fp64 instructions, the
+# pivmin guard 2 / 3, the count 2): its fraction is the issue efficiency.
+METHOD_PIVOT_OPS = 3
+ISSUED_PIVOT_OPS = {"f32": 15, "f64": 17}
 LANE_OPS_PER_S = {"f32": 157.3e12 / 2, "f64": 78.6e12 / 2}
 
 
@@ -154,11 +174,14 @@ def measure_svals(bbm, torch, d, e, w, steps, stream, cpu_seconds, with_cpu):
     # of 2n pivots each
     pivots = float(n) * halvings * 2 * n
     rate = pivots / (ms * 1e-3) / 1e9
-    peak = LANE_OPS_PER_S[w.dtype] / PIVOT_OPS[w.dtype] / 1e9
+    peak = LANE_OPS_PER_S[w.dtype] / METHOD_PIVOT_OPS / 1e9
+    issue_peak = LANE_OPS_PER_S[w.dtype] / ISSUED_PIVOT_OPS[w.dtype] / 1e9
     out = {"kernel": "k_gk_prep + k_tree + k_bisect", "ms": round(ms, 4), "values": n,
            "split": {"tree_levels": tree, "levels": levels}, "halvings": halvings,
            "roofline": {"bound": "alu", "achieved": round(rate, 2), "peak": round(peak, 1), "unit": "Gpivot/s",
-                        "frac": round(rate / peak, 4)}}
+                        "frac": round(rate / peak, 4),
+                        "peak_basis": "3 method operations per pivot (division, subtraction, sign test)",
+                        "issue_peak": round(issue_peak, 1), "issue_frac": round(rate / issue_peak, 4)}}
     if with_cpu:
         import oracle
         oracle.build_svals()
@@ -354,14 +377,14 @@ def cpu_threaded(band, w, seconds):
 
 def kernel_source_hash() -> str:
     """Hash of the sources of the reduction's kernels and their launch set-up
-    (every HIP source but the singular-value step's and the symmetric
-    reduction's): stored counter readings
+    (every HIP source but the singular-value step's, the symmetric
+    reduction's and the bandwidth probes'): stored counter readings
     are only valid for it."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "band_bidiagonal_bulge_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.startswith("bb_svals") or f.startswith("bb_sym"):
+        if f.startswith("bb_svals") or f.startswith("bb_sym") or f.startswith("bb_probe"):
             continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
@@ -382,31 +405,66 @@ def stored_traffic(workload: str):
     return t
 
 
-def cache_ceiling(torch, dev, stream, mib=128, reps=10, inner=10):
-    """A measured ceiling for the level that holds the working band: an
-    elementwise streaming update y += x over two fp32 buffers of mib/2 MiB
-    each (together above the 8 x 4 MiB of L2, inside the 256 MiB Infinity
-    Cache), repeated so the buffers stay resident; bytes = 3 per element
-    (read x, read y, write y), `inner` back-to-back launches between two
-    events (so launch gaps weigh little), best of `reps`."""
-    n = (mib << 20) // 8
-    x = torch.ones(n, dtype=torch.float32, device=dev)
-    y = torch.zeros(n, dtype=torch.float32, device=dev)
-    for _ in range(3):
-        y.add_(x)
-    torch.cuda.synchronize()
-    best = float("inf")
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(inner):
-            y.add_(x)
-        b.record(stream)
-        b.synchronize()
-        best = min(best, a.elapsed_time(b) / inner)
-    return {"probe": f"y += x over two fp32 buffers of {mib // 2} MiB each (torch elementwise kernel), "
-                     f"{inner} launches per timing, best of {reps}", "GBps": round(3 * 4 * n / (best * 1e-3) / 1e9, 1)}
+# Published peak of the 256 MiB Infinity Cache of the CDNA 3 part (MI300X,
+# 17.2 TB/s); MI355X keeps the same 256 MiB last-level cache in front of HBM.
+# Used as the datasheet figure for the level that holds a working band.
+IC_PEAK_GBPS = 17200.0
+L2_PER_XCD = 4 << 20
+IC_BYTES = 256 << 20
+
+
+def memory_level(nbytes: int) -> str:
+    """The level whose capacity bounds a working set that every XCD touches
+    through agent-coherent accesses: one XCD's L2 cannot hold a set above 4
+    MiB, the Infinity Cache holds up to 256 MiB, HBM the rest."""
+    if nbytes <= L2_PER_XCD:
+        return "l2"
+    return "infinity_cache" if nbytes <= IC_BYTES else "hbm"
+
+
+def probe_ceilings(bbm, torch, dev, stream, sizes, reps=5, launch_bytes=4e9):
+    """Measured ceilings of the level that holds the working band, from the
+    library's two probes (bb_probe_stream: z = x + y; bb_probe_transpose_add:
+    B = A + A^T), each over a footprint of every size in `sizes` bytes (all
+    operands together), repeated inside one launch until the launch moves
+    about `launch_bytes` (each repetition on other XCDs), timed with events on
+    the stream it runs on, best of `reps` launches.  12 bytes move per
+    element and repetition."""
+    sp = stream.cuda_stream
+    out = []
+
+    def timed(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            best = min(best, a.elapsed_time(b))
+        return round(nbytes / (best * 1e-3) / 1e9, 1), round(best * 1e3, 1)
+
+    for size in sizes:
+        n = max(4, (size // 12) // 4 * 4)
+        r = max(1, int(launch_bytes // (12 * n)))
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.ones(n, dtype=torch.float32, device=dev)
+        z = torch.zeros(n, dtype=torch.float32, device=dev)
+        gbps, us = timed(lambda: bbm.bb_probe_stream(x.data_ptr(), y.data_ptr(), z.data_ptr(), n, r, sp), 12 * n * r)
+        out.append({"probe": "stream z = x + y", "footprint_mib": round(12 * n / 2**20, 2), "repetitions": r,
+                    "GBps": gbps, "us_per_launch": us})
+        del x, y, z
+        m = max(1, int((size // 8) ** 0.5))
+        r = max(1, int(launch_bytes // (12 * m * m)))
+        a = torch.ones(m, m, dtype=torch.float32, device=dev)
+        b = torch.zeros(m, m, dtype=torch.float32, device=dev)
+        gbps, us = timed(lambda: bbm.bb_probe_transpose_add(a.data_ptr(), b.data_ptr(), m, r, sp), 12 * m * m * r)
+        out.append({"probe": f"transpose-add B = A + A^T, m = {m}", "footprint_mib": round(8 * m * m / 2**20, 2),
+                    "repetitions": r, "GBps": gbps, "us_per_launch": us})
+        del a, b
+    return out
 
 
 def scheduler_times(bbm, torch, tb, w, dt, work, stream, reps=2):
@@ -487,7 +545,7 @@ def main():
     ap.add_argument("--no-svals", action="store_true")
     ap.add_argument("--no-sym", action="store_true")
     ap.add_argument("--no-f16", action="store_true")
-    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured cache ceiling probe")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the bandwidth probes of the working set's level")
     ap.add_argument("--no-schedulers", action="store_true", help="skip the step / persistent scheduler times")
     ap.add_argument("--pass-ranges", action="store_true",
                     help="time each pass alone, each consecutive pair in one launch and all passes, then exit")
@@ -645,10 +703,17 @@ def main():
                     "GBps": round(ab / (pass_ms[i] * 1e-3) / 1e9, 2)}
                    for i, (b, t, ab) in enumerate(passes)],
     }
+    ws = int(work.numel())
+    level = {"working_set_bytes": ws, "level": memory_level(ws)}
+    if level["level"] == "infinity_cache":
+        level.update({"datasheet_peak": IC_PEAK_GBPS, "datasheet_frac": round(achieved / IC_PEAK_GBPS, 5),
+                      "datasheet": "MI300X Infinity Cache peak (the CDNA 3 part's published figure)"})
     if not args.no_ceiling:
-        ceil = cache_ceiling(torch, dev, stream)
-        ceil["frac"] = round(achieved / ceil["GBps"], 5)
-        out["roofline"]["cache_ceiling"] = ceil
+        probes = probe_ceilings(bbm, torch, dev, stream, [ws, 64 << 20])
+        for p in probes:
+            p["frac"] = round(achieved / p["GBps"], 5)
+        level["probes"] = probes
+    out["roofline"]["working_set"] = level
     if not args.no_schedulers:
         out["schedulers_ms"] = scheduler_times(bbm, torch, tb, w, dt, work, stream)
         out["schedulers_ms"]["default"] = round(statistics.median(step_ms), 3)

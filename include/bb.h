@@ -272,6 +272,28 @@ bb_status bb_svals_split(int64_t values, int32_t dtype, int32_t *tree_levels, in
 /* Static description of a status code. */
 const char *bb_status_str(int32_t status);
 
+/* ---- Measurement probes (not part of the reduction) ----------------------
+ * Bandwidth ceilings for the memory level that holds a working band, for
+ * the cycle kernels' roofline (page "Accelerating Bidiagonalization of Banded
+ * Matrices through Memory-Aware Bulge-Chasing on GPUs", profiling section:
+ * runtime tracks the throughput of the cache levels, and a matrix
+ * transpose-add is the reference point for row- and column-wise access).
+ * Both enqueue one kernel on `stream` and return at once; the caller times
+ * them and owns every buffer.  The kernel repeats the operation `reps` >= 1
+ * times, handing each element to another workgroup (so another XCD) on each
+ * repetition; the result does not depend on `reps`.
+ *
+ * z[i] = x[i] + y[i], i < n, fp32, 16-byte accesses with the cycle kernels'
+ * agent-coherent cache policy: 12 n bytes move per repetition.  x, y, z:
+ * device, 16-byte aligned, z distinct from x and y; n a multiple of 4,
+ * 4 n bytes < 2 GiB.  Errors: BB_ERR_ARG, BB_ERR_HIP. */
+bb_status bb_probe_stream(const void *x, const void *y, void *z, int64_t n, int32_t reps, void *stream);
+
+/* B = A + A^T for an m x m row-major fp32 matrix, through LDS tiles (both
+ * reads coalesced): 12 m^2 bytes move per repetition.  a, b: device,
+ * distinct; m^2 <= 2^30.  Errors: BB_ERR_ARG, BB_ERR_HIP. */
+bb_status bb_probe_transpose_add(const void *a, void *b, int32_t m, int32_t reps, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,3 +24,18 @@ def test_sym_pass_bytes_matches_enumeration():
                     total += 2 * es * entries
                     k += 1
             assert bench.sym_pass_bytes(n, b, t, es) == total
+
+
+def test_memory_level_by_working_set():
+    import bench
+    assert bench.memory_level(1 << 20) == "l2"
+    assert bench.memory_level(8651520) == "infinity_cache"  # the n = 16384, BW = 64 fp32 working band
+    assert bench.memory_level(300 << 20) == "hbm"
+
+
+def test_cycle_kernel_names():
+    import bench
+    assert bench.is_cycle_kernel("void bb::(anonymous namespace)::k_group<float, 17, 100, false>(float*, int)", "f32")
+    assert not bench.is_cycle_kernel("void bb::(anonymous namespace)::k_group<float, 17, 0, true>(float*, int)", "f32")
+    assert bench.is_cycle_kernel("void bb::(anonymous namespace)::k_persist<double, 33, 16>(double*, long)", "f64")
+    assert not bench.is_cycle_kernel("bb::(anonymous namespace)::k_probe_stream(float const*, long, int)", "f32")
