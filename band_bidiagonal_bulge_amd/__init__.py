@@ -7,16 +7,17 @@ for device memory and the stream only).
 """
 from __future__ import annotations
 
-from ._lib import (BB_ERR_TIMEOUT, BB_F16, BB_F32, BB_F64, BB_OK, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
+from ._lib import (BB_ERR_TIMEOUT, BB_ERR_WORKSPACE, BB_NOALLOC_SCRATCH_BYTES, BB_F16, BB_F32, BB_F64, BB_OK, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
                    BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
+                   bb_reduce_noalloc,
                    bb_launch_plan, bb_probe_stream, bb_probe_transpose_add, bb_run_pass, bb_run_passes,
                    bb_status_str, bb_svals, bb_svals_split, bb_svals_workspace_bytes, bb_sym_device_status,
                    bb_sym_export_band, bb_sym_reduce, bb_sym_workspace_bytes, bb_tuning,
                    bb_workspace_bytes, lib)
 
 __all__ = ["reduce", "export_band", "workspace", "tuning", "dtype_code", "bb_plan", "bb_workspace_bytes",
-           "bb_reduce", "bb_pack", "bb_run_pass", "bb_run_passes", "bb_launch_plan", "bb_extract", "bb_export_band", "bb_device_status", "bb_svals", "bb_svals_workspace_bytes", "bb_svals_split",
+           "bb_reduce", "bb_reduce_noalloc", "bb_pack", "bb_run_pass", "bb_run_passes", "bb_launch_plan", "bb_extract", "bb_export_band", "bb_device_status", "bb_svals", "bb_svals_workspace_bytes", "bb_svals_split",
            "bb_sym_workspace_bytes", "bb_sym_reduce", "bb_sym_export_band", "bb_sym_device_status",
            "bb_status_str", "svals", "sym_reduce", "sym_workspace", "BBError", "EXPORTS"]
 

@@ -21,7 +21,7 @@ EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass
            "bb_launch_plan", "bb_export_band",
            "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce", "bb_sym_export_band",
            "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split", "bb_status_str",
-           "bb_probe_stream", "bb_probe_transpose_add")
+           "bb_probe_stream", "bb_probe_transpose_add", "bb_reduce_noalloc")
 
 
 class bb_tuning(ctypes.Structure):
@@ -102,6 +102,7 @@ def lib():
         L.bb_svals_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.bb_svals.argtypes = [vp, vp, i64, i32, i64, i64, i32, i32, vp, vp, sz, vp]
         L.bb_svals_split.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.bb_reduce_noalloc.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, ctypes.POINTER(bb_tuning), vp]
         L.bb_probe_stream.argtypes = [vp, vp, vp, i64, i32, vp]
         L.bb_probe_transpose_add.argtypes = [vp, vp, i32, i32, vp]
         L.bb_status_str.argtypes = [i32]
@@ -110,7 +111,7 @@ def lib():
                   "bb_launch_plan", "bb_extract",
                   "bb_export_band", "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce",
                   "bb_sym_export_band", "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split",
-                  "bb_probe_stream", "bb_probe_transpose_add"):
+                  "bb_probe_stream", "bb_probe_transpose_add", "bb_reduce_noalloc"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -142,6 +143,17 @@ def bb_reduce(band_ptr: int, ld_band: int, n: int, bw: int, tw: int, dtype: int,
                          ctypes.byref(tuning) if tuning is not None else None, stream or None)
     if rc != BB_OK:
         raise BBError(rc, "bb_reduce")
+
+
+BB_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def bb_reduce_noalloc(band_ptr: int, ld_band: int, n: int, bw: int, tw: int, dtype: int, d_ptr: int, e_ptr: int,
+                      status_ptr: int, tuning: bb_tuning | None, stream: int) -> None:
+    rc = lib().bb_reduce_noalloc(band_ptr, ld_band, n, bw, tw, dtype, d_ptr, e_ptr or None, status_ptr or None,
+                                 ctypes.byref(tuning) if tuning is not None else None, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_reduce_noalloc")
 
 
 def bb_pack(band_ptr: int, ld_band: int, n: int, bw: int, tw: int, dtype: int, work_ptr: int, work_bytes: int,

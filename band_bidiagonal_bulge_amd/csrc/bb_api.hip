@@ -683,6 +683,55 @@ bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, in
   return bb_extract(work, work_bytes, n, bw, tw, dtype, d, e, stream);
 }
 
+}  // extern "C"
+
+// The workspace of bb_reduce_noalloc: one array per GPU, in the library's
+// code object, held until the process ends.  Host code never uses its name
+// as an address (that is a host-side stand-in): each device's address comes
+// from hipGetSymbolAddress, called once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[BB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`.
+bb_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BB_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BB_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bb_status bb_reduce_noalloc(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype,
+                            void *d, void *e, void *status, const bb_tuning *tuning, void *stream) {
+  size_t need = 0;
+  bb_status rc = bb_workspace_bytes(n, bw, tw, dtype, &need);
+  if (rc != BB_OK) return rc;
+  if (need > size_t(BB_NOALLOC_SCRATCH_BYTES)) return BB_ERR_WORKSPACE;
+  void *work = nullptr;
+  if ((rc = scratch_of_current_device(&work)) != BB_OK) return rc;
+  if ((rc = bb_reduce(band, ld_band, n, bw, tw, dtype, d, e, work, size_t(BB_NOALLOC_SCRATCH_BYTES), tuning,
+                      stream)) != BB_OK)
+    return rc;
+  if (!status) return BB_OK;
+  const bb::Geometry g = bb::make_geometry(n, bw, tw, dtype);
+  return hip_status(hipMemcpyAsync(status, static_cast<const char *>(work) + g.sync_offset, sizeof(uint32_t),
+                                   hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+}
+
 bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,
                          void *stream) {
   if (!valid_shape(n, bw, tw, dtype) || !work || !dst) return BB_ERR_ARG;

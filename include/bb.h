@@ -133,6 +133,31 @@ bb_status bb_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, s
 bb_status bb_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype,
                     void *d, void *e, void *work, size_t work_bytes, const bb_tuning *tuning, void *stream);
 
+/* Largest workspace bb_reduce_noalloc can use: 16 MiB per GPU. */
+#define BB_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * bb_reduce for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same reduction with the same results, bit for bit, but with no `work`
+ * argument.  Its workspace is a fixed array of BB_NOALLOC_SCRATCH_BYTES in
+ * the library's code object, one per GPU, held until the process ends; the
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ *   band, ld_band, n, bw, tw, dtype, d, e, tuning, stream: as for bb_reduce,
+ *            on the device current at the call.
+ *   status   device pointer to one uint32_t, or NULL: receives the launch's
+ *            status word when the reduction is done (0 = completed, nonzero =
+ *            a bounded wait expired, as bb_device_status reports it).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the call resets what must start at zero): calls that overlap on
+ * one GPU (concurrent streams, or host threads) race and must be serialised
+ * by the caller.  Errors: as bb_reduce, and BB_ERR_WORKSPACE when the shape
+ * needs more than BB_NOALLOC_SCRATCH_BYTES (bb_workspace_bytes); n = 16384,
+ * bw = 64, tw = 16 fp32 needs 8.3 MiB.
+ */
+bb_status bb_reduce_noalloc(const void *band, int64_t ld_band, int64_t n, int32_t bw, int32_t tw, int32_t dtype,
+                            void *d, void *e, void *status, const bb_tuning *tuning, void *stream);
+
 /*
  * The three stages bb_reduce runs, for callers that time or interleave them:
  * bb_pack, then bb_run_passes over passes 0 .. passes-1 (in one call, or
