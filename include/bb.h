@@ -105,15 +105,30 @@ typedef struct {
   double flops;       /* floating-point operations of all reflectors/applies */
 } bb_plan_info;
 
-/* Plan for (n, bw, tw, dtype).  out: host pointer.  Errors: BB_ERR_ARG. */
+/* Plan for (n, bw, tw, dtype): the pass list (page "Accelerating
+ * Bidiagonalization of Banded Matrices through Memory-Aware Bulge-Chasing on
+ * GPUs", bandwidth-tiling passage: each pass takes TW diagonals off the
+ * current bandwidth), the sweeps and cycles of each pass (same page, the
+ * passage on the cycle's window moving BW down the band per cycle), and the
+ * algorithmic bytes by which that page's profiling section rates the kernel.
+ * out: host pointer.  Errors: BB_ERR_ARG. */
 bb_status bb_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, bb_plan_info *out);
 
-/* Bytes of device workspace bb_reduce needs (working band + counters).
+/* Bytes of device workspace bb_reduce needs: the working band, whose rows
+ * hold the bw + 2 min(tw, bw-1) + 1 diagonals a pass's bulges can reach
+ * (page "Accelerating Bidiagonalization of Banded Matrices through
+ * Memory-Aware Bulge-Chasing on GPUs": a cycle's window spans 1 + BW + TW
+ * entries in each direction), plus the schedulers' counters.
  * bytes: host pointer.  Errors: BB_ERR_ARG, BB_ERR_UNSUPPORTED. */
 bb_status bb_workspace_bytes(int64_t n, int32_t bw, int32_t tw, int32_t dtype, size_t *bytes);
 
 /*
- * Reduces the band to bidiagonal form.
+ * Reduces the band to bidiagonal form: every pass, sweep and cycle of the
+ * page "Accelerating Bidiagonalization of Banded Matrices through
+ * Memory-Aware Bulge-Chasing on GPUs" (Algorithm 1: the sweeps' schedule;
+ * Algorithm 2: one cycle's row and column reflectors and their applies), in
+ * the order of the sequential chase of the page "A two-stage reduction on an
+ * Apple M5 Pro", section 6, whose results it reproduces bit for bit.
  *   band     device, read only: row i holds A(i, i+o) at band[i*ld_band + o],
  *            o = 0..bw; entries with i+o >= n are ignored.
  *   ld_band  >= bw + 1 (elements).
@@ -176,7 +191,7 @@ bb_status bb_reduce_noalloc(const void *band, int64_t ld_band, int64_t n, int32_
  * bb_run_passes: runs passes first .. first+count-1 (count >= 0) in order,
  *   as bb_run_pass would one by one.  Under BB_SCHED_DEFAULT, consecutive
  *   passes that run on the LDS group kernel with register tiles of one
- *   family (8/9 or 16/17 entries) share one launch, at most 8 passes each:
+ *   family (8/9 or 16/17 entries) share one launch, at most 4 passes each:
  *   the first sweep group of a pass starts on rows the previous pass is done
  *   with while that pass still runs (each row's owner in the previous pass
  *   publishes when it is done with the row).  bb_run_pass never shares a
@@ -204,14 +219,20 @@ bb_status bb_launch_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const
                          int32_t *launch_of_pass, int32_t capacity, int32_t *launches);
 
 /* Copies the working band left in `work` by the last bb_reduce with the same
- * (n, bw, tw, dtype) to dst (device, n * ld elements of dtype; element (i,j)
+ * (n, bw, tw, dtype) -- the whole matrix state after the passes, fill and
+ * annihilated entries included (page "Accelerating Bidiagonalization of
+ * Banded Matrices through Memory-Aware Bulge-Chasing on GPUs", Algorithm 2
+ * passage: annihilated entries are written back as zeros) -- to dst (device, n * ld elements of dtype; element (i,j)
  * at dst[i*ld + j-i+sub] with ld, sub from bb_plan).  Errors: BB_ERR_ARG,
  * BB_ERR_HIP. */
 bb_status bb_export_band(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *dst,
                          void *stream);
 
 /* Synchronises `stream` and reports the device-side status word of the
- * last bb_reduce on `work` (BB_OK or BB_ERR_TIMEOUT).  Errors: BB_ERR_ARG,
+ * last bb_reduce on `work` (BB_OK or BB_ERR_TIMEOUT): whether every bounded
+ * wait of the sweep dependency rule (page "A two-stage reduction on an Apple
+ * M5 Pro", section 6: a sweep waits until the previous sweep has finished
+ * the step two ahead) ended before its bound.  Errors: BB_ERR_ARG,
  * BB_ERR_HIP. */
 bb_status bb_device_status(const void *work, int64_t n, int32_t bw, int32_t tw, int32_t dtype, void *stream);
 
