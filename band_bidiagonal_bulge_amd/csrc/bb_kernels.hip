@@ -164,6 +164,101 @@ __device__ void col_half(const B &A, const Cyc &q, const T *ys) {
   }
 }
 
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// 16-byte chunks that cover MAXM consecutive entries from any element-aligned
+// start: one staged row of the block.
+template <typename T, int MAXM>
+constexpr int stage_chunks() {
+  return (MAXM * int(sizeof(T)) + 16 - int(sizeof(T)) + 15) / 16;
+}
+
+// Row half with the block staged in LDS (persistent kernel, wide tiles whose
+// block fits): the workgroup first copies the 16-byte chunks covering rows
+// r..ch, columns c..ch from memory straight into LDS (LDS-direct loads,
+// consecutive chunks on consecutive lanes, so one load instruction reads a
+// few whole lines instead of one piece of 64 different rows).  Each thread
+// then takes its row from LDS, applies the reflector formed from row r in
+// LDS and puts the row back; the block is then stored element by element
+// (consecutive lanes, consecutive addresses).  Arithmetic, operation order
+// and results are those of row_half.
+template <typename T, int MAXM, bool FULL, int AUX>
+__device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned char *blk, T *ys) {
+  constexpr int CH = stage_chunks<T, MAXM>();
+  constexpr int RB = CH * 16;  // LDS bytes per staged row
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int lane = tid & 63;
+  const int m = FULL ? MAXM : q.m;
+  const int nr = int(q.ch - q.r) + 1;
+  const uint32_t rstep = A.row_step();
+  const uint32_t o0 = A.off(q.r, q.c);
+  const int nch = nr * CH;
+  for (int e0 = tid - lane; e0 < nch; e0 += nt) {
+    const int e = e0 + lane;
+    if (e < nch) {
+      const int i = e / CH;
+      const uint32_t src = ((o0 + uint32_t(i) * rstep) & ~15u) + uint32_t(e - i * CH) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(A.r, (lds_ptr_t)(blk + e0 * 16), 16, src, 0, 0, AUX);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  const T *x0 = reinterpret_cast<const T *>(blk + (o0 & 15u));  // row r, columns c..ch
+  const Refl<T> h = house<T, MAXM, FULL>(x0, m);
+  T v[MAXM];
+  for (int i = tid; i < nr; i += nt) {
+    const uint32_t o = o0 + uint32_t(i) * rstep;
+    T *row = reinterpret_cast<T *>(blk + i * RB + (o & 15u));
+#pragma unroll
+    for (int j = 0; j < MAXM; ++j) v[j] = (FULL || j < m) ? row[j] : T(0);
+    if (i == 0) {
+      if (h.nz) v[0] = h.beta;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j) v[j] = T(0);
+    } else if (h.nz) {
+      T s = T(0);
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) s = fma_(v[j], x0[j], s);
+      const T w = fma_(s, h.inv, v[0]);
+      const T tw = h.tau * w;
+      v[0] = v[0] - tw;
+#pragma unroll
+      for (int j = 1; j < MAXM; ++j)
+        if (FULL || j < m) v[j] = fma_(-tw, x0[j] * h.inv, v[j]);
+    }
+    const int ic = i - int(q.c - q.r);  // row c + ic
+    if (ic >= 0) ys[ic] = v[0];
+    if (i == 0) {
+      store_seg<T, MAXM, FULL>(A, o, v, m);  // row r: (beta, 0, ..., 0); others still read it in LDS
+    } else if (h.nz) {
+#pragma unroll
+      for (int j = 0; j < MAXM; ++j)
+        if (FULL || j < m) row[j] = v[j];
+    }
+  }
+  if (!h.nz) return;  // uniform: every thread formed the same reflector; rows r+1..ch unchanged
+  __syncthreads();
+  // rows r+1..ch, element by element: consecutive lanes store consecutive
+  // entries of a row
+  const int ne = (nr - 1) * m;
+  for (int e = tid; e < ne; e += nt) {
+    const int i = 1 + e / m;
+    const int j = e - (i - 1) * m;
+    const uint32_t o = o0 + uint32_t(i) * rstep;
+    A.st_(o + uint32_t(j * int(sizeof(T))), reinterpret_cast<const T *>(blk + i * RB + (o & 15u))[j]);
+  }
+}
+
+template <typename T, int MAXM, int AUX>
+__device__ __forceinline__ void row_half_staged_any(const Band<T, AUX> &A, const Cyc &q, unsigned char *blk, T *ys) {
+  if (q.m == MAXM)
+    row_half_staged<T, MAXM, true, AUX>(A, q, blk, ys);
+  else
+    row_half_staged<T, MAXM, false, AUX>(A, q, blk, ys);
+}
+
 template <typename T, int MAXM, class B>
 __device__ __forceinline__ void row_half_any(const B &A, const Cyc &q, T *xs, T *ys) {
   if (q.m == MAXM)
@@ -237,6 +332,9 @@ __device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t nee
 // time (WaitClock); on expiry the workgroup sets the status word and stops,
 // and every other workgroup stops at its next wait or claim.
 //
+// STAGED: row halves go through row_half_staged (the block in LDS, coalesced
+// copies) instead of row_half (one row per lane straight to VGPRs).
+//
 // AUX selects how band data crosses between workgroups (and XCDs, whose L2
 // caches are not coherent with each other): kSc1 makes every band access an
 // agent-coherent one, so completing the stores (vmcnt 0) before the counter
@@ -246,12 +344,13 @@ __device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t nee
 #ifndef BB_PERSIST_AUX
 #define BB_PERSIST_AUX 16
 #endif
-template <typename T, int MAXM, int AUX>
+template <typename T, int MAXM, int AUX, bool STAGED>
 __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, int64_t n, int b, int t,
                                                  int64_t nsweeps, uint32_t *sync, uint32_t spin_limit) {
   const Band<T, AUX> A = make_band<T, AUX>(a, ld, sub, n);
   __shared__ T xs[MAXM];
   __shared__ T ys[MAXM];
+  extern __shared__ __attribute__((aligned(16))) unsigned char blk[];  // staged block (row halves)
   __shared__ int64_t sR;
   __shared__ int sgo;
   uint32_t *status = sync;
@@ -302,7 +401,10 @@ __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, 
         }
         BB_TICK(t_wait);
         if (h == 0) {
-          row_half_any<T, MAXM>(A, q, xs, ys);
+          if constexpr (STAGED)
+            row_half_staged_any<T, MAXM, AUX>(A, q, blk, ys);
+          else
+            row_half_any<T, MAXM>(A, q, xs, ys);
           BB_TICK(t_row);
         } else {
           col_half_any<T, MAXM>(A, q, ys);
@@ -400,12 +502,30 @@ hipError_t step_dispatch(int maxm, void *wband, const Geometry &g, int b, int t,
   }
 }
 
+// LDS for the staged row half: the block's rows (at most b + t + 1) of
+// stage_chunks 16-byte chunks.  Staging pays for wide tiles (t + 1 >= 32)
+// on blocks of at least kStageMinBytes (measured: the unstaged half's
+// per-lane row accesses, one row per lane, cost 2-5x the staged copies once
+// every CU is busy; below about 10 KB per block the extra LDS pass costs
+// more than it saves); other blocks, and blocks above kStageLdsBytes, take
+// the unstaged row half.
+#ifndef BB_PERSIST_STAGE
+#define BB_PERSIST_STAGE 1
+#endif
+constexpr size_t kStageLdsBytes = 64 * 1024;
+constexpr size_t kStageMinBytes = 10 * 1024;
+
 template <typename T, int MAXM>
 hipError_t persist_t(void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync, int grid,
                      int nt, uint32_t spin_limit, hipStream_t st) {
-  hipLaunchKernelGGL((k_persist<T, MAXM, BB_PERSIST_AUX>), dim3(unsigned(grid)), dim3(nt), 0, st,
-                     static_cast<T *>(wband),
-                     int64_t(g.stride), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
+  const size_t lds = size_t(b + t + 1) * size_t(stage_chunks<T, MAXM>()) * 16;
+  const size_t block = size_t(b + t + 1) * size_t(MAXM) * sizeof(T);
+  if (BB_PERSIST_STAGE && MAXM >= 32 && block >= kStageMinBytes && lds <= kStageLdsBytes)
+    hipLaunchKernelGGL((k_persist<T, MAXM, BB_PERSIST_AUX, true>), dim3(unsigned(grid)), dim3(nt), lds, st,
+                       static_cast<T *>(wband), int64_t(g.stride), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
+  else
+    hipLaunchKernelGGL((k_persist<T, MAXM, BB_PERSIST_AUX, false>), dim3(unsigned(grid)), dim3(nt), 0, st,
+                       static_cast<T *>(wband), int64_t(g.stride), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
   return hipGetLastError();
 }
 
