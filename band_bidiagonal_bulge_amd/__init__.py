@@ -11,7 +11,7 @@ from ._lib import (BB_ERR_TIMEOUT, BB_ERR_WORKSPACE, BB_NOALLOC_SCRATCH_BYTES, B
                    BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
                    bb_reduce_noalloc,
-                   bb_launch_plan, bb_probe_stream, bb_probe_transpose_add, bb_run_pass, bb_run_passes,
+                   bb_launch_plan, bb_probe_norm_clocks, bb_probe_stream, bb_probe_transpose_add, bb_run_pass, bb_run_passes,
                    bb_status_str, bb_svals, bb_svals_split, bb_svals_workspace_bytes, bb_sym_device_status,
                    bb_sym_export_band, bb_sym_reduce, bb_sym_workspace_bytes, bb_tuning,
                    bb_workspace_bytes, lib)

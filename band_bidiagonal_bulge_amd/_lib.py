@@ -21,7 +21,7 @@ EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass
            "bb_launch_plan", "bb_export_band",
            "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce", "bb_sym_export_band",
            "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split", "bb_status_str",
-           "bb_probe_stream", "bb_probe_transpose_add", "bb_reduce_noalloc")
+           "bb_probe_stream", "bb_probe_transpose_add", "bb_probe_norm_clocks", "bb_reduce_noalloc")
 
 
 class bb_tuning(ctypes.Structure):
@@ -105,13 +105,14 @@ def lib():
         L.bb_reduce_noalloc.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, ctypes.POINTER(bb_tuning), vp]
         L.bb_probe_stream.argtypes = [vp, vp, vp, i64, i32, vp]
         L.bb_probe_transpose_add.argtypes = [vp, vp, i32, i32, vp]
+        L.bb_probe_norm_clocks.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.bb_status_str.argtypes = [i32]
         L.bb_status_str.restype = ctypes.c_char_p
         for f in ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_run_passes",
                   "bb_launch_plan", "bb_extract",
                   "bb_export_band", "bb_device_status", "bb_sym_workspace_bytes", "bb_sym_reduce",
                   "bb_sym_export_band", "bb_sym_device_status", "bb_svals_workspace_bytes", "bb_svals", "bb_svals_split",
-                  "bb_probe_stream", "bb_probe_transpose_add", "bb_reduce_noalloc"):
+                  "bb_probe_stream", "bb_probe_transpose_add", "bb_probe_norm_clocks", "bb_reduce_noalloc"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -269,6 +270,13 @@ def bb_probe_transpose_add(a_ptr: int, b_ptr: int, m: int, reps: int, stream: in
     rc = lib().bb_probe_transpose_add(a_ptr, b_ptr, m, reps, stream or None)
     if rc != BB_OK:
         raise BBError(rc, "bb_probe_transpose_add")
+
+
+def bb_probe_norm_clocks(m: int, mode: int, reps: int, x_ptr: int, out_ptr: int, clocks_ptr: int,
+                         stream: int) -> None:
+    rc = lib().bb_probe_norm_clocks(m, mode, reps, x_ptr, out_ptr, clocks_ptr, stream or None)
+    if rc != BB_OK:
+        raise BBError(rc, "bb_probe_norm_clocks")
 
 
 def bb_status_str(status: int) -> str:

@@ -11,7 +11,14 @@
 //                    form is the reference point), through 64 x 64 LDS tiles
 //                    so that both reads are coalesced; 12 bytes per element.
 //
-// Both repeat the whole operation `reps` times in one launch, so that launch
+//   k_probe_norm:    the latency of one reflector norm (the sum of squares
+//                    of the m - 1 entries below the pivot) in one wave, by
+//                    the serial FMA chain the reduction uses (every lane the
+//                    same entries) or by a DPP cross-lane reduction (one
+//                    entry per lane, then a broadcast): a chain of `reps`
+//                    dependent norms timed with the shader clock.
+//
+// Both bandwidth probes repeat the whole operation `reps` times in one launch, so that launch
 // cost weighs nothing at cache-sized footprints and a small footprint still
 // fills the chip: the work is cut into chunks (256 vectors; one 64 x 64
 // tile), the (repetition, chunk) pairs are dealt to the workgroups in turn,
@@ -72,10 +79,61 @@ __global__ void __launch_bounds__(256) k_probe_tadd(const float *a, float *b, in
   }
 }
 
+template <int M>
+__global__ void __launch_bounds__(64) k_probe_norm(const float *x, float *out, int32_t reps, int32_t mode,
+                                                   unsigned long long *clocks) {
+  const int lane = threadIdx.x;
+  float v[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) v[j] = x[j];
+  float mine = lane < M ? x[lane] : 0.f;
+  float acc = 0.f;
+  const uint64_t t0 = clock64();
+  if (mode == 0) {
+    for (int32_t r = 0; r < reps; ++r) {
+      float s = v[1] * v[1];
+#pragma unroll
+      for (int j = 2; j < M; ++j) s = __builtin_fmaf(v[j], v[j], s);
+      acc += s;
+      v[1] = v[1] + s * 1e-30f;  // the next norm depends on this one
+    }
+  } else {
+    for (int32_t r = 0; r < reps; ++r) {
+      float s = lane >= 1 ? mine * mine : 0.f;
+      // pairs, quads, rows of 16 (rotations), then rows into lane 63
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x124, 0xF, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x128, 0xF, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x142, 0xA, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x143, 0xC, 0xF, false));
+      s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
+      acc += s;
+      mine = mine + s * 1e-30f;
+    }
+  }
+  const uint64_t t1 = clock64();
+  if (lane == 0) *clocks = t1 - t0;
+  out[lane] = acc;
+}
+
 }  // namespace
 }  // namespace bb
 
 extern "C" {
+
+bb_status bb_probe_norm_clocks(int32_t m, int32_t mode, int32_t reps, const void *x, void *out, void *clocks,
+                               void *stream) {
+  if ((m != 17 && m != 33) || (mode != 0 && mode != 1) || reps < 1 || !x || !out || !clocks) return BB_ERR_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m == 17)
+    hipLaunchKernelGGL(bb::k_probe_norm<17>, dim3(1), dim3(64), 0, st, static_cast<const float *>(x),
+                       static_cast<float *>(out), reps, mode, static_cast<unsigned long long *>(clocks));
+  else
+    hipLaunchKernelGGL(bb::k_probe_norm<33>, dim3(1), dim3(64), 0, st, static_cast<const float *>(x),
+                       static_cast<float *>(out), reps, mode, static_cast<unsigned long long *>(clocks));
+  return hipGetLastError() == hipSuccess ? BB_OK : BB_ERR_HIP;
+}
 
 bb_status bb_probe_stream(const void *x, const void *y, void *z, int64_t n, int32_t reps, void *stream) {
   if (!x || !y || !z || n < 0 || (n & 3) || n * int64_t(sizeof(float)) >= (int64_t(1) << 31) || reps < 1 ||

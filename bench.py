@@ -467,6 +467,26 @@ def probe_ceilings(bbm, torch, dev, stream, sizes, reps=5, launch_bytes=4e9):
     return out
 
 
+def norm_clocks(bbm, torch, dev, stream, reps=20000):
+    """Shader clocks per reflector norm in one wave (bb_probe_norm_clocks):
+    the serial FMA chain the reduction uses against a DPP cross-lane
+    reduction, for the register tiles of 17 and 33 entries."""
+    x = torch.rand(64, dtype=torch.float32, device=dev)
+    out = torch.empty(64, dtype=torch.float32, device=dev)
+    clk = torch.zeros(1, dtype=torch.int64, device=dev)
+    res = {}
+    for m in (17, 33):
+        for mode, name in ((0, "serial_fma"), (1, "dpp_reduction")):
+            best = None
+            for _ in range(3):
+                bbm.bb_probe_norm_clocks(m, mode, reps, x.data_ptr(), out.data_ptr(), clk.data_ptr(), stream.cuda_stream)
+                torch.cuda.synchronize()
+                c = clk.item() / reps
+                best = c if best is None else min(best, c)
+            res[f"m{m}_{name}"] = round(best, 1)
+    return res
+
+
 def scheduler_times(bbm, torch, tb, w, dt, work, stream, reps=2):
     """Median ms per reduction of the whole path under the step scheduler
     (one launch per step, the page's design) and the persistent scheduler,
@@ -713,6 +733,7 @@ def main():
         for p in probes:
             p["frac"] = round(achieved / p["GBps"], 5)
         level["probes"] = probes
+        out["norm_clocks"] = norm_clocks(bbm, torch, dev, stream)
     out["roofline"]["working_set"] = level
     if not args.no_schedulers:
         out["schedulers_ms"] = scheduler_times(bbm, torch, tb, w, dt, work, stream)

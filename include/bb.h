@@ -340,6 +340,17 @@ bb_status bb_probe_stream(const void *x, const void *y, void *z, int64_t n, int3
  * distinct; m^2 <= 2^30.  Errors: BB_ERR_ARG, BB_ERR_HIP. */
 bb_status bb_probe_transpose_add(const void *a, void *b, int32_t m, int32_t reps, void *stream);
 
+/* Shader clocks of `reps` dependent reflector norms (the sum of squares of
+ * m - 1 fp32 entries) in one wave: mode 0 sums serially with FMAs in every
+ * lane (the reduction's own order, page "Accelerating Bidiagonalization of
+ * Banded Matrices through Memory-Aware Bulge-Chasing on GPUs", Algorithm 2
+ * memory-strategy passage: the TW+1 staged entries form the reflector),
+ * mode 1 by a DPP cross-lane reduction, one entry per lane.  m: 17 or 33;
+ * x: device, 64 floats; out: device, 64 floats (scratch); clocks: device,
+ * one uint64 (written).  Errors: BB_ERR_ARG, BB_ERR_HIP. */
+bb_status bb_probe_norm_clocks(int32_t m, int32_t mode, int32_t reps, const void *x, void *out, void *clocks,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,3 +46,22 @@ def test_probe_argument_checks():
         bbm.bb_probe_transpose_add(p, p, 2, 1, 0)  # in place
     with pytest.raises(bbm.BBError):
         bbm.bb_probe_transpose_add(p, p + 16, -1, 1, 0)
+
+
+@pytest.mark.parametrize("m", [17, 33])
+def test_norm_probe_runs(m):
+    import torch
+    log(f"norm probe m={m}")
+    x = torch.rand(64, device="cuda:0")
+    out = torch.zeros(64, device="cuda:0")
+    clk = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    for mode in (0, 1):
+        bbm.bb_probe_norm_clocks(m, mode, 100, x.data_ptr(), out.data_ptr(), clk.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert clk.item() > 0
+        # one norm alone: both ways sum the same squares to within rounding
+        ref = float((x[1:m].double() ** 2).sum())
+        assert abs(out[0].item() / 100 - ref) <= 1e-4 * ref
+    with pytest.raises(bbm.BBError):
+        bbm.bb_probe_norm_clocks(16, 0, 1, x.data_ptr(), out.data_ptr(), clk.data_ptr(), 0)
