@@ -71,6 +71,10 @@ bb_status hip_status(hipError_t e) { return e == hipSuccess ? BB_OK : BB_ERR_HIP
 // a row half and per column of a column half (b + t + 1 each), in whole
 // waves, at most 256.
 int default_threads(const bb::Pass &p) { return std::min(256, std::max(64, (p.b + p.t + 1 + 63) / 64 * 64)); }
+// The persistent kernel with staged row halves: its copies in and out use
+// every thread, so more waves pay (measured on the n = 32768 and 65536
+// workloads): 256 threads above 128 rows per block, else 128.
+int staged_threads(const bb::Pass &p) { return p.b + p.t + 1 > 128 ? 256 : 128; }
 
 bb_status run_step_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
                         hipStream_t st) {
@@ -119,7 +123,7 @@ bb_status run_persistent_pass(void *wband, const bb::Geometry &g, const bb::Pass
       bb::launch_fill_u32(sync + bb::kSyncHeader, ns * bb::kLine, 0u, st) != hipSuccess)
     return BB_ERR_HIP;
   int nt = tu.threads_per_block;
-  if (nt == 0) nt = default_threads(p);
+  if (nt == 0) nt = bb::persist_staged(g.dtype, maxm, p.b, p.t) ? staged_threads(p) : default_threads(p);
   int64_t grid = tu.max_blocks > 0 ? tu.max_blocks : 2 * int64_t(device_cus());
   grid = std::min<int64_t>(grid, ns);
   const uint32_t spin = wait_ticks(tu);

@@ -53,6 +53,8 @@ hipError_t launch_group(const GroupRun &run, void *wband, const Geometry &g, int
 // LDS bytes one workgroup stages per cycle for a pass (b, t) with register
 // tile maxm.
 size_t stage_lds_bytes(int dtype, int maxm, int b, int t);
+// Whether the persistent kernel stages the pass's row-half blocks in LDS.
+bool persist_staged(int dtype, int maxm, int b, int t);
 
 // Symmetric band -> tridiagonal (bb_sym.hip).  pack: user upper rows into the
 // working band (fill region zeroed); persist: one pass, `grid` workgroups of

@@ -516,11 +516,17 @@ constexpr size_t kStageLdsBytes = 64 * 1024;
 constexpr size_t kStageMinBytes = 10 * 1024;
 
 template <typename T, int MAXM>
+bool staged_t(int b, int t) {
+  const size_t lds = size_t(b + t + 1) * size_t(stage_chunks<T, MAXM>()) * 16;
+  const size_t block = size_t(b + t + 1) * size_t(MAXM) * sizeof(T);
+  return BB_PERSIST_STAGE && MAXM >= 32 && block >= kStageMinBytes && lds <= kStageLdsBytes;
+}
+
+template <typename T, int MAXM>
 hipError_t persist_t(void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync, int grid,
                      int nt, uint32_t spin_limit, hipStream_t st) {
   const size_t lds = size_t(b + t + 1) * size_t(stage_chunks<T, MAXM>()) * 16;
-  const size_t block = size_t(b + t + 1) * size_t(MAXM) * sizeof(T);
-  if (BB_PERSIST_STAGE && MAXM >= 32 && block >= kStageMinBytes && lds <= kStageLdsBytes)
+  if (staged_t<T, MAXM>(b, t))
     hipLaunchKernelGGL((k_persist<T, MAXM, BB_PERSIST_AUX, true>), dim3(unsigned(grid)), dim3(nt), lds, st,
                        static_cast<T *>(wband), int64_t(g.stride), g.sub, g.n, b, t, nsweeps, sync, spin_limit);
   else
@@ -551,6 +557,23 @@ size_t stage_lds_bytes(int dtype, int maxm, int b, int t) {
   (void)b;
   (void)t;
   return size_t(2 * maxm) * (dtype == 1 ? 8 : (dtype == 2 ? 2 : 4));
+}
+
+template <typename T>
+bool staged_dispatch(int maxm, int b, int t) {
+  switch (maxm) {
+    case 32: return staged_t<T, 32>(b, t);
+    case 33: return staged_t<T, 33>(b, t);
+    case 64: return staged_t<T, 64>(b, t);
+    case 65: return staged_t<T, 65>(b, t);
+    default: return false;
+  }
+}
+
+bool persist_staged(int dtype, int maxm, int b, int t) {
+  if (dtype == 1) return staged_dispatch<double>(maxm, b, t);
+  if (dtype == 2) return staged_dispatch<_Float16>(maxm, b, t);
+  return staged_dispatch<float>(maxm, b, t);
 }
 
 hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,
