@@ -506,14 +506,14 @@ hipError_t step_dispatch(int maxm, void *wband, const Geometry &g, int b, int t,
 // stage_chunks 16-byte chunks.  Staging pays for wide tiles (t + 1 >= 32)
 // on blocks of at least kStageMinBytes (measured: the unstaged half's
 // per-lane row accesses, one row per lane, cost 2-5x the staged copies once
-// every CU is busy; below about 10 KB per block the extra LDS pass costs
-// more than it saves); other blocks, and blocks above kStageLdsBytes, take
-// the unstaged row half.
+// every CU is busy; the smallest wide block, 64 x 32 fp32, still gains with
+// 128 threads); other blocks, and blocks above kStageLdsBytes, take the
+// unstaged row half.
 #ifndef BB_PERSIST_STAGE
 #define BB_PERSIST_STAGE 1
 #endif
 constexpr size_t kStageLdsBytes = 64 * 1024;
-constexpr size_t kStageMinBytes = 10 * 1024;
+constexpr size_t kStageMinBytes = 8 * 1024;
 
 template <typename T, int MAXM>
 bool staged_t(int b, int t) {
