@@ -88,3 +88,91 @@ def test_rule_cannot_be_loosened():
     assert uncovered_conflicts(50, 4, 2, lag=2) > 0
     # lag 3 is not enough for b' = 1
     assert uncovered_conflicts(50, 2, 1, lag=3) > 0
+
+
+# ---- Early and late parts of a half (persistent kernel, b' >= 4) ----------
+#
+# In an interior cycle (k >= 1, full blocks) of a pass with b' >= 4, the
+# predecessor's next half touches only t + 1 rows of a row half's block (rows
+# c-1 .. c+t-1, its column half of cycle k) and only t + 1 columns of a column
+# half's block (columns c+b-1 .. c+b+t-1, its row half of cycle k+1).  The rest
+# of the block (the early part) needs one half less of the predecessor: the
+# kernel may run it before the half's usual wait, and the rest (the late part)
+# after it.  With b' = 3 the early part can meet a half of the sweep three
+# back that the weaker wait no longer orders (a scan of every shape with
+# b <= 40 finds b' = 3 the only failing case), so the split needs b' >= 4.
+
+def split_parts(n, b, t, R, q, min_bp=4):
+    """(early cells, late cells) of half q of sweep R, or None when the half
+    runs whole (first cycle, truncated blocks, b' < min_bp)."""
+    k, h = q // 2, q % 2
+    c = R + (b - t) + k * b
+    if b - t < min_bp or k == 0 or R == 0 or c + t + b > n - 1:
+        return None
+    cells = half_cells(n, b, t, R, k, h)
+    if h == 0:
+        late = {(i, j) for (i, j) in cells if c - 1 <= i <= c + t - 1}
+    else:
+        late = {(i, j) for (i, j) in cells if c + b - 1 <= j <= c + b + t - 1}
+    return cells - late, late
+
+
+def uncovered_split_conflicts(n, b, t, early_lag=1, min_bp=4):
+    """Conflicts left unordered when the early part of a split half waits for
+    q + early_lag halves of the predecessor instead of q + d, and the late
+    part for the usual q + d."""
+    bp = b - t
+    ns = max(n - bp - 1, 0)
+    K = [cycles_of_sweep(n, b, t, R) for R in range(ns)]
+    ops = {}  # (R, q) -> [(cells, need on R-1)]
+    for R in range(ns):
+        for q in range(2 * K[R]):
+            full = rule(b, t, q // 2, q % 2, K[R - 1]) if R > 0 else 0
+            sp = split_parts(n, b, t, R, q, min_bp)
+            if sp is None:
+                ops[(R, q)] = [(half_cells(n, b, t, R, q // 2, q % 2), full)]
+            else:
+                ops[(R, q)] = [(sp[0], min(q + early_lag, 2 * K[R - 1])), (sp[1], full)]
+    cells = {key: set().union(*[c for c, _ in v]) for key, v in ops.items()}
+
+    def need_whole(R, q):  # what half q of R waited for on R-1, all parts done
+        return max(w for _, w in ops[(R, q)])
+
+    bad = 0
+    for R in range(1, ns):
+        for q in range(2 * K[R]):
+            for (cs, w0) in ops[(R, q)]:
+                done = {}
+                Rp, w = R - 1, w0
+                while Rp >= 0 and w > 0:
+                    if w == 2 * K[Rp]:
+                        done.update({x: 2 * K[x] for x in range(Rp + 1)})
+                        break
+                    done[Rp] = w
+                    if Rp == 0:
+                        break
+                    w = need_whole(Rp, w - 1)
+                    Rp -= 1
+                for Rp in range(R):
+                    for qp in range(2 * K[Rp]):
+                        if done.get(Rp, 0) <= qp and cells[(Rp, qp)] & cs:
+                            bad += 1
+    return bad
+
+
+@pytest.mark.parametrize("n,b,t", [(200, 64, 16), (150, 48, 16), (120, 32, 16), (100, 18, 15), (90, 12, 4),
+                                   (130, 40, 8), (96, 20, 16), (80, 7, 3), (300, 128, 32), (400, 96, 32),
+                                   (120, 19, 15)])
+def test_early_part_needs_one_half_less(n, b, t):
+    assert uncovered_split_conflicts(n, b, t) == 0
+
+
+def test_early_part_cannot_start_two_halves_early():
+    # the early part still needs the predecessor's previous half
+    assert uncovered_split_conflicts(200, 64, 16, early_lag=0) > 0
+
+
+def test_split_needs_target_band_of_four():
+    # with b' = 3 a sweep further back still overlaps the early part
+    assert uncovered_split_conflicts(100, 18, 15, min_bp=3) > 0
+    assert uncovered_split_conflicts(40, 4, 1, min_bp=3) > 0
