@@ -7,7 +7,7 @@ for device memory and the stream only).
 """
 from __future__ import annotations
 
-from ._lib import (BB_ERR_TIMEOUT, BB_ERR_WORKSPACE, BB_NOALLOC_SCRATCH_BYTES, BB_F16, BB_F32, BB_F64, BB_OK, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
+from ._lib import (BB_ERR_TIMEOUT, BB_ERR_WORKSPACE, BB_NOALLOC_SCRATCH_BYTES, BB_F16, BB_F32, BB_F64, BB_OK, BB_SCHED_BARRIER, BB_SCHED_DEFAULT, BB_SCHED_GROUP, BB_SCHED_PERSISTENT, BB_SCHED_STEP, EXPORTS,
                    BBError,
                    bb_device_status, bb_export_band, bb_extract, bb_pack, bb_plan, bb_plan_info, bb_reduce,
                    bb_reduce_noalloc,

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libbb.so")
 
 BB_F32, BB_F64, BB_F16 = 0, 1, 2
 BB_OK, BB_ERR_ARG, BB_ERR_WORKSPACE, BB_ERR_HIP, BB_ERR_UNSUPPORTED, BB_ERR_TIMEOUT = range(6)
-BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT, BB_SCHED_GROUP = 0, 1, 2, 3
+BB_SCHED_DEFAULT, BB_SCHED_STEP, BB_SCHED_PERSISTENT, BB_SCHED_GROUP, BB_SCHED_BARRIER = 0, 1, 2, 3, 4
 
 # Every symbol include/bb.h declares.
 EXPORTS = ("bb_plan", "bb_workspace_bytes", "bb_reduce", "bb_pack", "bb_run_pass", "bb_run_passes", "bb_extract",

@@ -113,6 +113,28 @@ uint32_t wait_ticks(const bb_tuning &tu) {
   return uint32_t((tu.spin_limit > 0 ? tu.spin_limit : kDefaultWaitUs) * 100);
 }
 
+// The grid-barrier scheduler: one launch per pass, one resident workgroup
+// per CU (at most one per sweep), the step scheduler's steps separated by a
+// device-wide barrier.
+bb_status run_barrier_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
+                           uint32_t *sync, hipStream_t st) {
+  const int maxm = pick_maxm(p.t);
+  const int64_t ns = bb::sweeps_of(g.n, p);
+  if (ns == 0) return BB_OK;
+  const int32_t s = stagger_for(p, tu.stagger);
+  int nt = tu.threads_per_block;
+  if (nt == 0) nt = default_threads(p);
+  const int64_t grid = std::min<int64_t>(tu.max_blocks > 0 ? std::min(tu.max_blocks, device_cus()) : device_cus(), ns);
+  // arrivals and the generation start at zero for every pass
+  if (bb::launch_fill_u32(sync + bb::kClaim, 1, 0u, st) != hipSuccess ||
+      bb::launch_fill_u32(sync + bb::kSyncHeader, bb::kLine, 0u, st) != hipSuccess)
+    return BB_ERR_HIP;
+  if (bb::launch_barrier(maxm, wband, g, p.b, p.t, s, ns, bb::steps_of(g.n, p, s), sync, int(grid), nt,
+                         wait_ticks(tu), st) != hipSuccess)
+    return BB_ERR_HIP;
+  return BB_OK;
+}
+
 bb_status run_persistent_pass(void *wband, const bb::Geometry &g, const bb::Pass &p, const bb_tuning &tu,
                               uint32_t *sync, hipStream_t st) {
   const int maxm = pick_maxm(p.t);
@@ -259,7 +281,7 @@ bb_status check_work(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const voi
 bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
   std::memset(tu, 0, sizeof(*tu));
   if (tuning) *tu = *tuning;
-  if (tu->scheduler < 0 || tu->scheduler > BB_SCHED_GROUP) return BB_ERR_ARG;
+  if (tu->scheduler < 0 || tu->scheduler > BB_SCHED_BARRIER) return BB_ERR_ARG;
   if (tu->stagger != 0 && (tu->stagger < 2 || tu->stagger > 64)) return BB_ERR_ARG;
   if (tu->threads_per_block != 0 && (tu->threads_per_block < 64 || tu->threads_per_block > 256 ||
                                      tu->threads_per_block % 64 != 0))
@@ -275,7 +297,8 @@ bb_status check_tuning(const bb_tuning *tuning, bb_tuning *tu) {
 bb_status run_passes(void *work, const bb::Geometry &g, const std::vector<bb::Pass> &passes, int first, int count,
                      const bb_tuning &tu, hipStream_t st) {
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
-  if (g.dtype == BB_F16 && tu.scheduler == BB_SCHED_STEP) return BB_ERR_UNSUPPORTED;  // no fp16 step kernel
+  if (g.dtype == BB_F16 && (tu.scheduler == BB_SCHED_STEP || tu.scheduler == BB_SCHED_BARRIER))
+    return BB_ERR_UNSUPPORTED;  // no fp16 step or barrier kernel
   bb_status rc = BB_OK;
   for (const LaunchItem &it : plan_launches(g, passes, first, count, tu)) {
     const bb::Pass &p = passes[size_t(it.first)];
@@ -283,6 +306,8 @@ bb_status run_passes(void *work, const bb::Geometry &g, const std::vector<bb::Pa
       rc = run_group_launch(work, g, it, tu, sync, st);
     else if (tu.scheduler == BB_SCHED_STEP)
       rc = run_step_pass(work, g, p, tu, st);
+    else if (tu.scheduler == BB_SCHED_BARRIER)
+      rc = run_barrier_pass(work, g, p, tu, sync, st);
     else
       rc = run_persistent_pass(work, g, p, tu, sync, st);
     if (rc != BB_OK) return rc;
@@ -500,7 +525,7 @@ bb_status bb_sym_reduce(const void *band, int64_t ld_band, int64_t n, int32_t bw
   if (rc != BB_OK) return rc;
   bb_tuning tu;
   if ((rc = check_tuning(tuning, &tu)) != BB_OK) return rc;
-  if (tu.scheduler == BB_SCHED_STEP) return BB_ERR_UNSUPPORTED;
+  if (tu.scheduler == BB_SCHED_STEP || tu.scheduler == BB_SCHED_BARRIER) return BB_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint32_t *sync = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + g.sync_offset);
   if (bb::launch_sym_pack(band, ld_band, work, g, st) != hipSuccess ||
@@ -647,7 +672,8 @@ bb_status bb_launch_plan(int64_t n, int32_t bw, int32_t tw, int32_t dtype, const
   bb_tuning tu;
   bb_status rc = check_tuning(tuning, &tu);
   if (rc != BB_OK) return rc;
-  if (dtype == BB_F16 && tu.scheduler == BB_SCHED_STEP) return BB_ERR_UNSUPPORTED;  // as bb_run_passes
+  if (dtype == BB_F16 && (tu.scheduler == BB_SCHED_STEP || tu.scheduler == BB_SCHED_BARRIER))
+    return BB_ERR_UNSUPPORTED;  // as bb_run_passes
   const std::vector<bb::Pass> passes = bb::pass_list(bw, tw);
   if (capacity > 0 && capacity < int32_t(passes.size())) return BB_ERR_ARG;
   const std::vector<LaunchItem> items = plan_launches(g, passes, 0, int(passes.size()), tu);

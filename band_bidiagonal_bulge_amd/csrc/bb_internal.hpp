@@ -15,6 +15,12 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t count, uint32_t v, hipStream_t s
 
 // One-launch-per-step scheduler: launches nblk workgroups of nt threads for
 // sweeps Rlo .. Rlo+nblk-1 of step L (cycle k = L - s R each).
+// Grid-barrier scheduler: one launch of `grid` resident workgroups for the
+// whole pass; steps as launch_step (`steps` of them, stagger s); sync as for
+// launch_persist (status word, the claim word counts arrivals, the first
+// progress line holds the barrier generation; both start at zero).
+hipError_t launch_barrier(int maxm, void *wband, const Geometry &g, int b, int t, int s, int64_t nsweeps,
+                          int64_t steps, uint32_t *sync, int grid, int nt, uint32_t spin_limit, hipStream_t st);
 hipError_t launch_step(int maxm, void *wband, const Geometry &g, int b, int t, int64_t L, int s, int64_t Rlo,
                        int64_t nblk, int nt, hipStream_t st);
 

@@ -440,6 +440,68 @@ __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, 
 #undef BB_TICK
 }
 
+// Grid-barrier scheduler: one launch per pass with every workgroup resident
+// (one per CU).  Step L of the step scheduler -- every sweep R with cycle
+// k = L - s R in range -- is shared out among the workgroups, and all of them
+// meet at a device-wide barrier before step L + 1 (the page's Algorithm 1
+// schedule with the kernel boundary replaced by a barrier inside one
+// launch).  Band accesses are agent-coherent (sc1): a workgroup's stores are
+// complete (vmcnt 0) before it arrives, so the barrier orders the steps as
+// the kernel boundary does.  The barrier wait is bounded (WaitClock); on
+// expiry the status word is set and every workgroup leaves at its next
+// barrier.
+template <typename T, int MAXM>
+__global__ void __launch_bounds__(256) k_barrier(T *a, int64_t ld, int32_t sub, int64_t n, int b, int t, int s,
+                                                 int64_t nsweeps, int64_t steps, uint32_t *sync,
+                                                 uint32_t spin_limit) {
+  const Band<T, kSc1> A = make_band<T, kSc1>(a, ld, sub, n);
+  __shared__ T xs[MAXM];
+  __shared__ T ys[MAXM];
+  __shared__ int sgo;
+  uint32_t *status = sync;
+  uint32_t *arrived = sync + kClaim;  // arrivals at the current barrier
+  uint32_t *gen = sync + kSyncHeader;  // barrier generation, a line of its own
+  const int tid = threadIdx.x;
+  const int64_t bp = b - t;
+  for (int64_t L = 0; L < steps; ++L) {
+    // sweeps with 0 <= L - s R < K_R
+    const int64_t rhi = L / s < nsweeps - 1 ? L / s : nsweeps - 1;
+    const int64_t num = L * b - (n - 2 - bp), den = int64_t(s) * b - 1;
+    const int64_t rlo = num <= 0 ? 0 : (num + den - 1) / den;
+    for (int64_t R = rlo + blockIdx.x; R <= rhi; R += gridDim.x) {
+      const Cyc q(n, b, t, R, L - int64_t(s) * R);
+      row_half_any<T, MAXM>(A, q, xs, ys);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the column half reloads cells the row half stored
+      __syncthreads();
+      col_half_any<T, MAXM>(A, q, ys);
+      __syncthreads();  // xs, ys are reused by the next cycle
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0) {
+      // read the generation before arriving: it cannot move without us
+      const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool go = true;
+      if (atomicAdd(arrived, 1u) == gridDim.x - 1) {
+        __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gen, g0 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        WaitClock wc;
+        while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+          __builtin_amdgcn_s_sleep(1);
+          if (!wc.tick(spin_limit, status)) {
+            go = false;
+            break;
+          }
+        }
+      }
+      sgo = go && !launch_failed(status);
+    }
+    __syncthreads();
+    if (!sgo) return;
+  }
+}
+
 // User band (row-offset layout) -> working band with zeroed bulge room.
 template <typename T>
 __global__ void k_pack(const T *__restrict__ band, int64_t ld_band, int64_t n, int bw, T *__restrict__ a,
@@ -523,6 +585,30 @@ bool staged_t(int b, int t) {
 }
 
 template <typename T, int MAXM>
+hipError_t barrier_t(void *wband, const Geometry &g, int b, int t, int s, int64_t nsweeps, int64_t steps,
+                     uint32_t *sync, int grid, int nt, uint32_t spin_limit, hipStream_t st) {
+  hipLaunchKernelGGL((k_barrier<T, MAXM>), dim3(unsigned(grid)), dim3(nt), 0, st, static_cast<T *>(wband),
+                     int64_t(g.stride), g.sub, g.n, b, t, s, nsweeps, steps, sync, spin_limit);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t barrier_dispatch(int maxm, void *wband, const Geometry &g, int b, int t, int s, int64_t nsweeps,
+                            int64_t steps, uint32_t *sync, int grid, int nt, uint32_t spin_limit, hipStream_t st) {
+  switch (maxm) {
+    case 8: return barrier_t<T, 8>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    case 9: return barrier_t<T, 9>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    case 16: return barrier_t<T, 16>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    case 17: return barrier_t<T, 17>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    case 32: return barrier_t<T, 32>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    case 33: return barrier_t<T, 33>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    case 64: return barrier_t<T, 64>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    case 65: return barrier_t<T, 65>(wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int MAXM>
 hipError_t persist_t(void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync, int grid,
                      int nt, uint32_t spin_limit, hipStream_t st) {
   const size_t lds = size_t(b + t + 1) * size_t(stage_chunks<T, MAXM>()) * 16;
@@ -574,6 +660,14 @@ bool persist_staged(int dtype, int maxm, int b, int t) {
   if (dtype == 1) return staged_dispatch<double>(maxm, b, t);
   if (dtype == 2) return staged_dispatch<_Float16>(maxm, b, t);
   return staged_dispatch<float>(maxm, b, t);
+}
+
+hipError_t launch_barrier(int maxm, void *wband, const Geometry &g, int b, int t, int s, int64_t nsweeps,
+                          int64_t steps, uint32_t *sync, int grid, int nt, uint32_t spin_limit, hipStream_t st) {
+  if (g.dtype == 1)
+    return barrier_dispatch<double>(maxm, wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
+  if (g.dtype == 2) return hipErrorInvalidValue;  // no fp16 instantiation (as the step kernel)
+  return barrier_dispatch<float>(maxm, wband, g, b, t, s, nsweeps, steps, sync, grid, nt, spin_limit, st);
 }
 
 hipError_t launch_persist(int maxm, void *wband, const Geometry &g, int b, int t, int64_t nsweeps, uint32_t *sync,

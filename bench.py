@@ -17,7 +17,9 @@ Prints one JSON line:
                   fraction
   ms_per_reduction_events  median and min of the per-step event times
   schedulers_ms   the same path under the step scheduler (the page's one
-                  launch per step) and the persistent scheduler, and the sum
+                  launch per step), the grid-barrier scheduler (the same
+                  steps in one launch per pass, a device-wide barrier
+                  between steps) and the persistent scheduler, and the sum
                   of the per-pass times below (the group kernel, one launch
                   per pass)
   passes          each pass in a launch of its own (bb_run_pass), timed after
@@ -489,10 +491,11 @@ def norm_clocks(bbm, torch, dev, stream, reps=20000):
 
 def scheduler_times(bbm, torch, tb, w, dt, work, stream, reps=2):
     """Median ms per reduction of the whole path under the step scheduler
-    (one launch per step, the page's design) and the persistent scheduler,
-    for comparison with the default."""
+    (one launch per step, the page's design), the grid-barrier scheduler and
+    the persistent scheduler, for comparison with the default."""
     out = {}
-    for name, code in (("step", bbm.BB_SCHED_STEP), ("persistent", bbm.BB_SCHED_PERSISTENT)):
+    for name, code in (("step", bbm.BB_SCHED_STEP), ("barrier", bbm.BB_SCHED_BARRIER),
+                       ("persistent", bbm.BB_SCHED_PERSISTENT)):
         tun = bbm.tuning(scheduler=code)
         bbm.reduce(tb, w.bw, w.tw, tun, work)
         torch.cuda.synchronize()

@@ -65,11 +65,15 @@ typedef enum {
   BB_SCHED_DEFAULT = 0,   /* the fastest scheduler for the shape */
   BB_SCHED_STEP = 1,      /* one launch per step: step L runs every (R, k=L-s*R) */
   BB_SCHED_PERSISTENT = 2, /* resident workgroups; per-sweep progress counters */
-  BB_SCHED_GROUP = 3       /* resident workgroups each running a group of
+  BB_SCHED_GROUP = 3,      /* resident workgroups each running a group of
                               consecutive sweeps on a ring of band rows in LDS;
                               passes whose ring does not fit run PERSISTENT;
                               one launch per pass (DEFAULT also lets
                               consecutive group passes share a launch) */
+  BB_SCHED_BARRIER = 4     /* one launch per pass of resident workgroups (one
+                              per CU, at most max_blocks) running STEP's steps
+                              with a device-wide barrier between steps; fp32
+                              and fp64 only, general band only */
 } bb_scheduler;
 
 /* Optional tuning; pass NULL for the gfx950 defaults.  Zero fields take the

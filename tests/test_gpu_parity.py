@@ -84,7 +84,7 @@ def test_all_zero_and_zero_rows(dt):
     _check_bitwise(band, bw, tw)
 
 
-STEP, PERSIST, GROUP = 1, 2, 3
+STEP, PERSIST, GROUP, BARRIER = 1, 2, 3, 4
 
 
 @pytest.mark.parametrize("tun", [dict(scheduler=STEP), dict(scheduler=STEP, stagger=3),
@@ -96,7 +96,10 @@ STEP, PERSIST, GROUP = 1, 2, 3
                                  dict(scheduler=GROUP), dict(scheduler=GROUP, group_sweeps=1),
                                  dict(scheduler=GROUP, group_sweeps=2, max_blocks=1),
                                  dict(scheduler=GROUP, group_sweeps=3, max_blocks=2),
-                                 dict(scheduler=GROUP, group_sweeps=6, max_blocks=5)])
+                                 dict(scheduler=GROUP, group_sweeps=6, max_blocks=5),
+                                 dict(scheduler=BARRIER), dict(scheduler=BARRIER, stagger=3),
+                                 dict(scheduler=BARRIER, max_blocks=1),
+                                 dict(scheduler=BARRIER, max_blocks=3, threads_per_block=64)])
 @pytest.mark.parametrize("n,bw,tw,dt", [(900, 48, 16, "f32"), (700, 24, 7, "f64"), (400, 9, 2, "f32")])
 def test_scheduler_variants_bitwise(tun, n, bw, tw, dt):
     log(f"variant {tun} n={n} bw={bw} tw={tw} {dt}")
@@ -126,7 +129,21 @@ def test_fused_passes_bitwise(tun, n, bw, tw, dt):
     _check_bitwise(band, bw, tw, bbm.tuning(**tun))
 
 
-@pytest.mark.parametrize("sched", [PERSIST, GROUP, bbm.BB_SCHED_DEFAULT])
+@pytest.mark.parametrize("n,bw,tw,dt", [(500, 64, 32, "f64"), (300, 40, 31, "f32")])
+def test_barrier_scheduler_wide_tiles_bitwise(n, bw, tw, dt):
+    log(f"barrier scheduler n={n} bw={bw} tw={tw} {dt}")
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=6)
+    _check_bitwise(band, bw, tw, bbm.tuning(scheduler=BARRIER))
+
+
+def test_barrier_scheduler_refuses_half_precision():
+    import torch
+    band = torch.zeros(64, 9, dtype=torch.float16, device="cuda:0")
+    with pytest.raises(bbm.BBError):
+        bbm.reduce(band, 8, 4, bbm.tuning(scheduler=BARRIER))
+
+
+@pytest.mark.parametrize("sched", [PERSIST, GROUP, bbm.BB_SCHED_DEFAULT, BARRIER])
 def test_forced_timeout_reports_status(sched):
     # A spin limit of one poll makes the first wait on a predecessor expire;
     # every workgroup then stops and the launch ends normally.
