@@ -770,13 +770,12 @@ def _read_counter_csv(path, counter):
 
 def is_cycle_kernel(name, dtype):
     """The workload's cycle kernel in a profiler row: the general band's
-    k_group / k_persist / k_step in the workload's element type (not the
-    symmetric sweep groups, not the half-precision run)."""
+    k_group / k_persist / k_step / k_barrier in the workload's element type
+    (not the symmetric sweep groups, not the half-precision run)."""
     ctype = {"f32": "float", "f64": "double", "f16": "_Float16"}[dtype]
-    for k in ("k_group<", "k_persist<", "k_step<"):
-        if k + ctype + "," in name:
-            return not name.split(k, 1)[1].split(">", 1)[0].endswith("true")
-    return False
+    if "k_group<" + ctype + "," in name:  # k_group<T, MAXM, SC, SYM>: not the symmetric one
+        return not name.split("k_group<", 1)[1].split(">", 1)[0].endswith("true")
+    return any(k + ctype + "," in name for k in ("k_persist<", "k_step<", "k_barrier<"))
 
 
 def ingest_counters(workload, fetch_csv, write_csv, copy_mib):

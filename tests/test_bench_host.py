@@ -38,4 +38,7 @@ def test_cycle_kernel_names():
     assert bench.is_cycle_kernel("void bb::(anonymous namespace)::k_group<float, 17, 100, false>(float*, int)", "f32")
     assert not bench.is_cycle_kernel("void bb::(anonymous namespace)::k_group<float, 17, 0, true>(float*, int)", "f32")
     assert bench.is_cycle_kernel("void bb::(anonymous namespace)::k_persist<double, 33, 16>(double*, long)", "f64")
+    assert bench.is_cycle_kernel("void bb::(anonymous namespace)::k_persist<double, 33, 16, true>(double*, long)", "f64")
+    assert bench.is_cycle_kernel("void bb::(anonymous namespace)::k_persist<float, 32, 16, false>(float*, long)", "f32")
+    assert not bench.is_cycle_kernel("void bb::(anonymous namespace)::k_persist<float, 32, 16, true>(float*)", "f64")
     assert not bench.is_cycle_kernel("bb::(anonymous namespace)::k_probe_stream(float const*, long, int)", "f32")
