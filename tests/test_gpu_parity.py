@@ -40,6 +40,8 @@ SMALL = [
     (500, 256, 32, "f32", "uniform_zero_rows"),
     (500, 18, 16, "f32", "normal"),   # a b' = 2 pass (18 -> 2), then 2 -> 1
     (400, 12, 10, "f64", "normal"),   # the same in fp64 (12 -> 2 -> 1)
+    (300, 65, 16, "f32", "normal"),   # split halves with 64 early lanes (65 -> 49), then 49 -> 33
+    (600, 64, 16, "f64", "normal"),   # split halves in fp64
 ]
 
 
