@@ -72,14 +72,21 @@ __device__ __forceinline__ void store_seg(const B &A, uint32_t o, const T (&v)[M
   }
 }
 
+// What a half does once its early part is stored (see k_persist): nothing
+// for the schedulers whose halves are ordered by launches or barriers.
+struct NoPub {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // Row half of a cycle, executed by the whole workgroup: one band row per
 // thread, rows r..ch, each row's m entries (columns c..ch) loaded straight
 // into VGPRs with vector loads.  Row r is the reflector input: its thread
 // stages it in LDS (xs); every thread then forms the reflector and the
 // threads of rows r+1..ch apply it from the right.  Row r becomes (beta,
 // 0, ..., 0); column c of rows c..ch goes to LDS (ys) for the column half.
-template <typename T, int MAXM, bool FULL, class B>
-__device__ void row_half(const B &A, const Cyc &q, T *xs, T *ys) {
+// The whole half is its early part: pub runs after every store.
+template <typename T, int MAXM, bool FULL, class B, class Pub>
+__device__ void row_half(const B &A, const Cyc &q, T *xs, T *ys, const Pub &pub) {
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int m = q.m;
@@ -118,15 +125,17 @@ __device__ void row_half(const B &A, const Cyc &q, T *xs, T *ys) {
     if (ic >= 0) ys[ic] = v[0];
     if (i == 0 || h.nz) store_seg<T, MAXM, FULL>(A, o, v, m);
   }
+  pub();
 }
 
 // Column half: one band column per thread, columns c..jend, each column's m
 // entries (rows c..ch, (ld-1) elements apart) loaded into VGPRs; threads of
 // consecutive columns touch consecutive words.  The reflector comes from the
 // updated column c in LDS (ys); columns c+1..jend are updated from the left
-// and column c becomes (beta, 0, ..., 0).
-template <typename T, int MAXM, bool FULL, class B>
-__device__ void col_half(const B &A, const Cyc &q, const T *ys) {
+// and column c becomes (beta, 0, ..., 0).  Columns c..c+early (the early
+// part) are done first, then pub runs, then the rest.
+template <typename T, int MAXM, bool FULL, class B, class Pub>
+__device__ void col_half(const B &A, const Cyc &q, const T *ys, int early, const Pub &pub) {
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int m = q.m;
@@ -139,29 +148,55 @@ __device__ void col_half(const B &A, const Cyc &q, const T *ys) {
     for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o0 + uint32_t(tid) * uint32_t(sizeof(T)) + uint32_t(i) * rstep);
   }
   const Refl<T> g = house<T, MAXM, FULL>(ys, m);
-  for (int jj = tid; jj < nc; jj += nt) {
-    const uint32_t o = o0 + uint32_t(jj) * uint32_t(sizeof(T));
-    if (jj == 0) {
-      A.st_(o, g.nz ? g.beta : ys[0]);
-      for (int i = 1; i < m; ++i) A.st_(o + uint32_t(i) * rstep, T(0));
-      continue;
-    }
-    if (!g.nz) continue;
-    if (jj != tid) {
-#pragma unroll
-      for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o + uint32_t(i) * rstep);
-    }
+  // column jj's updated entries into v (v holds its old ones)
+  auto update = [&](int jj) {
     T s = T(0);
 #pragma unroll
     for (int i = 1; i < MAXM; ++i)
       if (FULL || i < m) s = fma_(ys[i], v[i], s);
     const T w = fma_(s, g.inv, v[0]);
     const T tw = g.tau * w;
-    A.st_(o, v[0] - tw);
+    v[0] = v[0] - tw;
 #pragma unroll
     for (int i = 1; i < MAXM; ++i)
-      if (FULL || i < m) A.st_(o + uint32_t(i) * rstep, fma_(-tw, ys[i] * g.inv, v[i]));
+      if (FULL || i < m) v[i] = fma_(-tw, ys[i] * g.inv, v[i]);
+  };
+  auto store = [&](int jj) {
+    const uint32_t o = o0 + uint32_t(jj) * uint32_t(sizeof(T));
+#pragma unroll
+    for (int i = 0; i < MAXM; ++i)
+      if (FULL || i < m) A.st_(o + uint32_t(i) * rstep, v[i]);
+  };
+  auto beyond = [&]() {  // columns past the workgroup's first nt
+    if (!g.nz) return;
+    for (int jj = tid + nt; jj < nc; jj += nt) {
+      const uint32_t o = o0 + uint32_t(jj) * uint32_t(sizeof(T));
+#pragma unroll
+      for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o + uint32_t(i) * rstep);
+      update(jj);
+      store(jj);
+    }
+  };
+  // A workgroup of at most early threads may hold early columns past its
+  // first nt: it finishes the half before publishing.
+  const bool split = nt > early;
+  // the thread's first column: updated, and stored now if early
+  const bool own = tid >= 1 && tid < nc && g.nz;
+  if (own) update(tid);
+  if (tid == 0) {
+    A.st_(o0, g.nz ? g.beta : ys[0]);
+    for (int i = 1; i < m; ++i) A.st_(o0 + uint32_t(i) * rstep, T(0));
+  } else if (own && (tid <= early || !split)) {
+    store(tid);
   }
+  if (!split) {
+    beyond();
+    pub();
+    return;
+  }
+  pub();
+  if (own && tid > early) store(tid);
+  beyond();
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -182,8 +217,12 @@ constexpr int stage_chunks() {
 // LDS and puts the row back; the block is then stored element by element
 // (consecutive lanes, consecutive addresses).  Arithmetic, operation order
 // and results are those of row_half.
-template <typename T, int MAXM, bool FULL, int AUX>
-__device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned char *blk, T *ys) {
+//
+// Rows r+1..r+early (the early part) are stored first, then pub runs, then
+// the rest.
+template <typename T, int MAXM, bool FULL, int AUX, class Pub>
+__device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned char *blk, T *ys, int early,
+                                const Pub &pub) {
   constexpr int CH = stage_chunks<T, MAXM>();
   constexpr int RB = CH * 16;  // LDS bytes per staged row
   const int tid = threadIdx.x;
@@ -238,41 +277,50 @@ __device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned ch
         if (FULL || j < m) row[j] = v[j];
     }
   }
-  if (!h.nz) return;  // uniform: every thread formed the same reflector; rows r+1..ch unchanged
+  if (!h.nz) {  // uniform: every thread formed the same reflector; rows r+1..ch unchanged
+    pub();
+    return;
+  }
   __syncthreads();
   // rows r+1..ch, element by element: consecutive lanes store consecutive
   // entries of a row
-  const int ne = (nr - 1) * m;
-  for (int e = tid; e < ne; e += nt) {
+  auto element = [&](int e) {
     const int i = 1 + e / m;
     const int j = e - (i - 1) * m;
     const uint32_t o = o0 + uint32_t(i) * rstep;
     A.st_(o + uint32_t(j * int(sizeof(T))), reinterpret_cast<const T *>(blk + i * RB + (o & 15u))[j]);
-  }
+  };
+  const int ne = (nr - 1) * m;
+  const int ep = min(early, nr - 1) * m;
+  for (int e = tid; e < ep; e += nt) element(e);
+  pub();
+  for (int e = ep + tid; e < ne; e += nt) element(e);
 }
 
-template <typename T, int MAXM, int AUX>
-__device__ __forceinline__ void row_half_staged_any(const Band<T, AUX> &A, const Cyc &q, unsigned char *blk, T *ys) {
+template <typename T, int MAXM, int AUX, class Pub>
+__device__ __forceinline__ void row_half_staged_any(const Band<T, AUX> &A, const Cyc &q, unsigned char *blk, T *ys,
+                                                    int early, const Pub &pub) {
   if (q.m == MAXM)
-    row_half_staged<T, MAXM, true, AUX>(A, q, blk, ys);
+    row_half_staged<T, MAXM, true, AUX>(A, q, blk, ys, early, pub);
   else
-    row_half_staged<T, MAXM, false, AUX>(A, q, blk, ys);
+    row_half_staged<T, MAXM, false, AUX>(A, q, blk, ys, early, pub);
 }
 
-template <typename T, int MAXM, class B>
-__device__ __forceinline__ void row_half_any(const B &A, const Cyc &q, T *xs, T *ys) {
+template <typename T, int MAXM, class B, class Pub = NoPub>
+__device__ __forceinline__ void row_half_any(const B &A, const Cyc &q, T *xs, T *ys, const Pub &pub = Pub()) {
   if (q.m == MAXM)
-    row_half<T, MAXM, true>(A, q, xs, ys);
+    row_half<T, MAXM, true>(A, q, xs, ys, pub);
   else
-    row_half<T, MAXM, false>(A, q, xs, ys);
+    row_half<T, MAXM, false>(A, q, xs, ys, pub);
 }
 
-template <typename T, int MAXM, class B>
-__device__ __forceinline__ void col_half_any(const B &A, const Cyc &q, const T *ys) {
+template <typename T, int MAXM, class B, class Pub = NoPub>
+__device__ __forceinline__ void col_half_any(const B &A, const Cyc &q, const T *ys, int early = 0,
+                                             const Pub &pub = Pub()) {
   if (q.m == MAXM)
-    col_half<T, MAXM, true>(A, q, ys);
+    col_half<T, MAXM, true>(A, q, ys, early, pub);
   else
-    col_half<T, MAXM, false>(A, q, ys);
+    col_half<T, MAXM, false>(A, q, ys, early, pub);
 }
 
 // One launch per step L of a pass: block q runs sweep R = Rlo + q, cycle
@@ -294,20 +342,25 @@ __global__ void __launch_bounds__(256) k_step(T *a, int64_t ld, int32_t sub, int
 }
 
 
-// Half-cycles of sweep R-1 that must be complete before half h of cycle k of
-// sweep R may start.  Half-cycles are numbered 2k (row half) and 2k+1
-// (column half).  A lag of d = 2 half-cycles suffices when b' >= 3, 3 when
+// Progress of sweep R-1 that half h of cycle k of sweep R waits for, in
+// steps: half-cycle p (2k: row half, 2k+1: column half) done counts 2p + 2,
+// and 2p + 1 once every earlier half is done and half p's early part -- its
+// pivot and the t + 1 rows (row half) or columns (column half) after it --
+// is stored (persist_early may make the early part the whole half).  Half
+// p = 2k + h needs sweep R-1's halves before p + d - 1 done and the early
+// part of half p + d - 1, with d = 2 when b' >= 3, 3 when
 // b' = 2 and 4 when b' = 1 (the page's rule: two cycles of separation only
-// when the target band is wider than bidiagonal), capped at all of R-1.  The
+// when the target band is wider than bidiagonal): no cell of this half lies
+// in the rest of that half or in any later one.  Capped at all of R-1; the
 // cap is only sound because a sweep publishes its final count after its
 // predecessor has published its own: "sweep R-1 complete" then implies
 // "every earlier sweep complete", which the truncated windows at the last
 // column need (there sweeps further back than R-1 still overlap).
-__device__ __forceinline__ int64_t half_cycles_needed(int b, int t, int64_t k, int h, int64_t kprev) {
+__device__ __forceinline__ int64_t steps_needed(int b, int t, int64_t k, int h, int64_t kprev) {
   const int bp = b - t;
   const int d = bp >= 3 ? 2 : (bp == 2 ? 3 : 4);
-  const int64_t all = 2 * kprev;
-  const int64_t need = 2 * k + h + d;
+  const int64_t all = 4 * kprev;
+  const int64_t need = 2 * (2 * k + h + d - 1) + 1;
   return need < all ? need : all;
 }
 
@@ -324,10 +377,44 @@ __device__ __forceinline__ bool wait_progress(const uint32_t *line, uint32_t nee
   return true;
 }
 
+// Rows or columns after the pivot that a persistent half stores and
+// publishes before the rest (k_persist): t + 1, the least the successor
+// needs; b + t + 1, the whole half.  A sweep trails its predecessor by about
+// (d - 1) half periods plus the part of a half before its publish, so the
+// early publish pays where d = 2 (b' >= 3).  Where d >= 3 it pays only if
+// the half's period does not grow: measured (d = 4), fp32 halves keep their
+// period and gain, fp64 ones (heavier register pressure) grow by about 10%
+// and lose, so fp64 publishes those halves whole.
+template <typename T>
+__host__ __device__ __forceinline__ int persist_early(int b, int t) {
+  return (b - t >= 3 || sizeof(T) != 8) ? t + 1 : b + t + 1;
+}
+
+// Publishes `step` on a sweep's progress line once every store issued so
+// far by the workgroup is complete (whole workgroup; see k_persist).
+template <int AUX>
+struct PersistPub {
+  uint32_t *line;
+  uint32_t step;
+  __device__ __forceinline__ void operator()() const {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (AUX == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(line, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+};
+
 // Persistent scheduler: each workgroup claims sweeps in increasing order
 // (an atomic counter), and runs all cycles of its sweep; before each half
-// cycle it waits on its predecessor's progress counter, after it publishes
-// its own.  Claims are monotone, so every sweep waited on is held by a
+// cycle it waits on its predecessor's progress counter (steps_needed).  A
+// half stores its early part first and publishes it (step 2p + 1) before
+// it stores the rest, so the successor, which needs nothing else of that
+// half, starts while the rest is still being stored; the rest is complete
+// before the sweep's next half reads anything (every wave waits for its
+// stores, then the workgroup meets) and before any later publish.  Claims
+// are monotone, so every sweep waited on is held by a
 // running workgroup: no deadlock for any grid size.  Waits are bounded by
 // time (WaitClock); on expiry the workgroup sets the status word and stops,
 // and every other workgroup stops at its next wait or claim.
@@ -357,6 +444,7 @@ __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, 
   uint32_t *claim = sync + kClaim;
   uint32_t *prog = sync + kSyncHeader;
   const int tid = threadIdx.x;
+  const int early = persist_early<T>(b, t);
 #ifdef BB_PROFILE
   // wall-clock ticks spent waiting, in row halves, column halves, publishing
   uint64_t t_wait = 0, t_row = 0, t_col = 0, t_pub = 0, n_half = 0, t_mark = 0;
@@ -384,6 +472,7 @@ __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, 
     const int64_t K = cycles_of_dev(A.n, b, t, R);
     const int64_t Kp = R > 0 ? cycles_of_dev(A.n, b, t, R - 1) : 0;
     const uint32_t *pred = prog + (R - 1) * kLine;
+    uint32_t *mine = prog + R * kLine;
     for (int64_t k = 0; k < K; ++k) {
       const Cyc q(A.n, b, t, R, k);
       for (int h = 0; h < 2; ++h) {
@@ -391,41 +480,42 @@ __global__ void __launch_bounds__(256) k_persist(T *a, int64_t ld, int32_t sub, 
         t_mark = wall_clock64();
         ++n_half;
 #endif
-        if (R > 0) {
-          if (tid == 0) {
-            sgo = wait_progress(pred, uint32_t(half_cycles_needed(b, t, k, h, Kp)), spin_limit, status);
-            if (AUX == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          }
-          __syncthreads();
-          if (!sgo) return;
+        if (R > 0 && tid == 0) {
+          sgo = wait_progress(pred, uint32_t(steps_needed(b, t, k, h, Kp)), spin_limit, status);
+          if (AUX == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
-        BB_TICK(t_wait);
-        if (h == 0) {
-          if constexpr (STAGED)
-            row_half_staged_any<T, MAXM, AUX>(A, q, blk, ys);
-          else
-            row_half_any<T, MAXM>(A, q, xs, ys);
-          BB_TICK(t_row);
-        } else {
-          col_half_any<T, MAXM>(A, q, ys);
-          BB_TICK(t_col);
-        }
-        // Publish: every wave's stores complete, then one thread moves the
-        // counter.  The final count waits for the predecessor's final count.
+        // the previous half's late stores complete (every wave), then the
+        // workgroup meets: this half may read what they wrote
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        if (tid == 0) {
-          bool go = true;
-          if (R > 0 && h == 1 && k == K - 1) go = wait_progress(pred, uint32_t(2 * Kp), spin_limit, status);
-          if (AUX == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-          if (go)
-            __hip_atomic_store(prog + R * kLine, uint32_t(2 * k + h + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!sgo) return;
+        BB_TICK(t_wait);
+        const PersistPub<AUX> pub{mine, uint32_t(2 * (2 * k + h) + 1)};
+        if (h == 0) {
+          if constexpr (STAGED)
+            row_half_staged_any<T, MAXM, AUX>(A, q, blk, ys, early, pub);
           else
-            sgo = 0;  // the final count never moves: successors time out in turn
+            row_half_any<T, MAXM>(A, q, xs, ys, pub);
+          BB_TICK(t_row);
+        } else {
+          col_half_any<T, MAXM>(A, q, ys, early, pub);
+          BB_TICK(t_col);
         }
-        BB_TICK(t_pub);
       }
     }
+    // The final count: every store complete, and only after the
+    // predecessor's final count.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0) {
+      const bool go = R == 0 || wait_progress(pred, uint32_t(4 * Kp), spin_limit, status);
+      if (AUX == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (go)
+        __hip_atomic_store(mine, uint32_t(4 * K), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        sgo = 0;  // the final count never moves: successors time out in turn
+    }
+    BB_TICK(t_pub);
     __syncthreads();  // sR is rewritten by the next claim
   }
 #ifdef BB_PROFILE

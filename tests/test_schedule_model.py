@@ -176,3 +176,90 @@ def test_split_needs_target_band_of_four():
     # with b' = 3 a sweep further back still overlaps the early part
     assert uncovered_split_conflicts(100, 18, 15, min_bp=3) > 0
     assert uncovered_split_conflicts(40, 4, 1, min_bp=3) > 0
+
+
+# ---- Publishing a half's early part (persistent kernel) ------------------
+#
+# A half publishes step 2p + 1 once every earlier half is done and its
+# pivot and the t + 1 rows (row half) or columns (column half) after it are
+# stored, and the sweep's final count once it is done; half q of sweep R
+# waits for min(2(q + d - 1) + 1, all) steps of sweep R-1 (the kernel's
+# steps_needed): the early part of R-1's half q + d - 1 instead of the whole
+# half.  The rest of a half is read before its early part is published and
+# written after, so it must meet nothing the successor touches.
+
+def part_cells(n, b, t, R, q, part, early):
+    """Cells of half q of sweep R in its early part (part 0: the pivot and
+    offsets 1..early) or the rest (part 1)."""
+    k, h = q // 2, q % 2
+    c = R + (b - t) + k * b
+    ch = min(c + t, n - 1)
+    r = R if k == 0 else c - b
+    jend = min(c + t + b, n - 1)
+    s = set()
+    if h == 0:
+        for i in range(r, ch + 1):
+            if (i - r <= early) == (part == 0):
+                s.update((i, j) for j in range(c, ch + 1))
+    else:
+        for j in range(c, jend + 1):
+            if (j - c <= early) == (part == 0):
+                s.update((i, j) for i in range(c, ch + 1))
+    return s
+
+
+def uncovered_partial_conflicts(n, b, t, early=None, extra=0):
+    """Conflicts left unordered under the early-part rule; early: offsets in
+    the early part (t + 1; fewer plants a mistake), extra: steps added to
+    every wait (-1 plants a mistake)."""
+    early = t + 1 if early is None else early
+    bp = b - t
+    d = 2 if bp >= 3 else (3 if bp == 2 else 4)
+    ns = max(n - bp - 1, 0)
+    K = [cycles_of_sweep(n, b, t, R) for R in range(ns)]
+    cells = {(R, 2 * q + p): part_cells(n, b, t, R, q, p, early)
+             for R in range(ns) for q in range(2 * K[R]) for p in (0, 1)}
+
+    def need(R, q):
+        return min(2 * (q + d - 1) + 1 + extra, 4 * K[R - 1])
+
+    bad = 0
+    for R in range(1, ns):
+        for q in range(2 * K[R]):
+            done = {}  # sweep -> steps guaranteed published (ops 0..w-1 done)
+            Rp, w = R - 1, need(R, q)
+            while Rp >= 0 and w > 0:
+                if w == 4 * K[Rp]:
+                    done.update({x: 4 * K[x] for x in range(Rp + 1)})
+                    break
+                done[Rp] = w
+                if Rp == 0:
+                    break
+                w = need(Rp, (w - 1) // 2)
+                Rp -= 1
+            mine = cells[(R, 2 * q)] | cells[(R, 2 * q + 1)]
+            for Rp in range(R):
+                for op in range(4 * K[Rp]):
+                    if done.get(Rp, 0) <= op and cells[(Rp, op)] & mine:
+                        bad += 1
+    return bad
+
+
+PARTIAL_SHAPES = [(150, 48, 16), (120, 16, 8), (100, 18, 15), (90, 12, 4), (60, 10, 1), (50, 4, 2), (64, 33, 32),
+                  (40, 39, 13), (17, 16, 5), (50, 2, 1), (160, 64, 32)]
+
+
+@pytest.mark.parametrize("n,b,t", sorted({(n, bb, tt) for (n, bw, tw) in PARTIAL_SHAPES
+                                          for (bb, tt) in pass_list(bw, tw)}))
+def test_early_part_publication_orders_every_conflict(n, b, t):
+    assert uncovered_partial_conflicts(n, b, t) == 0
+
+
+def test_early_part_publication_cannot_be_loosened():
+    # one row or column fewer in the early part (b' >= 3) ...
+    assert uncovered_partial_conflicts(120, 16, 8, early=8) > 0
+    assert uncovered_partial_conflicts(100, 18, 15, early=15) > 0
+    # ... or one step less of the predecessor, at every lag
+    assert uncovered_partial_conflicts(120, 16, 8, extra=-1) > 0
+    assert uncovered_partial_conflicts(50, 4, 2, extra=-1) > 0
+    assert uncovered_partial_conflicts(50, 2, 1, extra=-1) > 0
