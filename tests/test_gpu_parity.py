@@ -131,6 +131,26 @@ def test_fused_passes_bitwise(tun, n, bw, tw, dt):
     _check_bitwise(band, bw, tw, bbm.tuning(**tun))
 
 
+# The persistent kernel publishes each half's pivot and first t+1 rows or
+# columns before the rest (the whole half for fp64 passes with b' <= 2):
+# wide and narrow tiles, staged and unstaged row halves, workgroups smaller
+# than the early part (64 threads, t+1 = 65), passes with b' = 1 and 2 in
+# both precisions, identity reflectors (zero rows), ragged last cycles.
+@pytest.mark.parametrize("n,bw,tw,dt,dist,nt", [(301, 128, 64, "f32", "normal", 64),
+                                                (257, 96, 64, "f64", "normal", 0),
+                                                (333, 40, 31, "f32", "normal", 0),
+                                                (333, 40, 31, "f64", "normal", 128),
+                                                (211, 18, 16, "f64", "normal", 0),
+                                                (211, 18, 16, "f32", "normal", 64),
+                                                (517, 128, 32, "f32", "uniform_zero_rows", 0),
+                                                (517, 64, 32, "f64", "uniform_zero_rows", 192),
+                                                (450, 48, 16, "f32", "normal", 0)])
+def test_persistent_early_publication_bitwise(n, bw, tw, dt, dist, nt):
+    log(f"persistent early publication n={n} bw={bw} tw={tw} {dt} {dist} threads={nt}")
+    band = bb_inputs.make_band(n, bw, dt, dist, seed=n + tw)
+    _check_bitwise(band, bw, tw, bbm.tuning(scheduler=PERSIST, threads_per_block=nt))
+
+
 @pytest.mark.parametrize("n,bw,tw,dt", [(500, 64, 32, "f64"), (300, 40, 31, "f32")])
 def test_barrier_scheduler_wide_tiles_bitwise(n, bw, tw, dt):
     log(f"barrier scheduler n={n} bw={bw} tw={tw} {dt}")
