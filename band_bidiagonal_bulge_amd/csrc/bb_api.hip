@@ -160,8 +160,25 @@ constexpr size_t kGroupLdsBytes = kMaxLdsBytes - 2048;  // headroom for the stat
 constexpr int kGroupMaxSweeps = bb::kGroupMaxWaves - 2;
 
 struct GroupPlan {
-  int G = 0, W = 0;  // G = 0: the pass does not fit
+  int G = 0, W = 0;          // G = 0: the pass does not fit
+  int ring_stride = 0, w0 = 0;  // ring rows as windows of the band's rows (0: whole rows)
 };
+
+// Entries of a stored working-band row that pass (b, t) touches: offsets
+// j - i from -t (the bulge below the diagonal) to b + t (the bulge the
+// column half makes), i.e. stored entries sub - t .. sub + b + t; the window
+// starts and ends on 16-byte boundaries.
+void ring_window(const bb::Geometry &g, const bb::Pass &p, int *w0, int *stride) {
+  const int per16 = 16 / int(g.esize);
+  const int lo = int(g.sub) - p.t, hi = int(g.sub) + p.b + p.t + 1;
+  *w0 = lo / per16 * per16;
+  *stride = (hi - *w0 + per16 - 1) / per16 * per16;
+}
+
+// Windowed groups: the 32-entry tile (t = 31) in fp32 with one row per lane
+// (b + t <= 64), and at least this many sweeps per group (fewer hand every
+// sweep through memory, as the persistent kernel does).
+constexpr int kWinMinSweeps = 3;
 
 int64_t ring_rows_cached(int64_t n, const bb::Pass &p, int G) {
   static std::mutex mu;
@@ -180,15 +197,25 @@ int64_t ring_rows_cached(int64_t n, const bb::Pass &p, int G) {
 
 GroupPlan group_plan(const bb::Geometry &g, const bb::Pass &p, int requested_g) {
   GroupPlan gp;
-  if (pick_maxm(p.t) > 17) return gp;  // wider tiles spill registers in the group kernel
-  const int64_t row_bytes = int64_t(g.stride) * g.esize;
+  const int maxm = pick_maxm(p.t);
+  const bool win = maxm > 17;
+  // wider tiles spill registers in the group kernel, except fp32 with one
+  // row per lane on windows of the rows
+  if (win && !(maxm == 32 && g.esize == 4 && p.b + p.t <= 64)) return gp;  // t = 31: b = 32 or 33
+  int w0 = 0, stride = int(g.stride);
+  if (win) ring_window(g, p, &w0, &stride);
+  const int64_t row_bytes = int64_t(stride) * g.esize;
   const int64_t W = std::min<int64_t>(int64_t(kGroupLdsBytes) / row_bytes, g.n);
-  const int lo = requested_g > 0 ? requested_g : 1;
+  const int lo = requested_g > 0 ? requested_g : (win ? kWinMinSweeps : 1);
   const int hi = requested_g > 0 ? requested_g : kGroupMaxSweeps;
   for (int G = hi; G >= lo; --G) {
     if (ring_rows_cached(g.n, p, G) <= W) {
       gp.G = G;
       gp.W = int(W);
+      if (win) {
+        gp.ring_stride = stride;
+        gp.w0 = w0;
+      }
       return gp;
     }
   }
@@ -207,7 +234,7 @@ struct LaunchItem {
   int W = 0;
 };
 
-int tile_family(int maxm) { return maxm <= 9 ? 9 : 17; }
+int tile_family(int maxm) { return maxm <= 9 ? 9 : (maxm <= 17 ? 17 : 33); }
 
 std::vector<LaunchItem> plan_launches(const bb::Geometry &g, const std::vector<bb::Pass> &passes, int first, int count,
                                       const bb_tuning &tu) {
@@ -236,7 +263,7 @@ std::vector<LaunchItem> plan_launches(const bb::Geometry &g, const std::vector<b
     LaunchItem *cur = out.empty() ? nullptr : &out.back();
     const bool join = fuse && cur && cur->group && cur->first + cur->count == i &&
                       cur->run.npass < bb::kMaxRunPasses && cur->run.maxm == tile_family(maxm) && cur->W == gp.W &&
-                      cur->run.total + ngroups <= lines;
+                      gp.ring_stride == 0 && cur->run.ring_stride == 0 && cur->run.total + ngroups <= lines;
     if (!join) {
       out.emplace_back();
       cur = &out.back();
@@ -244,6 +271,8 @@ std::vector<LaunchItem> plan_launches(const bb::Geometry &g, const std::vector<b
       cur->first = i;
       cur->W = gp.W;
       cur->run.maxm = tile_family(maxm);
+      cur->run.ring_stride = gp.ring_stride;
+      cur->run.w0 = gp.w0;
     }
     const int variant = (maxm != cur->run.maxm ? 1 : 0) | (g.esize != 8 && p.b + p.t > 64 ? 2 : 0);
     cur->run.pass[cur->run.npass] = bb::group_pass_word(p.b, p.t, gp.G, variant);

@@ -721,11 +721,33 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 
 
+// Where ring rows come from in memory.  Whole rows (Win unused): ring row i
+// is the working band's row i.  Windows: ring row i holds the bytes
+// w0_bytes .. w0_bytes + ring row bytes of the band's row i (row_bytes
+// apart in memory); rcp = 1 / (ring row bytes / 16), for the row of a
+// chunk.
+struct Win {
+  int32_t row_bytes, w0_bytes;
+  float rcp;
+};
+
+// The memory offset of byte e (a multiple of 16) of ring rows lo, lo+1, ...
+// stored back to back (windows of rb bytes).
+__device__ __forceinline__ uint32_t win_offset(const Win &w, int32_t rb, int32_t lo, int32_t e) {
+  const int32_t c16 = e >> 4, rc = rb >> 4;
+  int32_t i = int32_t(float(c16) * w.rcp);  // the chunk's row, corrected below (c16 < 2^24)
+  if ((i + 1) * rc <= c16) ++i;
+  if (i * rc > c16) --i;
+  return uint32_t((lo + i) * w.row_bytes + w.w0_bytes + (e - i * rb));
+}
+
 // Copies rows [lo, hi) of the band from memory into their ring slots with
 // LDS-direct 16-byte loads (no registers involved), split where the ring
-// wraps.  Complete once vmcnt reaches zero.
-template <typename T>
-__device__ void ring_fill(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t lo, int32_t hi, int lane) {
+// wraps.  Complete once vmcnt reaches zero.  WIN: each ring row is a window
+// of the band's row (win).
+template <typename T, bool WIN = false>
+__device__ void ring_fill(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t lo, int32_t hi, int lane,
+                          const Win &win = Win{}) {
   const int32_t row_bytes = A.S * int32_t(sizeof(T));
   unsigned char *base = reinterpret_cast<unsigned char *>(A.L);
   while (lo < hi) {
@@ -733,9 +755,11 @@ __device__ void ring_fill(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t 
     const int32_t run = min(hi - lo, A.W - s);  // rows up to the end of the ring
     const int32_t bytes = run * row_bytes;
     for (int32_t off = 0; off < bytes; off += 1024) {
-      if (off + lane * 16 < bytes)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(mem, (lds_ptr_t)(base + s * row_bytes + off), 16,
-                                                 uint32_t(lo * row_bytes + off + lane * 16), 0, 0, kSc1);
+      if (off + lane * 16 < bytes) {
+        const uint32_t src = WIN ? win_offset(win, row_bytes, lo, off + lane * 16)
+                                 : uint32_t(lo * row_bytes + off + lane * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(mem, (lds_ptr_t)(base + s * row_bytes + off), 16, src, 0, 0, kSc1);
+      }
     }
     lo += run;
   }
@@ -748,8 +772,9 @@ __device__ void ring_fill(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t 
 // repeat its last chunk (the same bytes to the same address), so no lane is
 // masked off.
 constexpr int kDrainChunks = 16;
-template <typename T>
-__device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t lo, int32_t hi, int lane) {
+template <typename T, bool WIN = false>
+__device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t lo, int32_t hi, int lane,
+                           const Win &win = Win{}) {
   const int32_t row_bytes = A.S * int32_t(sizeof(T));
   const unsigned char *base = reinterpret_cast<const unsigned char *>(A.L);
   while (lo < hi) {
@@ -769,7 +794,9 @@ __device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t
 #pragma unroll
       for (int u = 0; u < kDrainChunks; ++u)
         if (off0 + u * 1024 < bytes)  // wave-uniform: chunks of this round that hold any of the run
-          __builtin_amdgcn_raw_buffer_store_b128(v[u], mem, dst + uint32_t(off[u]), 0, kSc1);
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], mem,
+                                                 WIN ? win_offset(win, row_bytes, lo, off[u]) : dst + uint32_t(off[u]),
+                                                 0, kSc1);
     }
     lo += run;
   }
@@ -788,10 +815,10 @@ __device__ __forceinline__ bool aux_idle(WaitClock &idle, uint32_t limit, GroupC
 
 // The writer: writes back the rows every sweep is done with, then publishes
 // X_g = rows written.
-template <typename T>
+template <typename T, bool WIN = false>
 __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
                              int32_t Gg, uint32_t *xself_line, int lane, uint32_t spin_limit, uint32_t *status,
-                             uint32_t *sync) {
+                             uint32_t *sync, const Win &win = Win{}) {
   int32_t written = R0;
   WaitClock idle;
   for (;;) {
@@ -811,7 +838,7 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
     // sweep needs the lowest released rows first
     const int32_t wb = min(min(dead, lh), written + kDrainBatchRows);
     if (wb > written) {
-      ring_drain(A, mem, written, wb, lane);
+      ring_drain<T, WIN>(A, mem, written, wb, lane, win);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in memory
       written = wb;
       lds_store(&ctl.written, written);  // their slots may be refilled
@@ -839,9 +866,10 @@ struct PrevRows {
 
 // The loader: polls the released rows and loads them into free ring slots,
 // in batches, signalling each batch.
-template <typename T>
+template <typename T, bool WIN = false>
 __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
-                             const PrevRows src, int lane, uint32_t spin_limit, uint32_t *status, uint32_t *sync) {
+                             const PrevRows src, int lane, uint32_t spin_limit, uint32_t *status, uint32_t *sync,
+                             const Win &win = Win{}) {
   int32_t loaded = R0;
   int32_t xprev = src.line ? 0 : n;
   WaitClock idle;
@@ -865,7 +893,7 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
     }
     const int32_t lim = min(min(xprev, wr + A.W), want);
     if (lim > loaded) {
-      ring_fill(A, mem, loaded, lim, lane);
+      ring_fill<T, WIN>(A, mem, loaded, lim, lane, win);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in LDS
       loaded = lim;
       lds_store(&ctl.loaded_hi, loaded);
@@ -882,7 +910,12 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
 // sizeof(T).  MAXM: the run's register tile; a pass of the run may use
 // MAXM - 1 instead (variant bit 0).  SYM: the sweeps are the symmetric
 // reduction's (by half-cycles, with the same lag d), every pass at MAXM.
-template <typename T, int MAXM, int SC, bool SYM = false>
+//
+// WIN (the 33-entry tile family, one row per lane): ring rows are windows of
+// the band's rows (run.ring_stride entries from entry run.w0, every entry a
+// pass touches), so that a pass of a wide working band still gets a ring of
+// several sweeps; S stays the band's row stride in memory.
+template <typename T, int MAXM, int SC, bool SYM = false, bool WIN = false>
 __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, int32_t sub, int32_t n, GroupRun run,
                                                                  int W, uint32_t *sync, uint32_t spin_limit) {
   extern __shared__ __align__(16) unsigned char lds_ring[];
@@ -892,7 +925,13 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
   uint32_t *status = sync;
   uint32_t *claim = sync + kClaim;
   uint32_t *prog = sync + kSyncHeader;
-  const Ring<T> A{reinterpret_cast<T *>(lds_ring), S, W, sub};
+  const Ring<T> A{reinterpret_cast<T *>(lds_ring), WIN ? run.ring_stride : S, W, WIN ? sub - run.w0 : sub};
+  Win win{};
+  if constexpr (WIN) {
+    win.row_bytes = S * int32_t(sizeof(T));
+    win.w0_bytes = run.w0 * int32_t(sizeof(T));
+    win.rcp = 1.0f / float(run.ring_stride * int32_t(sizeof(T)) / 16);
+  }
   const __amdgpu_buffer_rsrc_t mem =
       __builtin_amdgcn_make_buffer_rsrc(a, 0, int(uint32_t(int64_t(n) * S * int64_t(sizeof(T)))), kRsrcWord3);
   // the run's table goes to LDS once, so that no SGPRs hold it while the
@@ -966,7 +1005,10 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         const bool lo = (variant & 1) != 0;
         const bool two = (variant & 2) != 0;
         const int32_t R = R0 + wave;
-        if constexpr (sizeof(T) == 8) {
+        if constexpr (WIN) {
+          // one row per lane (b + t <= 64) leaves t = 31 only: tile MAXM - 1
+          group_sweep<T, MAXM - 1, SC, 0>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+        } else if constexpr (sizeof(T) == 8) {
           if (lo)
             group_sweep<T, MAXM - 1, SC, 2>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
           else
@@ -984,7 +1026,7 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         }
       }
     } else if (wave == run.gmax) {
-      group_writer<T>(A, ctl, mem, n, R0, Gg, prog + int64_t(gi) * kLine, lane, spin_limit, status, sync);
+      group_writer<T, WIN>(A, ctl, mem, n, R0, Gg, prog + int64_t(gi) * kLine, lane, spin_limit, status, sync, win);
     } else if (wave == run.gmax + 1) {
       PrevRows src{nullptr, 0, 0};
       if (g > 0)
@@ -995,21 +1037,21 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         const int32_t qsweeps = max(n - (qb - qt) - 1, 0);
         src = PrevRows{prog + int64_t(ctl.prev_base) * kLine, qG, (qsweeps + qG - 1) / qG};
       }
-      group_loader<T>(A, ctl, mem, n, R0, src, lane, spin_limit, status, sync);
+      group_loader<T, WIN>(A, ctl, mem, n, R0, src, lane, spin_limit, status, sync, win);
     }
     __syncthreads();
   }
 }
 
-template <typename T, int MAXM, int SC>
+template <typename T, int MAXM, int SC, bool WIN = false>
 hipError_t group_t(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
                    uint32_t spin_limit, hipStream_t st) {
-  const size_t lds = size_t(W) * size_t(g.stride) * sizeof(T);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, SC>),
+  const size_t lds = size_t(W) * size_t(WIN ? run.ring_stride : g.stride) * sizeof(T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_group<T, MAXM, SC, false, WIN>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_group<T, MAXM, SC>), dim3(unsigned(grid)), dim3(unsigned(64 * (run.gmax + 2))), lds, st,
-                     static_cast<T *>(wband), g.stride, g.sub, int32_t(g.n), run, W, sync, spin_limit);
+  hipLaunchKernelGGL((k_group<T, MAXM, SC, false, WIN>), dim3(unsigned(grid)), dim3(unsigned(64 * (run.gmax + 2))),
+                     lds, st, static_cast<T *>(wband), g.stride, g.sub, int32_t(g.n), run, W, sync, spin_limit);
   return hipGetLastError();
 }
 
@@ -1036,6 +1078,10 @@ hipError_t group_dispatch(const GroupRun &run, void *wband, const Geometry &g, i
   switch (run.maxm) {
     case 9: return group_stride<T, 9>(run, wband, g, W, sync, grid, spin_limit, st);
     case 17: return group_stride<T, 17>(run, wband, g, W, sync, grid, spin_limit, st);
+    case 33:  // windows of wide rows, fp32 only
+      if constexpr (sizeof(T) == 4)
+        if (run.ring_stride > 0) return group_t<T, 33, 0, true>(run, wband, g, W, sync, grid, spin_limit, st);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -52,6 +52,10 @@ struct GroupRun {
   int32_t gmax, maxm;    // largest G (block = 64 (gmax+2) threads); the run's register tile family
   uint32_t pass[kMaxRunPasses];
   int32_t base[kMaxRunPasses];  // the pass's first group in the run
+  // Ring rows hold a window of each working-band row (the 33-entry tile
+  // family only): entries w0 .. w0 + ring_stride - 1 of the stored row; 0,
+  // 0: whole rows (ring stride = the working band's stride).
+  int32_t ring_stride, w0;
 };
 hipError_t launch_group(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
                         uint32_t wait_ticks, hipStream_t st);

@@ -151,6 +151,24 @@ def test_persistent_early_publication_bitwise(n, bw, tw, dt, dist, nt):
     _check_bitwise(band, bw, tw, bbm.tuning(scheduler=PERSIST, threads_per_block=nt))
 
 
+# Passes with t = 31 and b + t <= 64 in fp32 run the group kernel on windows
+# of the working band's rows (the band's full rows would leave room for one
+# sweep per group): alone, after persistent passes, before a narrow pass,
+# ragged, several group sizes, and a pass of b = 33 (b' = 2).
+@pytest.mark.parametrize("n,bw,tw,dt,tun", [(700, 32, 31, "f32", dict()),
+                                            (517, 64, 31, "f32", dict()),
+                                            (1000, 256, 32, "f32", dict()),
+                                            (150, 32, 31, "f32", dict()),
+                                            (611, 32, 31, "f32", dict(scheduler=GROUP, group_sweeps=3)),
+                                            (611, 32, 31, "f32", dict(scheduler=GROUP, group_sweeps=6, max_blocks=2)),
+                                            (444, 33, 31, "f32", dict(scheduler=GROUP, group_sweeps=4)),
+                                            (700, 32, 31, "f64", dict())])
+def test_windowed_group_passes_bitwise(n, bw, tw, dt, tun):
+    log(f"windowed group n={n} bw={bw} tw={tw} {dt} {tun}")
+    band = bb_inputs.make_band(n, bw, dt, "normal", seed=n + 3)
+    _check_bitwise(band, bw, tw, bbm.tuning(**tun))
+
+
 @pytest.mark.parametrize("n,bw,tw,dt", [(500, 64, 32, "f64"), (300, 40, 31, "f32")])
 def test_barrier_scheduler_wide_tiles_bitwise(n, bw, tw, dt):
     log(f"barrier scheduler n={n} bw={bw} tw={tw} {dt}")
