@@ -177,7 +177,10 @@ void ring_window(const bb::Geometry &g, const bb::Pass &p, int *w0, int *stride)
 
 // Windowed groups: the 32-entry tile (t = 31) in fp32 with one row per lane
 // (b + t <= 64), and at least this many sweeps per group (fewer hand every
-// sweep through memory, as the persistent kernel does).
+// sweep through memory, as the persistent kernel does).  Not fp64: its
+// 768-byte windows leave room for three sweeps, and its 32-entry tiles spill
+// registers (the n = 32768 BW 128 workload's last pass took 764 ms on
+// windows against 583 ms on the persistent kernel).
 constexpr int kWinMinSweeps = 3;
 
 int64_t ring_rows_cached(int64_t n, const bb::Pass &p, int G) {
