@@ -911,11 +911,12 @@ __device__ void group_loader(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
 // MAXM - 1 instead (variant bit 0).  SYM: the sweeps are the symmetric
 // reduction's (by half-cycles, with the same lag d), every pass at MAXM.
 //
-// WIN (the 33-entry tile family, one row per lane): ring rows are windows of
-// the band's rows (run.ring_stride entries from entry run.w0, every entry a
-// pass touches), so that a pass of a wide working band still gets a ring of
-// several sweeps; S stays the band's row stride in memory.
-template <typename T, int MAXM, int SC, bool SYM = false, bool WIN = false>
+// WIN (the 33-entry tile family): ring rows are windows of the band's rows
+// (run.ring_stride entries from entry run.w0, every entry a pass touches),
+// so that a pass of a wide working band still gets a ring of several
+// sweeps; S stays the band's row stride in memory.  WIN = 1: t = 31, one row
+// per lane; 2: t = 32, two rows per lane.
+template <typename T, int MAXM, int SC, bool SYM = false, int WIN = 0>
 __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, int32_t sub, int32_t n, GroupRun run,
                                                                  int W, uint32_t *sync, uint32_t spin_limit) {
   extern __shared__ __align__(16) unsigned char lds_ring[];
@@ -1005,8 +1006,9 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         const bool lo = (variant & 1) != 0;
         const bool two = (variant & 2) != 0;
         const int32_t R = R0 + wave;
-        if constexpr (WIN) {
-          // one row per lane (b + t <= 64) leaves t = 31 only: tile MAXM - 1
+        if constexpr (WIN == 2) {
+          group_sweep<T, MAXM, SC, 1>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+        } else if constexpr (WIN == 1) {
           group_sweep<T, MAXM - 1, SC, 0>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
         } else if constexpr (sizeof(T) == 8) {
           if (lo)
@@ -1026,7 +1028,8 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         }
       }
     } else if (wave == run.gmax) {
-      group_writer<T, WIN>(A, ctl, mem, n, R0, Gg, prog + int64_t(gi) * kLine, lane, spin_limit, status, sync, win);
+      group_writer<T, WIN != 0>(A, ctl, mem, n, R0, Gg, prog + int64_t(gi) * kLine, lane, spin_limit, status, sync,
+                                win);
     } else if (wave == run.gmax + 1) {
       PrevRows src{nullptr, 0, 0};
       if (g > 0)
@@ -1037,13 +1040,13 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         const int32_t qsweeps = max(n - (qb - qt) - 1, 0);
         src = PrevRows{prog + int64_t(ctl.prev_base) * kLine, qG, (qsweeps + qG - 1) / qG};
       }
-      group_loader<T, WIN>(A, ctl, mem, n, R0, src, lane, spin_limit, status, sync, win);
+      group_loader<T, WIN != 0>(A, ctl, mem, n, R0, src, lane, spin_limit, status, sync, win);
     }
     __syncthreads();
   }
 }
 
-template <typename T, int MAXM, int SC, bool WIN = false>
+template <typename T, int MAXM, int SC, int WIN = 0>
 hipError_t group_t(const GroupRun &run, void *wband, const Geometry &g, int W, uint32_t *sync, int grid,
                    uint32_t spin_limit, hipStream_t st) {
   const size_t lds = size_t(W) * size_t(WIN ? run.ring_stride : g.stride) * sizeof(T);
@@ -1078,9 +1081,12 @@ hipError_t group_dispatch(const GroupRun &run, void *wband, const Geometry &g, i
   switch (run.maxm) {
     case 9: return group_stride<T, 9>(run, wband, g, W, sync, grid, spin_limit, st);
     case 17: return group_stride<T, 17>(run, wband, g, W, sync, grid, spin_limit, st);
-    case 33:  // windows of wide rows, fp32 only
-      if constexpr (sizeof(T) == 4)
-        if (run.ring_stride > 0) return group_t<T, 33, 0, true>(run, wband, g, W, sync, grid, spin_limit, st);
+    case 33:  // windows of wide rows, fp32 only; one pass per launch, two rows per lane: variant bit 1
+      if constexpr (sizeof(T) == 4) {
+        if (run.ring_stride > 0 && (run.pass[0] >> 30) & 1u)
+          return group_t<T, 33, 0, 2>(run, wband, g, W, sync, grid, spin_limit, st);
+        if (run.ring_stride > 0) return group_t<T, 33, 0, 1>(run, wband, g, W, sync, grid, spin_limit, st);
+      }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
