@@ -715,7 +715,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 5),
                      "traffic": None if traffic is None else round(traffic["hbm_bytes_per_launch"], 1),
                      "kernel": "cycle kernel (k_group where the pass's LDS ring fits, consecutive such passes "
-                               "in one launch; else k_persist, one launch per pass)",
+                               "in one launch, fp32 passes with t = 31 or 32 on windows of the rows; else "
+                               "k_persist, one launch per pass)",
                      "launches": launches, "avg_launch_ms": round(avg_launch_ms, 4),
                      "alg_bytes_per_launch": bytes_per_launch},
         "ms_per_reduction_events": {"median": round(statistics.median(step_ms), 4), "min": round(min(step_ms), 4)},
