@@ -175,13 +175,10 @@ void ring_window(const bb::Geometry &g, const bb::Pass &p, int *w0, int *stride)
   *stride = (hi - *w0 + per16 - 1) / per16 * per16;
 }
 
-// Windowed groups: fp32 passes with t = 31 (one row per lane, b + t <= 64)
-// or t = 32 (two rows per lane, b + t <= 128), and at least this many
-// sweeps per group (fewer hand every sweep through memory, as the
-// persistent kernel does).  Not fp64: its
-// 768-byte windows leave room for three sweeps, and its 32-entry tiles spill
-// registers (the n = 32768 BW 128 workload's last pass took 764 ms on
-// windows against 583 ms on the persistent kernel).
+// Windowed groups: passes with t = 31 (one row per lane, b + t <= 64; fp32
+// and fp64) or t = 32 (two rows per lane, b + t <= 128; fp32 only: fp64's
+// wider windows fit one sweep), and at least this many sweeps per group
+// (fewer hand every sweep through memory, as the persistent kernel does).
 constexpr int kWinMinSweeps = 2;
 
 int64_t ring_rows_cached(int64_t n, const bb::Pass &p, int G) {
@@ -206,7 +203,8 @@ GroupPlan group_plan(const bb::Geometry &g, const bb::Pass &p, int requested_g) 
   // wider tiles spill registers in the group kernel, except fp32 with one
   // row per lane on windows of the rows
   // fp32: t = 31 with one row per lane (b + t <= 64), t = 32 with two
-  if (win && !(g.esize == 4 && ((maxm == 32 && p.b + p.t <= 64) || (maxm == 33 && p.b + p.t <= 128)))) return gp;
+  if (win && !((g.esize != 2 && maxm == 32 && p.b + p.t <= 64) || (g.esize == 4 && maxm == 33 && p.b + p.t <= 128)))
+    return gp;
   int w0 = 0, stride = int(g.stride);
   if (win) ring_window(g, p, &w0, &stride);
   const int64_t row_bytes = int64_t(stride) * g.esize;

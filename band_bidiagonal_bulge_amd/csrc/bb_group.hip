@@ -217,6 +217,11 @@ __device__ __forceinline__ void ring_row_prep(const Ring<T> &A, int32_t sr, int3
   if (lane < m) px[lane] = lane > 0 ? T(0) : P.h.beta;  // row r becomes (beta, 0, ..., 0); beta = alpha for a zero tail
 }
 
+// Wide fp64 tiles form the reflector's tail x_j * inv where it is used
+// instead of holding all of it in registers (the same products).
+template <typename T, int MAXM>
+constexpr bool kLazyTail = sizeof(T) == 8 && MAXM >= 32;
+
 // Row half, second part: the reflector applied from the right to rows
 // r+1..ch, one lane per row (rows r+1+lane and, TWO, r+65+lane; wider bands
 // loop), each row's dot product with x serial in j.  nr = ch - r.
@@ -241,7 +246,7 @@ __device__ __forceinline__ void ring_row_apply(const Ring<T> &A, int32_t sr, int
     if (TWO) v1[j] = (FULL || j < m) ? p1[j] : T(0);
   }
 #pragma unroll
-  for (int j = 1; j < MAXM; ++j) xv[j] = P.x[j] * P.h.inv;  // the reflector's tail
+  for (int j = 1; j < MAXM; ++j) xv[j] = kLazyTail<T, MAXM> ? T(0) : P.x[j] * P.h.inv;  // the reflector's tail
   T d0 = T(0), d1 = T(0);
 #pragma unroll
   for (int j = 1; j < MAXM; ++j)
@@ -254,14 +259,14 @@ __device__ __forceinline__ void ring_row_apply(const Ring<T> &A, int32_t sr, int
     p0[0] = v0[0] - tw0;
 #pragma unroll
     for (int j = 1; j < MAXM; ++j)
-      if (FULL || j < m) p0[j] = fma_(-tw0, xv[j], v0[j]);
+      if (FULL || j < m) p0[j] = fma_(-tw0, kLazyTail<T, MAXM> ? P.x[j] * P.h.inv : xv[j], v0[j]);
   }
   if (TWO && h1) {
     const T tw1 = P.h.tau * fma_(d1, P.h.inv, v1[0]);
     p1[0] = v1[0] - tw1;
 #pragma unroll
     for (int j = 1; j < MAXM; ++j)
-      if (FULL || j < m) p1[j] = fma_(-tw1, xv[j], v1[j]);
+      if (FULL || j < m) p1[j] = fma_(-tw1, kLazyTail<T, MAXM> ? P.x[j] * P.h.inv : xv[j], v1[j]);
   }
   for (int32_t i = 129 + lane; i <= nr; i += 64) {  // bands wider than 128 rows
     int32_t si = sr + i;
@@ -278,7 +283,7 @@ __device__ __forceinline__ void ring_row_apply(const Ring<T> &A, int32_t sr, int
     p[0] = v[0] - tw;
 #pragma unroll
     for (int j = 1; j < MAXM; ++j)
-      if (FULL || j < m) p[j] = fma_(-tw, xv[j], v[j]);
+      if (FULL || j < m) p[j] = fma_(-tw, kLazyTail<T, MAXM> ? P.x[j] * P.h.inv : xv[j], v[j]);
   }
 }
 
@@ -333,7 +338,7 @@ __device__ __forceinline__ void ring_col_apply(const Ring<T> &A, T *base, int32_
     if (TWO) v1[i] = (FULL || i < m) ? q1[off[i]] : T(0);
   }
 #pragma unroll
-  for (int i = 1; i < MAXM; ++i) xv[i] = P.x[i] * P.h.inv;  // the reflector's tail
+  for (int i = 1; i < MAXM; ++i) xv[i] = kLazyTail<T, MAXM> ? T(0) : P.x[i] * P.h.inv;  // the reflector's tail
   T d0 = T(0), d1 = T(0);
 #pragma unroll
   for (int i = 1; i < MAXM; ++i)
@@ -346,14 +351,14 @@ __device__ __forceinline__ void ring_col_apply(const Ring<T> &A, T *base, int32_
     q0[0] = v0[0] - tw0;
 #pragma unroll
     for (int i = 1; i < MAXM; ++i)
-      if (FULL || i < m) q0[off[i]] = fma_(-tw0, xv[i], v0[i]);
+      if (FULL || i < m) q0[off[i]] = fma_(-tw0, kLazyTail<T, MAXM> ? P.x[i] * P.h.inv : xv[i], v0[i]);
   }
   if (TWO && h1) {
     const T tw1 = P.h.tau * fma_(d1, P.h.inv, v1[0]);
     q1[0] = v1[0] - tw1;
 #pragma unroll
     for (int i = 1; i < MAXM; ++i)
-      if (FULL || i < m) q1[off[i]] = fma_(-tw1, xv[i], v1[i]);
+      if (FULL || i < m) q1[off[i]] = fma_(-tw1, kLazyTail<T, MAXM> ? P.x[i] * P.h.inv : xv[i], v1[i]);
   }
   for (int32_t jj = 129 + lane; jj <= nc; jj += 64) {  // bands wider than 128 columns
     T *q = base + jj;
@@ -368,7 +373,125 @@ __device__ __forceinline__ void ring_col_apply(const Ring<T> &A, T *base, int32_
     q[0] = v[0] - tw;
 #pragma unroll
     for (int i = 1; i < MAXM; ++i)
-      if (FULL || i < m) q[off[i]] = fma_(-tw, xv[i], v[i]);
+      if (FULL || i < m) q[off[i]] = fma_(-tw, kLazyTail<T, MAXM> ? P.x[i] * P.h.inv : xv[i], v[i]);
+  }
+}
+
+// Wide tiles (the windowed group kernel): the defining entries live in LDS
+// (xs, MAXM per sweep) instead of registers.  The first part copies them to
+// xs (lane j: entry j) before the pivot overwrites them; the second part
+// reads them back by broadcast.  Same arithmetic and order as the register
+// versions above (x_j * inv is formed where it is used).
+template <typename T, int MAXM, int SC>
+__device__ __forceinline__ Refl<T> ring_row_prep_x(const Ring<T> &A, int32_t sr, int32_t colr, int lane, T *xs) {
+  const int32_t S = SC ? SC : A.S;
+  T *px = A.L + __umul24(sr, S) + colr;
+  T sn = T(0);
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j) {
+    const T xj = px[j];
+    sn = fma_(xj, xj, sn);
+  }
+  const Refl<T> h = house_from(px[0], sn);
+  if (lane < MAXM) {
+    xs[lane] = px[lane];
+    px[lane] = lane > 0 ? T(0) : h.beta;
+  }
+  return h;
+}
+
+template <typename T, int MAXM, bool TWO, int SC>
+__device__ __forceinline__ void ring_row_apply_x(const Ring<T> &A, int32_t sr, int32_t colr, int32_t nr, int lane,
+                                                 const Refl<T> &h, const T *xs) {
+  if (!h.nz) return;
+  const int32_t S = SC ? SC : A.S;
+  T *L = A.L;
+  const int32_t a0 = lane + 1, a1 = lane + 65;
+  const bool h0 = a0 <= nr, h1 = a1 <= nr;
+  const int32_t i0 = h0 ? a0 : nr, i1 = h1 ? a1 : nr;  // inactive lanes read row ch, store nothing
+  int32_t s0 = sr + i0, s1 = sr + i1;
+  s0 = s0 >= A.W ? s0 - A.W : s0;
+  s1 = s1 >= A.W ? s1 - A.W : s1;
+  T *p0 = L + __umul24(s0, S) + (colr - i0);
+  T *p1 = L + __umul24(s1, S) + (colr - i1);
+  T v0[MAXM], v1[MAXM];
+#pragma unroll
+  for (int j = 0; j < MAXM; ++j) {
+    v0[j] = p0[j];
+    if (TWO) v1[j] = p1[j];
+  }
+  T d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int j = 1; j < MAXM; ++j) {
+    d0 = fma_(v0[j], xs[j], d0);
+    if (TWO) d1 = fma_(v1[j], xs[j], d1);
+  }
+  const T tw0 = h.tau * fma_(d0, h.inv, v0[0]);
+  if (h0) {
+    p0[0] = v0[0] - tw0;
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j) p0[j] = fma_(-tw0, xs[j] * h.inv, v0[j]);
+  }
+  if (TWO && h1) {
+    const T tw1 = h.tau * fma_(d1, h.inv, v1[0]);
+    p1[0] = v1[0] - tw1;
+#pragma unroll
+    for (int j = 1; j < MAXM; ++j) p1[j] = fma_(-tw1, xs[j] * h.inv, v1[j]);
+  }
+}
+
+template <typename T, int MAXM, bool WRAP, int SC>
+__device__ __forceinline__ Refl<T> ring_col_prep_x(const Ring<T> &A, T *base, int32_t iw, int lane, T *xs) {
+  int32_t off[MAXM];
+  col_offsets<T, MAXM, WRAP, SC>(A, iw, off);
+  T sn = T(0);
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i) {
+    const T xi = base[off[i]];
+    sn = fma_(xi, xi, sn);
+  }
+  const Refl<T> h = house_from(base[off[0]], sn);
+  if (lane < MAXM) {
+    const int32_t S = SC ? SC : A.S;
+    const int32_t o = lane * (S - 1) - ((WRAP && lane >= iw) ? A.W * S : 0);
+    xs[lane] = base[o];
+    base[o] = lane > 0 ? T(0) : h.beta;
+  }
+  return h;
+}
+
+template <typename T, int MAXM, bool TWO, int SC, bool WRAP>
+__device__ __forceinline__ void ring_col_apply_x(const Ring<T> &A, T *base, int32_t iw, int32_t nc, int lane,
+                                                 const Refl<T> &h, const T *xs) {
+  if (!h.nz) return;
+  int32_t off[MAXM];
+  col_offsets<T, MAXM, WRAP, SC>(A, iw, off);
+  const int32_t a0 = lane + 1, a1 = lane + 65;
+  const bool h0 = a0 <= nc, h1 = a1 <= nc;
+  T *q0 = base + (h0 ? a0 : nc), *q1 = base + (h1 ? a1 : nc);
+  T v0[MAXM], v1[MAXM];
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) {
+    v0[i] = q0[off[i]];
+    if (TWO) v1[i] = q1[off[i]];
+  }
+  T d0 = T(0), d1 = T(0);
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i) {
+    d0 = fma_(xs[i], v0[i], d0);
+    if (TWO) d1 = fma_(xs[i], v1[i], d1);
+  }
+  const T tw0 = h.tau * fma_(d0, h.inv, v0[0]);
+  if (h0) {
+    q0[0] = v0[0] - tw0;
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i) q0[off[i]] = fma_(-tw0, xs[i] * h.inv, v0[i]);
+  }
+  if (TWO && h1) {
+    const T tw1 = h.tau * fma_(d1, h.inv, v1[0]);
+    q1[0] = v1[0] - tw1;
+#pragma unroll
+    for (int i = 1; i < MAXM; ++i) q1[off[i]] = fma_(-tw1, xs[i] * h.inv, v1[i]);
   }
 }
 
@@ -428,9 +551,12 @@ __device__ __forceinline__ bool row_common(int32_t m, int t) {
 // b' >= 3 the two second parts overlap and half q waits for 2(q+d) steps.
 // Either way it waits for all 4 Kp steps once the predecessor has no half
 // q+d-1 left.
-template <typename T, int MAXM, int SC, int TWO>
+//
+// XL: the defining entries of the fast halves live in LDS (xs, the sweep's
+// MAXM entries; wide tiles, ring_row_prep_x and the rest).
+template <typename T, int MAXM, int SC, int TWO, bool XL = false>
 __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, int t, int d, int32_t R, int j,
-                            int lane, uint32_t spin_limit, uint32_t *status, uint32_t *sync) {
+                            int lane, uint32_t spin_limit, uint32_t *status, uint32_t *sync, T *xs = nullptr) {
   const int32_t S = SC ? SC : A.S;
   const int32_t K = int32_t(cycles_of_dev(n, b, t, R));
   const int32_t Kp = j > 0 ? int32_t(cycles_of_dev(n, b, t, R - 1)) : 0;
@@ -476,18 +602,30 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
     // previous column half left it final, so it is formed before the wait;
     // the first one (row R) may still be updated by the predecessor.
     HalfRefl<T, MAXM> Pr;
+    Refl<T> hr;
     const bool row_fast = row_common<MAXM>(m, t);
     if (k > 0 && row_fast) {
-      ring_row_prep<T, MAXM, true, SC>(A, sr, colr, MAXM, lane, Pr);
+      if constexpr (XL)
+        hr = ring_row_prep_x<T, MAXM, SC>(A, sr, colr, lane, xs);
+      else
+        ring_row_prep<T, MAXM, true, SC>(A, sr, colr, MAXM, lane, Pr);
       publish_first(2 * k, r);  // the floor since the previous half: row c - b = r
     }
     if (!wait_half(2 * k, ch)) return;
     if (row_fast) {
-      if (k == 0) ring_row_prep<T, MAXM, true, SC>(A, sr, colr, MAXM, lane, Pr);
-      if (TWO == 1 || (TWO == 2 && nr > 64))
-        ring_row_apply<T, MAXM, true, true, SC>(A, sr, colr, MAXM, nr, lane, Pr);
-      else
-        ring_row_apply<T, MAXM, true, false, SC>(A, sr, colr, MAXM, nr, lane, Pr);
+      if constexpr (XL) {
+        if (k == 0) hr = ring_row_prep_x<T, MAXM, SC>(A, sr, colr, lane, xs);
+        if (TWO == 1 || (TWO == 2 && nr > 64))
+          ring_row_apply_x<T, MAXM, true, SC>(A, sr, colr, nr, lane, hr, xs);
+        else
+          ring_row_apply_x<T, MAXM, false, SC>(A, sr, colr, nr, lane, hr, xs);
+      } else {
+        if (k == 0) ring_row_prep<T, MAXM, true, SC>(A, sr, colr, MAXM, lane, Pr);
+        if (TWO == 1 || (TWO == 2 && nr > 64))
+          ring_row_apply<T, MAXM, true, true, SC>(A, sr, colr, MAXM, nr, lane, Pr);
+        else
+          ring_row_apply<T, MAXM, true, false, SC>(A, sr, colr, MAXM, nr, lane, Pr);
+      }
     } else {
       ring_row_half_masked<T, MAXM, SC>(A, sr, colr, m, nr, lane);
     }
@@ -503,15 +641,34 @@ __device__ void group_sweep(const Ring<T> &A, GroupCtl &ctl, int32_t n, int b, i
     const bool col_fast = m == MAXM;
     const int32_t iw = A.W - sc;
     const bool col_wrap = iw < MAXM;
+    Refl<T> hc;
     if (col_fast) {
-      if (col_wrap)
+      if constexpr (XL) {
+        if (col_wrap)
+          hc = ring_col_prep_x<T, MAXM, true, SC>(A, base, iw, lane, xs);
+        else
+          hc = ring_col_prep_x<T, MAXM, false, SC>(A, base, 0, lane, xs);
+      } else if (col_wrap) {
         ring_col_prep<T, MAXM, true, true, SC>(A, base, iw, MAXM, lane, Pc);
-      else
+      } else {
         ring_col_prep<T, MAXM, true, false, SC>(A, base, 0, MAXM, lane, Pc);
+      }
       publish_first(2 * k + 1, c);
     }
     if (!wait_half(2 * k + 1, ch)) return;
-    if (col_fast) {
+    if (XL && col_fast) {
+      const bool two = TWO == 1 || (TWO == 2 && nc > 64);
+      if (col_wrap) {
+        if (two)
+          ring_col_apply_x<T, MAXM, true, SC, true>(A, base, iw, nc, lane, hc, xs);
+        else
+          ring_col_apply_x<T, MAXM, false, SC, true>(A, base, iw, nc, lane, hc, xs);
+      } else if (two) {
+        ring_col_apply_x<T, MAXM, true, SC, false>(A, base, 0, nc, lane, hc, xs);
+      } else {
+        ring_col_apply_x<T, MAXM, false, SC, false>(A, base, 0, nc, lane, hc, xs);
+      }
+    } else if (col_fast) {
       const bool two = TWO == 1 || (TWO == 2 && nc > 64);
       if (col_wrap) {
         if (two)
@@ -1006,10 +1163,17 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
         const bool lo = (variant & 1) != 0;
         const bool two = (variant & 2) != 0;
         const int32_t R = R0 + wave;
+        // fp64 keeps the defining entries in LDS (their registers spill
+        // otherwise); fp32 keeps them in registers, which is faster
+        constexpr bool XL = sizeof(T) == 8;
         if constexpr (WIN == 2) {
-          group_sweep<T, MAXM, SC, 1>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+          __shared__ T win_xs[XL ? kGroupMaxSweeps * MAXM : 1];
+          group_sweep<T, MAXM, SC, 1, XL>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync,
+                                          win_xs + (XL ? wave * MAXM : 0));
         } else if constexpr (WIN == 1) {
-          group_sweep<T, MAXM - 1, SC, 0>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
+          __shared__ T win_xs[XL ? kGroupMaxSweeps * MAXM : 1];
+          group_sweep<T, MAXM - 1, SC, 0, XL>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync,
+                                              win_xs + (XL ? wave * MAXM : 0));
         } else if constexpr (sizeof(T) == 8) {
           if (lo)
             group_sweep<T, MAXM - 1, SC, 2>(A, ctl, n, pb, pt, pd, R, wave, lane, spin_limit, status, sync);
@@ -1086,6 +1250,10 @@ hipError_t group_dispatch(const GroupRun &run, void *wband, const Geometry &g, i
         if (run.ring_stride > 0 && (run.pass[0] >> 30) & 1u)
           return group_t<T, 33, 0, 2>(run, wband, g, W, sync, grid, spin_limit, st);
         if (run.ring_stride > 0) return group_t<T, 33, 0, 1>(run, wband, g, W, sync, grid, spin_limit, st);
+      }
+      if constexpr (sizeof(T) == 8) {
+        if (run.ring_stride > 0 && !((run.pass[0] >> 30) & 1u))
+          return group_t<T, 33, 0, 1>(run, wband, g, W, sync, grid, spin_limit, st);
       }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;

@@ -151,11 +151,11 @@ def test_persistent_early_publication_bitwise(n, bw, tw, dt, dist, nt):
     _check_bitwise(band, bw, tw, bbm.tuning(scheduler=PERSIST, threads_per_block=nt))
 
 
-# fp32 passes with t = 31 and b + t <= 64, or t = 32 and b + t <= 128, run
-# the group kernel on windows of the working band's rows (the band's full
-# rows would leave room for one sweep per group): alone, after persistent
-# passes, before a narrow pass, ragged, several group sizes, a pass of b = 33
-# (b' = 2), two rows per lane, zero rows.
+# Passes with t = 31 and b + t <= 64 (fp32 and fp64), or t = 32 and
+# b + t <= 128 (fp32), run the group kernel on windows of the working band's
+# rows (the band's full rows would leave room for one sweep per group):
+# alone, after persistent passes, before a narrow pass, ragged, several group
+# sizes, a pass of b = 33 (b' = 2), two rows per lane, zero rows.
 @pytest.mark.parametrize("n,bw,tw,dt,tun", [(700, 32, 31, "f32", dict()),
                                             (517, 64, 31, "f32", dict()),
                                             (1000, 256, 32, "f32", dict()),
@@ -167,7 +167,10 @@ def test_persistent_early_publication_bitwise(n, bw, tw, dt, dist, nt):
                                             (900, 64, 32, "f32", dict()),
                                             (700, 128, 32, "f32", dict()),
                                             (555, 96, 32, "f32", dict(scheduler=GROUP, group_sweeps=3)),
-                                            (333, 64, 32, "f32", "uniform_zero_rows")])
+                                            (333, 64, 32, "f32", "uniform_zero_rows"),
+                                            (444, 33, 31, "f64", dict()),
+                                            (321, 32, 31, "f64", "uniform_zero_rows"),
+                                            (600, 128, 32, "f64", dict(scheduler=GROUP))])
 def test_windowed_group_passes_bitwise(n, bw, tw, dt, tun):
     log(f"windowed group n={n} bw={bw} tw={tw} {dt} {tun}")
     dist = tun if isinstance(tun, str) else "normal"
