@@ -1,8 +1,9 @@
 """bb_reduce_noalloc (the entry point that allocates nothing; its workspace is
 the library's fixed per-GPU array) against bb_reduce with a caller workspace:
-bit patterns equal, on consecutive calls whose second and third are smaller
-than the first (the array keeps the previous call's contents), and the
-status word it hands back; shapes above the array's size are refused."""
+bit patterns equal, on consecutive calls each smaller than the one before
+(the array keeps the previous call's contents; the third has a pass on
+windowed ring rows), and the status word it hands back; shapes above the
+array's size are refused."""
 import numpy as np
 import pytest
 
@@ -12,7 +13,7 @@ from gpu_util import assert_bits_equal, log
 
 pytestmark = pytest.mark.gpu
 
-CALLS = [(16384, 64, 16, "f32"), (4096, 32, 16, "f32"), (777, 20, 7, "f64")]
+CALLS = [(16384, 64, 16, "f32"), (4096, 32, 16, "f32"), (900, 64, 31, "f32"), (777, 20, 7, "f64")]
 
 
 def _noalloc(tb, bw, tw, status):
