@@ -381,7 +381,8 @@ __device__ __forceinline__ void ring_col_apply(const Ring<T> &A, T *base, int32_
 // (xs, MAXM per sweep) instead of registers.  The first part copies them to
 // xs (lane j: entry j) before the pivot overwrites them; the second part
 // reads them back by broadcast.  Same arithmetic and order as the register
-// versions above (x_j * inv is formed where it is used).
+// versions above (x_j * inv is formed where it is used); up to 128 rows or
+// columns per half (the windowed passes have at most b + t = 128).
 template <typename T, int MAXM, int SC>
 __device__ __forceinline__ Refl<T> ring_row_prep_x(const Ring<T> &A, int32_t sr, int32_t colr, int lane, T *xs) {
   const int32_t S = SC ? SC : A.S;
