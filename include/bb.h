@@ -66,10 +66,13 @@ typedef enum {
   BB_SCHED_STEP = 1,      /* one launch per step: step L runs every (R, k=L-s*R) */
   BB_SCHED_PERSISTENT = 2, /* resident workgroups; per-sweep progress counters */
   BB_SCHED_GROUP = 3,      /* resident workgroups each running a group of
-                              consecutive sweeps on a ring of band rows in LDS;
-                              passes whose ring does not fit run PERSISTENT;
-                              one launch per pass (DEFAULT also lets
-                              consecutive group passes share a launch) */
+                              consecutive sweeps on a ring of band rows in LDS
+                              (tile widths up to 16; 31 and 32 in fp32 and 31
+                              in fp64 on rings of row windows, the entries a
+                              pass touches); passes whose ring does not fit
+                              run PERSISTENT; one launch per pass (DEFAULT
+                              also lets consecutive group passes share a
+                              launch, windowed ones excepted) */
   BB_SCHED_BARRIER = 4     /* one launch per pass of resident workgroups (one
                               per CU, at most max_blocks) running STEP's steps
                               with a device-wide barrier between steps; fp32
