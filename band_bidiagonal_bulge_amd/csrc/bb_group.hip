@@ -46,7 +46,16 @@ namespace {
 constexpr int kGroupMaxSweeps = kGroupMaxWaves - 2;
 
 constexpr int32_t kLoadBatchRows = 64;   // rows per loader batch: early rows are signalled early
-constexpr int32_t kDrainBatchRows = 32;  // rows per writer batch, published one batch at a time
+constexpr int32_t kDrainBatchRows = 32;  // rows per writer batch of the symmetric sweeps
+
+// Rows per writer batch of pass (b, t), each batch published on its own.
+// When the last sweep of a group moves its floor up by b rows, the next
+// group's first sweep waits for the lowest t + 2 of them (b' >= 2; for
+// b' = 1, for the lowest one), so the first batch should hold about those
+// and no more: t + 2 rounded up to 16 rows, and 16 rows for b' = 1 (fewer
+// rows per batch publish sooner but add batches; these sizes were the
+// fastest measured).
+__device__ __forceinline__ int32_t drain_batch(int b, int t) { return b - t >= 2 ? (t + 2 + 15) / 16 * 16 : 16; }
 
 struct GroupCtl {
   int32_t g;                         // group being run (numbered over the launch's run of passes)
@@ -971,12 +980,12 @@ __device__ __forceinline__ bool aux_idle(WaitClock &idle, uint32_t limit, GroupC
   return false;
 }
 
-// The writer: writes back the rows every sweep is done with, then publishes
-// X_g = rows written.
+// The writer: writes back the rows every sweep is done with, up to `batch`
+// rows at a time, publishing X_g = rows written after each batch.
 template <typename T, bool WIN = false>
 __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rsrc_t mem, int32_t n, int32_t R0,
                              int32_t Gg, uint32_t *xself_line, int lane, uint32_t spin_limit, uint32_t *status,
-                             uint32_t *sync, const Win &win = Win{}) {
+                             uint32_t *sync, int32_t batch, const Win &win = Win{}) {
   int32_t written = R0;
   WaitClock idle;
   for (;;) {
@@ -994,7 +1003,7 @@ __device__ void group_writer(const Ring<T> &A, GroupCtl &ctl, __amdgpu_buffer_rs
     for (int j = 0; j < kGroupMaxSweeps; ++j) dead = min(dead, __builtin_amdgcn_readlane(fl, j));
     // write back in batches, publishing after each: the next group's first
     // sweep needs the lowest released rows first
-    const int32_t wb = min(min(dead, lh), written + kDrainBatchRows);
+    const int32_t wb = min(min(dead, lh), written + batch);
     if (wb > written) {
       ring_drain<T, WIN>(A, mem, written, wb, lane, win);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the rows are in memory
@@ -1194,7 +1203,7 @@ __global__ void __launch_bounds__(64 * kGroupMaxWaves) k_group(T *a, int32_t S, 
       }
     } else if (wave == run.gmax) {
       group_writer<T, WIN != 0>(A, ctl, mem, n, R0, Gg, prog + int64_t(gi) * kLine, lane, spin_limit, status, sync,
-                                win);
+                                SYM ? kDrainBatchRows : drain_batch(pb, pt), win);
     } else if (wave == run.gmax + 1) {
       PrevRows src{nullptr, 0, 0};
       if (g > 0)
