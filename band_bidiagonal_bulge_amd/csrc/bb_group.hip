@@ -898,15 +898,51 @@ struct Win {
   float rcp;
 };
 
+// c16 / rc for the 16-byte chunk c16 of windows of rc chunks (rcp = 1 / rc):
+// the float quotient, corrected (c16 < 2^24).
+__device__ __forceinline__ int32_t win_row(const Win &w, int32_t rc, int32_t c16) {
+  int32_t i = int32_t(float(c16) * w.rcp);
+  if ((i + 1) * rc <= c16) ++i;
+  if (i * rc > c16) --i;
+  return i;
+}
+
 // The memory offset of byte e (a multiple of 16) of ring rows lo, lo+1, ...
 // stored back to back (windows of rb bytes).
 __device__ __forceinline__ uint32_t win_offset(const Win &w, int32_t rb, int32_t lo, int32_t e) {
-  const int32_t c16 = e >> 4, rc = rb >> 4;
-  int32_t i = int32_t(float(c16) * w.rcp);  // the chunk's row, corrected below (c16 < 2^24)
-  if ((i + 1) * rc <= c16) ++i;
-  if (i * rc > c16) --i;
+  const int32_t i = win_row(w, rb >> 4, e >> 4);
   return uint32_t((lo + i) * w.row_bytes + w.w0_bytes + (e - i * rb));
 }
+
+// A lane's walk over chunks lane, lane + 64, lane + 128, ... of ring rows
+// lo, lo+1, ... stored back to back (windows of rb bytes, rc = rb / 16
+// chunks each): `at` is the memory offset of the current chunk.  Moving on
+// by 64 chunks is q rows and s chunks (64 = q rc + s), and one row more
+// when the chunk's place in its row passes rc, so each step is a few adds
+// (win_offset per chunk costs four integer multiplies).
+struct WinWalk {
+  int32_t r, rc, s;
+  uint32_t at, d0, d1;
+  WinWalk() = default;
+  __device__ __forceinline__ WinWalk(const Win &w, int32_t rb, int32_t lo, int lane) {
+    rc = rb >> 4;
+    const int32_t q = win_row(w, rc, 64);
+    s = 64 - q * rc;
+    const int32_t i = win_row(w, rc, lane);
+    r = lane - i * rc;
+    at = uint32_t((lo + i) * w.row_bytes + w.w0_bytes + r * 16);
+    d0 = uint32_t(q * w.row_bytes + s * 16);
+    d1 = uint32_t(w.row_bytes - rc * 16);
+  }
+  __device__ __forceinline__ void step() {
+    r += s;
+    at += d0;
+    if (r >= rc) {
+      r -= rc;
+      at += d1;
+    }
+  }
+};
 
 // Copies rows [lo, hi) of the band from memory into their ring slots with
 // LDS-direct 16-byte loads (no registers involved), split where the ring
@@ -921,12 +957,21 @@ __device__ void ring_fill(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t 
     const int32_t s = A.slot(lo);
     const int32_t run = min(hi - lo, A.W - s);  // rows up to the end of the ring
     const int32_t bytes = run * row_bytes;
-    for (int32_t off = 0; off < bytes; off += 1024) {
-      if (off + lane * 16 < bytes) {
-        const uint32_t src = WIN ? win_offset(win, row_bytes, lo, off + lane * 16)
-                                 : uint32_t(lo * row_bytes + off + lane * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(mem, (lds_ptr_t)(base + s * row_bytes + off), 16, src, 0, 0, kSc1);
-      }
+    unsigned char *dst = base + s * row_bytes;
+    WinWalk wk = WIN ? WinWalk(win, row_bytes, lo, lane) : WinWalk{};
+    // whole 1 KiB chunks (every lane's 16 bytes inside the run) unmasked,
+    // then the last, partial one
+    const int32_t whole = bytes & ~1023;
+    int32_t off = 0;
+#pragma unroll 4
+    for (; off < whole; off += 1024) {
+      const uint32_t src = WIN ? wk.at : uint32_t(lo * row_bytes + off + lane * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mem, (lds_ptr_t)(dst + off), 16, src, 0, 0, kSc1);
+      if constexpr (WIN) wk.step();
+    }
+    if (off < bytes && off + lane * 16 < bytes) {
+      const uint32_t src = WIN ? wk.at : uint32_t(lo * row_bytes + off + lane * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mem, (lds_ptr_t)(dst + off), 16, src, 0, 0, kSc1);
     }
     lo += run;
   }
@@ -950,6 +995,10 @@ __device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t
     const int32_t bytes = run * row_bytes;
     const unsigned char *src = base + s * row_bytes;
     const uint32_t dst = uint32_t(lo * row_bytes);
+    // windows: the walk gives each chunk's offset; lanes past the end take
+    // the run's last chunk
+    WinWalk wk = WIN ? WinWalk(win, row_bytes, lo, lane) : WinWalk{};
+    const uint32_t last = WIN ? win_offset(win, row_bytes, lo, bytes - 16) : 0u;
     for (int32_t off0 = 0; off0 < bytes; off0 += kDrainChunks * 1024) {
       u32x4 v[kDrainChunks];
       int32_t off[kDrainChunks];
@@ -959,11 +1008,13 @@ __device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t
         v[u] = *reinterpret_cast<const u32x4 *>(src + off[u]);
       }
 #pragma unroll
-      for (int u = 0; u < kDrainChunks; ++u)
+      for (int u = 0; u < kDrainChunks; ++u) {
         if (off0 + u * 1024 < bytes)  // wave-uniform: chunks of this round that hold any of the run
-          __builtin_amdgcn_raw_buffer_store_b128(v[u], mem,
-                                                 WIN ? win_offset(win, row_bytes, lo, off[u]) : dst + uint32_t(off[u]),
-                                                 0, kSc1);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v[u], mem, WIN ? (off0 + u * 1024 + lane * 16 <= bytes - 16 ? wk.at : last) : dst + uint32_t(off[u]), 0,
+              kSc1);
+        if constexpr (WIN) wk.step();
+      }
     }
     lo += run;
   }
