@@ -999,7 +999,21 @@ __device__ void ring_drain(const Ring<T> &A, __amdgpu_buffer_rsrc_t mem, int32_t
     // the run's last chunk
     WinWalk wk = WIN ? WinWalk(win, row_bytes, lo, lane) : WinWalk{};
     const uint32_t last = WIN ? win_offset(win, row_bytes, lo, bytes - 16) : 0u;
-    for (int32_t off0 = 0; off0 < bytes; off0 += kDrainChunks * 1024) {
+    int32_t off0 = 0;
+    // whole rounds: every chunk of every lane inside the run
+    for (; off0 + kDrainChunks * 1024 <= bytes; off0 += kDrainChunks * 1024) {
+      u32x4 v[kDrainChunks];
+#pragma unroll
+      for (int u = 0; u < kDrainChunks; ++u) v[u] = *reinterpret_cast<const u32x4 *>(src + off0 + u * 1024 + lane * 16);
+#pragma unroll
+      for (int u = 0; u < kDrainChunks; ++u) {
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], mem, WIN ? wk.at : dst + uint32_t(off0 + u * 1024 + lane * 16), 0,
+                                               kSc1);
+        if constexpr (WIN) wk.step();
+      }
+    }
+    // the last, partial round
+    if (off0 < bytes) {
       u32x4 v[kDrainChunks];
       int32_t off[kDrainChunks];
 #pragma unroll
