@@ -319,18 +319,49 @@ __device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned ch
   }
   __syncthreads();
   // rows r+1..ch, element by element: consecutive lanes store consecutive
-  // entries of a row
-  auto element = [&](int e) {
-    const int i = 1 + e / m;
-    const int j = e - (i - 1) * m;
-    const uint32_t o = o0 + uint32_t(i) * rstep;
-    A.st_(o + uint32_t(j * int(sizeof(T))), reinterpret_cast<const T *>(blk + i * RB + (o & 15u))[j]);
-  };
+  // entries of a row.  Thread tid takes elements e = tid, tid + nt, ...
+  // (row 1 + e / m, entry e % m), stepping row and entry with adds only
+  // (nt = qs m + ss), four at a time so that one LDS wait covers four
+  // reads.  The rest continues the same walk after the publish: every
+  // element at or past ep is on some thread's walk from there.
   const int ne = (nr - 1) * m;
   const int ep = min(early, nr - 1) * m;
-  for (int e = tid; e < ep; e += nt) element(e);
+  const int qs = nt / m, ss = nt - qs * m;
+  const int i0 = 1 + tid / m;
+  int e = tid, j = tid - (i0 - 1) * m;
+  uint32_t ro = o0 + uint32_t(i0) * rstep;  // element (i, 0) in memory
+  int lr = i0 * RB;                          // staged row i in LDS
+  const uint32_t dro = uint32_t(qs) * rstep;
+  const int dlr = qs * RB;
+  auto step = [&]() {
+    e += nt;
+    j += ss;
+    ro += dro;
+    lr += dlr;
+    if (j >= m) {
+      j -= m;
+      ro += rstep;
+      lr += RB;
+    }
+  };
+  auto run = [&](int lim) {
+    while (e + 3 * nt < lim) {
+      uint32_t g[4];
+      T v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        g[u] = ro + uint32_t(j * int(sizeof(T)));
+        v[u] = reinterpret_cast<const T *>(blk + lr + (ro & 15u))[j];
+        step();
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) A.st_(g[u], v[u]);
+    }
+    for (; e < lim; step()) A.st_(ro + uint32_t(j * int(sizeof(T))), reinterpret_cast<const T *>(blk + lr + (ro & 15u))[j]);
+  };
+  run(ep);
   pub();
-  for (int e = ep + tid; e < ne; e += nt) element(e);
+  run(ne);
 }
 
 template <typename T, int MAXM, int AUX, class Pub>
