@@ -269,13 +269,28 @@ __device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned ch
   const uint32_t rstep = A.row_step();
   const uint32_t o0 = A.off(q.r, q.c);
   const int nch = nr * CH;
-  for (int e0 = tid - lane; e0 < nch; e0 += nt) {
-    const int e = e0 + lane;
-    if (e < nch) {
-      const int i = e / CH;
-      const uint32_t src = ((o0 + uint32_t(i) * rstep) & ~15u) + uint32_t(e - i * CH) * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(A.r, (lds_ptr_t)(blk + e0 * 16), 16, src, 0, 0, AUX);
+  {
+    // thread tid copies chunks tid, tid + nt, ...: chunk cc of row ci,
+    // stepped with adds (nt = qc CH + sc); whole waves of chunks unmasked,
+    // then the last, partial one
+    const int qc = nt / CH, sc = nt - qc * CH;
+    int ci = tid / CH, cc = tid - ci * CH;
+    uint32_t srow = o0 + uint32_t(ci) * rstep;
+    const uint32_t dsrow = uint32_t(qc) * rstep;
+    int e0 = tid - lane;
+    for (; e0 + 64 <= nch; e0 += nt) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(A.r, (lds_ptr_t)(blk + e0 * 16), 16,
+                                               (srow & ~15u) + uint32_t(cc) * 16u, 0, 0, AUX);
+      cc += sc;
+      srow += dsrow;
+      if (cc >= CH) {
+        cc -= CH;
+        srow += rstep;
+      }
     }
+    if (e0 < nch && e0 + lane < nch)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(A.r, (lds_ptr_t)(blk + e0 * 16), 16,
+                                               (srow & ~15u) + uint32_t(cc) * 16u, 0, 0, AUX);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
@@ -321,7 +336,7 @@ __device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned ch
   // rows r+1..ch, element by element: consecutive lanes store consecutive
   // entries of a row.  Thread tid takes elements e = tid, tid + nt, ...
   // (row 1 + e / m, entry e % m), stepping row and entry with adds only
-  // (nt = qs m + ss), four at a time so that one LDS wait covers four
+  // (nt = qs m + ss), eight at a time so that one LDS wait covers eight
   // reads.  The rest continues the same walk after the publish: every
   // element at or past ep is on some thread's walk from there.
   const int ne = (nr - 1) * m;
@@ -345,17 +360,17 @@ __device__ void row_half_staged(const Band<T, AUX> &A, const Cyc &q, unsigned ch
     }
   };
   auto run = [&](int lim) {
-    while (e + 3 * nt < lim) {
-      uint32_t g[4];
-      T v[4];
+    while (e + 7 * nt < lim) {
+      uint32_t g[8];
+      T v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         g[u] = ro + uint32_t(j * int(sizeof(T)));
         v[u] = reinterpret_cast<const T *>(blk + lr + (ro & 15u))[j];
         step();
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) A.st_(g[u], v[u]);
+      for (int u = 0; u < 8; ++u) A.st_(g[u], v[u]);
     }
     for (; e < lim; step()) A.st_(ro + uint32_t(j * int(sizeof(T))), reinterpret_cast<const T *>(blk + lr + (ro & 15u))[j]);
   };

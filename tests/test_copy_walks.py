@@ -12,7 +12,7 @@ check the identity each walk relies on, over the shapes the kernels meet:
   16 (c % rc);
 * the persistent kernel's element stores of a staged row half: thread t of
   nt visits elements t, t + nt, ... of the (nr - 1) x m block (row 1 + e // m,
-  entry e % m), four at a time, first below the early part's end ep and then
+  entry e % m), eight at a time, first below the early part's end ep and then
   on, continuing the same walk; every element must be visited exactly once.
 """
 import pytest
@@ -75,8 +75,8 @@ def element_walk(nt, m, ne, ep):
                 i += 1
 
         for lim in (ep, ne):
-            while e + 3 * nt < lim:
-                for _ in range(4):
+            while e + 7 * nt < lim:
+                for _ in range(8):
                     assert (i, j) == (1 + e // m, e % m)
                     seen[e] = seen.get(e, 0) + 1
                     step()
@@ -95,3 +95,43 @@ def test_element_walk_covers_each_element_once(nt):
                 ne, ep = (nr - 1) * m, min(early, nr - 1) * m
                 seen = element_walk(nt, m, ne, ep)
                 assert sorted(seen) == list(range(ne)) and set(seen.values()) <= {1}, (nt, m, nr, early)
+
+
+def staged_chunk_walk(nt, CH, nr, rstep, o0):
+    """The persistent kernel's staged loads: wave w's lanes copy chunks
+    e0 + lane, e0 = 64 w, 64 w + nt, ... (whole waves unmasked, then one
+    partial); thread tid keeps (row, chunk) and the row's memory offset by
+    adds.  Returns {chunk: source offset}."""
+    nch = nr * CH
+    got = {}
+    qc, sc = nt // CH, nt % CH
+    for tid in range(nt):
+        lane = tid % 64
+        ci, cc = tid // CH, tid % CH
+        srow = o0 + ci * rstep
+        e0 = tid - lane
+        while e0 + 64 <= nch:
+            assert e0 + lane not in got
+            got[e0 + lane] = (srow & ~15) + cc * 16
+            cc += sc
+            srow += qc * rstep
+            if cc >= CH:
+                cc -= CH
+                srow += rstep
+            e0 += nt
+        if e0 < nch and e0 + lane < nch:
+            assert e0 + lane not in got
+            got[e0 + lane] = (srow & ~15) + cc * 16
+    return got
+
+
+@pytest.mark.parametrize("nt", [64, 128, 192, 256])
+def test_staged_chunk_walk_matches_division(nt):
+    for CH in (3, 5, 9, 17):
+        for nr in (1, 2, 33, 97, 129, 161, 289):
+            for rstep, o0 in ((1292, 4), (1288, 8), (3000, 0), (2584, 16)):
+                got = staged_chunk_walk(nt, CH, nr, rstep, o0)
+                assert sorted(got) == list(range(nr * CH))
+                for e, src in got.items():
+                    i = e // CH
+                    assert src == ((o0 + i * rstep) & ~15) + (e - i * CH) * 16, (nt, CH, nr, e)
