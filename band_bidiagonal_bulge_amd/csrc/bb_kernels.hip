@@ -219,12 +219,11 @@ __device__ void col_half(const B &A, const Cyc &q, const T *ys, int early, const
   // the thread's first column: updated, and stored now if early
   const bool own = tid >= 1 && tid < nc && g.nz;
   if (own) update(tid);
-  if (tid == 0) {
-    A.st_(o0, g.nz ? g.beta : ys[0]);
-    for (int i = 1; i < m; ++i) A.st_(o0 + uint32_t(i) * rstep, T(0));
-  } else if (own && (tid <= early || !split)) {
-    store(tid);
-  }
+  // column c becomes (beta, 0, ..., 0): thread tid writes entries tid,
+  // tid + nt, ... (m may exceed nt), so that no one thread stores the whole
+  // column one entry at a time
+  for (int i = tid; i < m; i += nt) A.st_(o0 + uint32_t(i) * rstep, i > 0 ? T(0) : (g.nz ? g.beta : ys[0]));
+  if (own && (tid <= early || !split)) store(tid);
   if (!split) {
     beyond();
     pub();
