@@ -152,10 +152,16 @@ __device__ void col_half(const B &A, const Cyc &q, const T *ys, int early, const
   const int nc = int(q.jend - q.c) + 1;
   const uint32_t rstep = A.row_step();
   const uint32_t o0 = A.off(q.c, q.c);
+  // The thread's first column: tid, except that thread 0 (column c is the
+  // pivot's, stored by every thread below) takes column nt when the
+  // two-phase half has one, so that a band one column wider than the
+  // workgroup costs no second round of loads; thread 0 goes on with 2 nt,
+  // 3 nt, ... and thread tid with tid + nt, ...
+  const int first = (tid >= 1 || Pub::kOnePass) ? tid : nt;
   T v[MAXM];
-  if (tid >= 1 && tid < nc) {
+  if (first >= 1 && first < nc) {
 #pragma unroll
-    for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o0 + uint32_t(tid) * uint32_t(sizeof(T)) + uint32_t(i) * rstep);
+    for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o0 + uint32_t(first) * uint32_t(sizeof(T)) + uint32_t(i) * rstep);
   }
   const Refl<T> g = house<T, MAXM, FULL>(ys, m);
   if constexpr (Pub::kOnePass) {
@@ -205,7 +211,7 @@ __device__ void col_half(const B &A, const Cyc &q, const T *ys, int early, const
   };
   auto beyond = [&]() {  // columns past the workgroup's first nt
     if (!g.nz) return;
-    for (int jj = tid + nt; jj < nc; jj += nt) {
+    for (int jj = first + nt; jj < nc; jj += nt) {
       const uint32_t o = o0 + uint32_t(jj) * uint32_t(sizeof(T));
 #pragma unroll
       for (int i = 0; i < MAXM; ++i) v[i] = A.ld_(o + uint32_t(i) * rstep);
@@ -214,23 +220,24 @@ __device__ void col_half(const B &A, const Cyc &q, const T *ys, int early, const
     }
   };
   // A workgroup of at most early threads may hold early columns past its
-  // first nt: it finishes the half before publishing.
+  // first nt: it finishes the half before publishing.  Otherwise the early
+  // columns 1..early are first columns of threads 1..early.
   const bool split = nt > early;
   // the thread's first column: updated, and stored now if early
-  const bool own = tid >= 1 && tid < nc && g.nz;
-  if (own) update(tid);
+  const bool own = first >= 1 && first < nc && g.nz;
+  if (own) update(first);
   // column c becomes (beta, 0, ..., 0): thread tid writes entries tid,
   // tid + nt, ... (m may exceed nt), so that no one thread stores the whole
   // column one entry at a time
   for (int i = tid; i < m; i += nt) A.st_(o0 + uint32_t(i) * rstep, i > 0 ? T(0) : (g.nz ? g.beta : ys[0]));
-  if (own && (tid <= early || !split)) store(tid);
+  if (own && (first <= early || !split)) store(first);
   if (!split) {
     beyond();
     pub();
     return;
   }
   pub();
-  if (own && tid > early) store(tid);
+  if (own && first > early) store(first);
   beyond();
 }
 
