@@ -154,10 +154,11 @@ __device__ void col_half(const B &A, const Cyc &q, const T *ys, int early, const
   const uint32_t o0 = A.off(q.c, q.c);
   // The thread's first column: tid, except that thread 0 (column c is the
   // pivot's, stored by every thread below) takes column nt when the
-  // two-phase half has one, so that a band one column wider than the
-  // workgroup costs no second round of loads; thread 0 goes on with 2 nt,
-  // 3 nt, ... and thread tid with tid + nt, ...
-  const int first = (tid >= 1 || Pub::kOnePass) ? tid : nt;
+  // two-phase half has exactly nt + 1 columns, so that such a band costs no
+  // second round of loads (with more columns the round is needed anyway,
+  // and thread 0's far column would only spread its wave's first loads).
+  // Thread tid goes on with first + nt, first + 2 nt, ...
+  const int first = (tid >= 1 || Pub::kOnePass || nc != nt + 1) ? tid : nt;
   T v[MAXM];
   if (first >= 1 && first < nc) {
 #pragma unroll
